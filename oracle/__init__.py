@@ -1,0 +1,140 @@
+"""TEST INFRASTRUCTURE ONLY: Python access to the fp64 CPU oracle in ``oracle.c``.
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import this package. It does not import the HIP library, and the HIP
+library does not import it.
+
+The oracle follows the SketchSSM pages (readsearch.ai listing of arXiv
+2609.33051, Abstract; agihunt.info summary, "Mechanism details" and "Error
+control"): the full state is written once per window, a sketch B S_win is
+stored at each window start, and each decode step combines the sketch with
+query coefficients c = B q~ plus the exact within-window term. See the header
+of ``oracle.c`` for the exact definitions and the readings taken.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboracle.so")
+SOURCE = os.path.join(_HERE, "oracle.c")
+RULE_IDS = {"mamba2": 0, "gdn": 1, "kda": 2}
+
+_lib = None
+
+
+def build(out: str = LIB_PATH, extra_flags=(), source: str = SOURCE) -> str:
+    """Compile the oracle with gcc (host only, OpenMP, no fast-math)."""
+    cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-fPIC", "-shared",
+           *extra_flags, source, "-o", out]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def _load(path: str = LIB_PATH):
+    lib = ctypes.CDLL(path)
+    dp = ctypes.POINTER(ctypes.c_double)
+    lib.oracle_run.restype = ctypes.c_int
+    lib.oracle_run.argtypes = [ctypes.c_int] * 7 + [dp] * 14 + [ctypes.c_int]
+    lib.oracle_rule_step.restype = ctypes.c_int
+    lib.oracle_rule_step.argtypes = [ctypes.c_int] * 3 + [dp] * 4 + [ctypes.c_double]
+    lib.oracle_transition_matrix.restype = None
+    lib.oracle_transition_matrix.argtypes = [ctypes.c_int, ctypes.c_int, dp, dp,
+                                             ctypes.c_double, dp]
+    lib.oracle_max_threads.restype = ctypes.c_int
+    return lib
+
+
+def lib(path: Optional[str] = None):
+    """The loaded oracle library (built on first use if missing)."""
+    global _lib
+    if path is not None:
+        return _load(path)
+    if _lib is None:
+        if not os.path.exists(LIB_PATH) or os.path.getmtime(LIB_PATH) < os.path.getmtime(SOURCE):
+            build()
+        _lib = _load(LIB_PATH)
+    return _lib
+
+
+def _f64(x):
+    if x is None:
+        return None
+    return np.ascontiguousarray(x, dtype=np.float64)
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    return x.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def transition_matrix(rule: str, k, decay, beta: float = 0.0, _lib_override=None):
+    """The token's d_k x d_k transition matrix M_t (dense, fp64)."""
+    L = _lib_override or lib()
+    k = _f64(k)
+    decay = _f64(np.atleast_1d(decay))
+    dk = k.shape[0]
+    M = np.zeros((dk, dk))
+    L.oracle_transition_matrix(RULE_IDS[rule], dk, _ptr(k), _ptr(decay), float(beta), _ptr(M))
+    return M
+
+
+def rule_step(rule: str, S, k, v, decay, beta: float = 0.0, _lib_override=None):
+    """One token's state update S <- M_t S + b k v^T; returns the new state."""
+    L = _lib_override or lib()
+    S = _f64(S).copy()
+    k, v = _f64(k), _f64(v)
+    decay = _f64(np.atleast_1d(decay))
+    dk, dv = S.shape
+    rc = L.oracle_rule_step(RULE_IDS[rule], dk, dv, _ptr(S), _ptr(k), _ptr(v), _ptr(decay),
+                            float(beta))
+    if rc:
+        raise RuntimeError("oracle_rule_step failed")
+    return S
+
+
+def run(rule: str, S0, basis, q, k, v, decay, beta, window: int, *,
+        want_A: bool = False, want_R: bool = False, threads: int = 0,
+        _lib_override=None) -> dict:
+    """Run T decode steps for U independent units.
+
+    Shapes: S0 [U][dk][dv]; basis [U][r][dk]; q, k [T][U][dk]; v [T][U][dv];
+    decay [T][U] or [T][U][dk]; beta [T][U] (None for Mamba-2).
+    Returns y_exact, y_replay, y_sketch [T][U][dv]; S_win, Sk [T//W + 1][U][...]
+    (window-start states and sketches) and, if asked, A [T][U][dk][dk] and
+    R [T][U][dk][dv].
+    """
+    L = _lib_override or lib()
+    S0, basis, q, k, v, decay = map(_f64, (S0, basis, q, k, v, decay))
+    beta = _f64(beta)
+    U, dk, dv = S0.shape
+    r = basis.shape[1]
+    T = q.shape[0]
+    nwin = T // window
+    out = {
+        "y_exact": np.zeros((T, U, dv)),
+        "y_replay": np.zeros((T, U, dv)),
+        "y_sketch": np.zeros((T, U, dv)),
+        "S_win": np.zeros((nwin + 1, U, dk, dv)),
+        "Sk": np.zeros((nwin + 1, U, r, dv)),
+        "A": np.zeros((T, U, dk, dk)) if want_A else None,
+        "R": np.zeros((T, U, dk, dv)) if want_R else None,
+    }
+    rc = L.oracle_run(RULE_IDS[rule], U, dk, dv, r, window, T,
+                      _ptr(S0), _ptr(basis), _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(beta),
+                      _ptr(out["y_exact"]), _ptr(out["y_replay"]), _ptr(out["y_sketch"]),
+                      _ptr(out["S_win"]), _ptr(out["Sk"]), _ptr(out["A"]), _ptr(out["R"]),
+                      int(threads))
+    if rc:
+        raise RuntimeError("oracle_run failed")
+    return out
+
+
+def max_threads() -> int:
+    return int(lib().oracle_max_threads())
