@@ -1,0 +1,333 @@
+#!/usr/bin/env python3
+"""Decode-throughput benchmark of the SketchSSM windowed decode path on one GPU.
+
+Workload (default): a Gated DeltaNet decode layer, N=256 sequences x H=32
+heads, 128 x 128 fp32 state per (sequence, head), bf16 q/k/v, window W=8,
+sketch rank r=8. One timed step is one decode step of the whole layer: the
+current token is appended to the window buffer and the output is read from
+the sketch (one fused launch); after every W-th step the fused update +
+refresh writes the state once and stores the new sketch. K must be a multiple
+of W so that every window's state write is inside the timed region.
+
+Prints one JSON line. Extra fields: per-kernel times, the exact full-read path
+on the same tokens (the comparison), the byte model, the sketch's
+approximation error, and the oracle's CPU rate on a bounded sample.
+
+    python bench.py [--steps 64] [--warmup 16] [--config c3]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "update_refresh_gdn_n256_h32_128x128_w8_r8.traffic.json")
+KERNEL_SOURCES = ["common.hpp", "update_refresh.hip"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(HERE, "sketched_recurrent_state_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def bytes_model(cfg) -> dict:
+    """Algorithmic HBM bytes per unit (sequence, head)."""
+    s_in = 2 if cfg.in_dtype == "bf16" else 4
+    g = {"mamba2": 4, "gdn": 8, "kda": 4 * cfg.d_k + 4}[cfg.rule]
+    tok = (cfg.d_k + cfg.d_v) * s_in + g
+    W, r, dk, dv = cfg.window, cfg.rank, cfg.d_k, cfg.d_v
+    tau_mean = (W + 1) / 2
+    # per decode step: q + the current token (appended: read once, written once)
+    #   + the older buffered tokens + y; plus the sketch or the full state
+    step_common = dk * s_in + tok + (tau_mean - 1) * tok + tok + 4 * dv
+    sketch_step = 4 * r * dv + step_common
+    full_step = 4 * dk * dv + step_common
+    update = 8 * dk * dv + 4 * r * dv + W * tok          # read S, write S, write Sk, read buffer
+    update_no_refresh = 8 * dk * dv + W * tok
+    return dict(tok=tok, sketch_step=sketch_step, full_step=full_step, update=update,
+                update_no_refresh=update_no_refresh,
+                state_bytes_sketch=4 * r * dv, state_bytes_full=4 * dk * dv,
+                amortized_sketch=sketch_step + update / W,
+                amortized_full=full_step + update_no_refresh / W)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=64)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--config", default="c3")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-compare", action="store_true", help="skip the full-read comparison pass")
+    ap.add_argument("--cpu-units", type=int, default=512, help="oracle sample: units")
+    ap.add_argument("--cpu-steps", type=int, default=16, help="oracle sample: decode steps")
+    ap.add_argument("--only", choices=["sketch", "full", "update"], default=None,
+                    help="profiling: run only this leg's launches")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="profiling: copy MIB MiB with a plain device copy kernel, then exit")
+    a = ap.parse_args()
+
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {a.gpus} is not supported (the decode path "
+              "shards by whole heads or sequences with no exchange step).", file=sys.stderr)
+        return 2
+
+    import torch
+    import workloads
+    import sketched_recurrent_state_amd as ssm
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    dev = torch.device("cuda:0")
+
+    if a.copy_calibration:
+        n = a.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "launches": 3}))
+        return 0
+
+    cfg = workloads.get(a.config)
+    W = cfg.window
+    if a.steps % W or a.warmup % W:
+        print(f"--steps and --warmup must be multiples of the window W={W}", file=sys.stderr)
+        return 2
+    total = a.warmup + a.steps
+    d = ssm.Dims.make(cfg.rule, cfg.in_dtype, cfg.batch, cfg.heads, cfg.d_k, cfg.d_v, W, cfg.rank)
+    U = cfg.units
+
+    # ---- inputs, resident in HBM before timing ---------------------------------------
+    from concurrent.futures import ThreadPoolExecutor
+
+    def to_dev(x):
+        if x is None:
+            return None
+        if x.dtype == np.uint16:
+            return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(x).to(dev)
+
+    t0 = time.time()
+    with ThreadPoolExecutor(8) as ex:
+        S0 = np.concatenate(list(ex.map(lambda n: workloads.initial_state(cfg, [n]), range(cfg.batch))))
+        steps_host = list(ex.map(lambda t: workloads.step_inputs(cfg, t), range(total)))
+    S0_dev = to_dev(S0)
+    basis = to_dev(workloads.basis(cfg))
+    inputs = [(to_dev(s.q), to_dev(s.k), to_dev(s.v), to_dev(s.decay), to_dev(s.beta))
+              for s in steps_host]
+    gen_s = time.time() - t0
+
+    tin = torch.bfloat16 if cfg.in_dtype == "bf16" else torch.float32
+    k_buf = torch.zeros((cfg.batch, cfg.heads, W, cfg.d_k), device=dev, dtype=tin)
+    v_buf = torch.zeros((cfg.batch, cfg.heads, W, cfg.d_v), device=dev, dtype=tin)
+    d_buf = torch.zeros(workloads.decay_shape(cfg, (cfg.batch, cfg.heads, W)), device=dev)
+    b_buf = torch.zeros((cfg.batch, cfg.heads, W), device=dev) if cfg.has_beta else None
+    bufs = (k_buf, v_buf, d_buf, b_buf)
+    y = torch.empty((cfg.batch, cfg.heads, cfg.d_v), device=dev)
+    stream = torch.cuda.current_stream()
+
+    def run_sketch(state, sketch, t_lo, t_hi, upd_events=None, only=None):
+        for t in range(t_lo, t_hi):
+            q, k, v, dc, b = inputs[t]
+            tau = t % W + 1
+            if only in (None, "sketch"):
+                ssm.sketch_decode_step(d, sketch, basis, q, *bufs, tau, y, k_t=k, v_t=v,
+                                       decay_t=dc, beta_t=b, stream=stream)
+            elif only == "update":  # keep the buffer fed without the read
+                ssm.buffer_append(d, k, v, dc, b, *bufs, tau - 1, stream=stream)
+            if tau == W and only in (None, "update"):
+                if upd_events is not None:
+                    upd_events.append((torch.cuda.Event(enable_timing=True),
+                                       torch.cuda.Event(enable_timing=True)))
+                    upd_events[-1][0].record(stream)
+                ssm.window_update_refresh(d, state, sketch, basis, *bufs, W, stream=stream)
+                if upd_events is not None:
+                    upd_events[-1][1].record(stream)
+
+    def run_full(state, t_lo, t_hi, upd_events=None):
+        for t in range(t_lo, t_hi):
+            q, k, v, dc, b = inputs[t]
+            tau = t % W + 1
+            ssm.full_read_decode_step(d, state, q, *bufs, tau, y, k_t=k, v_t=v, decay_t=dc,
+                                      beta_t=b, stream=stream)
+            if tau == W:
+                if upd_events is not None:
+                    upd_events.append((torch.cuda.Event(enable_timing=True),
+                                       torch.cuda.Event(enable_timing=True)))
+                    upd_events[-1][0].record(stream)
+                ssm.window_update_refresh(d, state, None, None, *bufs, W, stream=stream)
+                if upd_events is not None:
+                    upd_events[-1][1].record(stream)
+
+    def timed(fn):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0 = time.perf_counter()
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - w0
+        return e0.elapsed_time(e1) / 1e3, wall
+
+    # ---- the sketch path (headline) ---------------------------------------------------
+    state = S0_dev.clone()
+    sketch = torch.empty((cfg.batch, cfg.heads, cfg.rank, cfg.d_v), device=dev)
+    ssm.window_update_refresh(d, state, sketch, basis, None, None, None, None, 0, stream=stream)
+    run_sketch(state, sketch, 0, a.warmup, only=a.only)
+    upd_ev = []
+    gpu_s, wall_s = timed(lambda: run_sketch(state, sketch, a.warmup, total, upd_ev, only=a.only))
+    elapsed = max(gpu_s, wall_s)
+    upd_ms = [s.elapsed_time(e) for s, e in upd_ev]
+    bm = bytes_model(cfg)
+
+    if a.only is not None:  # profiling runs stop here
+        print(json.dumps({"only": a.only, "steps": a.steps, "ms_per_step": elapsed * 1e3 / a.steps}))
+        return 0
+
+    # ---- per-kernel time of the sketch read (events around each launch) ---------------
+    def kernel_time(launch, reps):
+        evs = []
+        for i in range(reps):
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record(stream)
+            launch(i)
+            e.record(stream)
+            evs.append((s, e))
+        torch.cuda.synchronize()
+        return float(np.mean([s.elapsed_time(e) for s, e in evs]))
+
+    tau_mid = W // 2 + 1
+    q0 = inputs[0][0]
+    sketch_ms = kernel_time(lambda i: ssm.sketch_decode_step(d, sketch, basis, q0, *bufs, tau_mid, y,
+                                                             stream=stream), 20)
+    full_ms = kernel_time(lambda i: ssm.full_read_decode_step(d, state, q0, *bufs, tau_mid, y,
+                                                              stream=stream), 10)
+
+    # ---- the exact full-read path on the same tokens (comparison) ----------------------
+    full = None
+    if not a.no_compare:
+        state_f = S0_dev.clone()
+        run_full(state_f, 0, a.warmup)
+        upd_f = []
+        gpu_f, wall_f = timed(lambda: run_full(state_f, a.warmup, total, upd_f))
+        el_f = max(gpu_f, wall_f)
+        full = {"steps_per_s": a.steps / el_f, "ms_per_step": el_f * 1e3 / a.steps,
+                "update_no_refresh_ms": float(np.mean([s.elapsed_time(e) for s, e in upd_f]))}
+        del state_f
+
+    # ---- approximation error of the sketch read vs the exact read (untimed) -----------
+    st_a = S0_dev.clone()
+    sk_a = torch.empty_like(sketch)
+    ssm.window_update_refresh(d, st_a, sk_a, basis, None, None, None, None, 0, stream=stream)
+    errs = []
+    y_f = torch.empty_like(y)
+    for t in range(2 * W):
+        q, k, v, dc, b = inputs[t]
+        tau = t % W + 1
+        ssm.sketch_decode_step(d, sk_a, basis, q, *bufs, tau, y, k_t=k, v_t=v, decay_t=dc, beta_t=b,
+                               stream=stream)
+        ssm.full_read_decode_step(d, st_a, q, *bufs, tau, y_f, stream=stream)
+        num = (y - y_f).view(U, -1).norm(dim=1)
+        den = y_f.view(U, -1).norm(dim=1)
+        errs.append((num / den.clamp_min(1e-30)).cpu())
+        if tau == W:
+            ssm.window_update_refresh(d, st_a, sk_a, basis, *bufs, W, stream=stream)
+    e = torch.cat(errs).double().numpy()
+    approx = {"mean": float(e.mean()), "p50": float(np.median(e)), "p99": float(np.quantile(e, 0.99)),
+              "max": float(e.max()), "steps": 2 * W}
+    del st_a, sk_a
+
+    # ---- roofline of the dominant kernel (update + refresh) ---------------------------
+    upd_avg_ms = float(np.mean(upd_ms))
+    upd_bytes = bm["update"] * U
+    achieved = upd_bytes / (upd_avg_ms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as fh:
+            tr = json.load(fh)
+        if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("config") == cfg.name:
+            traffic = tr.get("bytes_per_launch")
+
+    # ---- CPU baseline: the oracle on a bounded sample --------------------------------
+    cpu = None
+    if not a.no_cpu_baseline:
+        import oracle
+        units = workloads.sample_units(cfg, min(a.cpu_units, U))
+        Ts = min(a.cpu_steps, total)
+        flat = lambda x, e: x.reshape((U,) + ((e,) if e else ()))[units]
+        h = [steps_host[t] for t in range(Ts)]
+        q = np.stack([workloads.widen(flat(s.q, cfg.d_k)) for s in h])
+        k = np.stack([workloads.widen(flat(s.k, cfg.d_k)) for s in h])
+        v = np.stack([workloads.widen(flat(s.v, cfg.d_v)) for s in h])
+        dc = np.stack([flat(s.decay, cfg.d_k if cfg.per_channel_decay else 0) for s in h]).astype(np.float64)
+        be = (np.stack([flat(s.beta, 0) for s in h]).astype(np.float64) if cfg.has_beta else None)
+        S0s = S0.reshape(U, cfg.d_k, cfg.d_v)[units].astype(np.float64)
+        Bs = workloads.basis(cfg)[units % cfg.heads].astype(np.float64)
+        threads = oracle.max_threads()
+        c0 = time.perf_counter()
+        oracle.run(cfg.rule, S0s, Bs, q, k, v, dc, be, W, threads=threads)
+        cpu_s = time.perf_counter() - c0
+        steps_per_s = Ts / (cpu_s * U / len(units))
+        cpu = {"value": steps_per_s, "unit": "decode steps/s", "cores": threads, "kind": "oracle",
+               "sample": f"{len(units)} of {U} (sequence, head) units x {Ts} steps, fp64, "
+                         f"{cpu_s:.2f} s wall on {threads} threads; rate scaled to all {U} units"}
+
+    value = a.steps / elapsed
+    out = {
+        "metric": "decode steps/sec and achieved HBM GB/s (% roofline), GDN 128×128 state, B=256, r=8",
+        "value": value,
+        "unit": "decode steps/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": elapsed * 1e3 / a.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.description, "rule": cfg.rule, "batch": cfg.batch,
+                   "heads": cfg.heads, "d_k": cfg.d_k, "d_v": cfg.d_v, "window": W,
+                   "rank": cfg.rank, "inputs": cfg.in_dtype, "state": "f32"},
+        "roofline": {"bound": "hbm", "kernel": "update_refresh_kernel", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "bytes_per_launch": upd_bytes,
+                     "avg_launch_ms": upd_avg_ms, "launches": len(upd_ms)},
+        "cpu_baseline": cpu,
+        "tokens_per_s": value * cfg.batch,
+        "kernels_ms": {"update_refresh": upd_avg_ms, "sketch_decode": sketch_ms,
+                       "full_read_decode": full_ms},
+        "sketch_decode_gbs": bm["sketch_step"] * U / (sketch_ms * 1e-3) / 1e9,
+        "full_read_decode_gbs": bm["full_step"] * U / (full_ms * 1e-3) / 1e9,
+        "full_read_path": full,
+        "speedup_vs_full_read": (value / full["steps_per_s"]) if full else None,
+        "bytes_per_unit": {k: bm[k] for k in ("state_bytes_sketch", "state_bytes_full", "sketch_step",
+                                              "full_step", "amortized_sketch", "amortized_full")},
+        "state_bytes_ratio": bm["state_bytes_full"] / bm["state_bytes_sketch"],
+        "read_path_bytes_ratio": bm["full_step"] / bm["sketch_step"],
+        "approx_error": approx,
+        "input_gen_s": gen_s,
+        "device": torch.cuda.get_device_name(0),
+    }
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,177 @@
+/*
+ * sketchssm.h -- C ABI of libsketchssm.so: the SketchSSM windowed
+ * linear-attention decode path on AMD Instinct MI355X (gfx950).
+ *
+ * Method (SketchSSM pages: readsearch.ai listing of arXiv 2609.33051,
+ * "SketchSSM: Write to the Full State, Read from a Compact Sketch", Abstract;
+ * agihunt.info summary, "Confirmed" bullets "Mechanism details" and
+ * "Error control"):
+ *   - keys, values and gates of the current window are buffered and the full
+ *     recurrent state S (d_k x d_v, fp32, one per (sequence, head) unit) is
+ *     written once per window;
+ *   - the same pass that writes S also stores a compact sketch: the outputs of
+ *     S for r fixed, offline basis vectors b_1..b_r;
+ *   - every decode step in between reads only the sketch and the buffer and
+ *     rebuilds the output from query-dependent coefficients; the sketch's
+ *     approximation error never reaches S.
+ *
+ * Notation (per unit). Token i of the window has key k_i, value v_i, gate(s)
+ * and, for the delta rules, a write strength beta_i. Its transition matrix M_i
+ * and update S <- M_i S + b_i k_i v_i^T are:
+ *   SSM_MAMBA2 : M = a I                         , b = 1      (scalar decay a)
+ *   SSM_GDN    : M = alpha (I - beta k k^T)      , b = beta   (scalar gate alpha)
+ *   SSM_KDA    : M = (I - beta k k^T) Diag(alpha), b = beta   (per-channel gate alpha[d_k])
+ * With S_win the state at the window start, after tau buffered tokens
+ *   S_tau = A S_win + R,  A = M_tau ... M_1,  R = sum_i M_tau..M_{i+1} b_i k_i v_i^T,
+ * and the exact output is y = S_tau^T q = S_win^T (A^T q) + R^T q.
+ * The sketch read replaces S_win^T q~ (q~ = A^T q) by Sk^T c with c = B q~.
+ *
+ * Memory layouts (row-major, every pointer a DEVICE pointer owned by the
+ * caller; the library keeps no pointer after a call returns):
+ *   state   S   fp32  [N][H][d_k][d_v]
+ *   sketch  Sk  fp32  [N][H][r][d_v]     row m = S^T b_m (the output for basis vector b_m)
+ *   basis   B   fp32  [H][r][d_k]        row m = b_m; rows orthonormal (not checked)
+ *   k_buf       in    [N][H][W][d_k]     window buffer, slot i = token i+1 of the window
+ *   v_buf       in    [N][H][W][d_v]
+ *   decay_buf   fp32  [N][H][W] (Mamba-2 a, GDN alpha) or [N][H][W][d_k] (KDA alpha)
+ *   beta_buf    fp32  [N][H][W] (GDN, KDA); NULL for Mamba-2
+ *   q, k_t      in    [N][H][d_k]        one token per unit
+ *   v_t         in    [N][H][d_v]
+ *   decay_t     fp32  [N][H] or [N][H][d_k];  beta_t fp32 [N][H] or NULL
+ *   y           fp32  [N][H][d_v]
+ * "in" is bf16 or fp32 as ssm_dims.in_dtype says. A unit is (n, h), flat
+ * index n*H + h.
+ *
+ * Calls are asynchronous: arguments are checked on the host, then the work is
+ * enqueued on `stream` (a hipStream_t; NULL = the default stream). No call
+ * allocates, frees or synchronises. Invalid arguments return a non-zero
+ * status before anything is enqueued; a failed launch returns SSM_E_LAUNCH.
+ * Faults inside a kernel surface at the caller's next synchronisation. No C++
+ * exception crosses this interface. The detail of the last failure on the
+ * calling thread is in ssm_last_error().
+ *
+ * Supported shapes: d_k in {16, 32, 64, 128}; d_v in {32, 64, 128};
+ * 1 <= W <= 16; 1 <= r <= min(d_k, 32); N >= 0 (N = 0 is a no-op); H >= 1;
+ * N*H < 2^24. Every pointer must be 16-byte aligned. Outputs must not
+ * overlap any input of the same call.
+ */
+#ifndef SKETCHSSM_H
+#define SKETCHSSM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSM_ABI_VERSION 1
+
+typedef enum { SSM_MAMBA2 = 0, SSM_GDN = 1, SSM_KDA = 2 } ssm_rule;
+typedef enum { SSM_IN_BF16 = 0, SSM_IN_F32 = 1 } ssm_in_dtype;
+
+typedef enum {
+  SSM_OK = 0,
+  SSM_E_NULL = 1,   /* a required pointer is NULL                          */
+  SSM_E_SHAPE = 2,  /* unsupported or inconsistent dimensions               */
+  SSM_E_ALIGN = 3,  /* a pointer is not 16-byte aligned                     */
+  SSM_E_RANGE = 4,  /* an enum, a token count, tau or slot is out of range,
+                       or beta is given for Mamba-2                         */
+  SSM_E_ALIAS = 5,  /* an output overlaps an input                          */
+  SSM_E_LAUNCH = 6  /* the HIP runtime refused the launch                   */
+} ssm_status;
+
+typedef struct {
+  int32_t rule;      /* ssm_rule                          */
+  int32_t in_dtype;  /* ssm_in_dtype of q, k, v           */
+  int32_t batch;     /* N sequences                       */
+  int32_t heads;     /* H heads                           */
+  int32_t d_k;       /* key / state rows                  */
+  int32_t d_v;       /* value / state columns             */
+  int32_t window;    /* W buffered tokens per state write */
+  int32_t rank;      /* r basis vectors (sketch rows)     */
+} ssm_dims;
+
+/* SSM_ABI_VERSION of the library. */
+int32_t ssm_abi_version(void);
+
+/* Static text for a status code. */
+const char* ssm_status_string(int32_t status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* ssm_last_error(void);
+
+/*
+ * Token buffering. Copies the current token of every unit into window slot
+ * `slot` (0-based, 0 <= slot < W): k_t -> k_buf, v_t -> v_buf,
+ * decay_t -> decay_buf, beta_t -> beta_buf (beta_t and beta_buf NULL for
+ * Mamba-2). Source: the pages' buffering of keys and values between state
+ * writes (readsearch.ai listing, Abstract, on ReplaySSM; agihunt.info
+ * "Confirmed", background bullet).
+ */
+ssm_status ssm_buffer_append(const ssm_dims* d,
+                             const void* k_t, const void* v_t,
+                             const float* decay_t, const float* beta_t,
+                             void* k_buf, void* v_buf, float* decay_buf, float* beta_buf,
+                             int32_t slot, void* stream);
+
+/*
+ * Window update fused with the sketch refresh. For every unit: reads S once,
+ * applies the first n_tokens buffered tokens in order (S <- M_i S + b_i k_i v_i^T),
+ * writes S back (only if n_tokens > 0), then, if `sketch` is not NULL, stores
+ * Sk = B S (row m = S^T b_m) from the updated state. n_tokens = 0 with a sketch
+ * is the refresh-only pass that creates the first sketch; sketch = NULL (basis
+ * may then be NULL) is a plain windowed update with no refresh.
+ * 0 <= n_tokens <= W. Source: readsearch.ai listing, Abstract (one full-state
+ * read per update precomputes the basis outputs); agihunt.info "Error control"
+ * (the full state is updated once per window and the sketch is refreshed in
+ * the same kernel).
+ * Outputs: state (in/out), sketch. Inputs: basis, the buffers.
+ */
+ssm_status ssm_window_update_refresh(const ssm_dims* d,
+                                     float* state, float* sketch, const float* basis,
+                                     const void* k_buf, const void* v_buf,
+                                     const float* decay_buf, const float* beta_buf,
+                                     int32_t n_tokens, void* stream);
+
+/*
+ * Sketch decode step (the per-step read). tau (1 <= tau <= W) tokens of the
+ * window are valid, the current token included. For every unit:
+ *   walk the buffer newest to oldest from u = q:  s_i = k_i . u,
+ *   intra += b_i s_i v_i,  u <- M_i^T u;  then q~ = u, c = B q~ and
+ *   y = Sk^T c + intra.
+ * Reads only the sketch, the basis, q and the buffer; never the state.
+ * Token append, fused: if k_t is not NULL, the current token (k_t, v_t,
+ * decay_t, beta_t) is first written into slot tau-1 of the buffer and used
+ * from there; if k_t is NULL, slot tau-1 must already hold it and v_t,
+ * decay_t, beta_t must be NULL too. The buffers are written only in the
+ * fused case. Source: readsearch.ai listing, Abstract (each decode step
+ * combines the sketch vectors with query-dependent coefficients);
+ * agihunt.info "Mechanism details" (within a window only the queries vary).
+ * Output: y. The sketch and the state are never written.
+ */
+ssm_status ssm_sketch_decode_step(const ssm_dims* d,
+                                  const float* sketch, const float* basis, const void* q,
+                                  const void* k_t, const void* v_t,
+                                  const float* decay_t, const float* beta_t,
+                                  void* k_buf, void* v_buf, float* decay_buf, float* beta_buf,
+                                  int32_t tau, float* y, void* stream);
+
+/*
+ * Exact full-read decode step (the comparison path: the buffered read that
+ * still reads all of S each step; readsearch.ai listing, Abstract, on
+ * ReplaySSM). Same walk as ssm_sketch_decode_step, then
+ * y = S_win^T q~ + intra, reading the whole window-start state S_win = state.
+ * Token append works as in ssm_sketch_decode_step. Output: y.
+ */
+ssm_status ssm_full_read_decode_step(const ssm_dims* d,
+                                     const float* state, const void* q,
+                                     const void* k_t, const void* v_t,
+                                     const float* decay_t, const float* beta_t,
+                                     void* k_buf, void* v_buf, float* decay_buf, float* beta_buf,
+                                     int32_t tau, float* y, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKETCHSSM_H */

@@ -1,0 +1,221 @@
+"""SketchSSM windowed linear-attention decode for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libsketchssm.so`` (C ABI in
+``include/sketchssm.h``). Each function here marshals its arguments and calls
+the library entry point of the same name; every step of the decode path runs
+in the library's HIP kernels. Tensors are PyTorch device tensors (PyTorch
+provides memory and streams only) or raw device addresses as ``int``.
+
+If the library has not been built this module raises on import: there is no
+fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Union
+
+__all__ = [
+    "Dims", "SSMError", "MAMBA2", "GDN", "KDA", "IN_BF16", "IN_F32", "RULES",
+    "abi_version", "buffer_append", "window_update_refresh", "sketch_decode_step",
+    "full_read_decode_step", "LIB_PATH", "HEADER", "declared_symbols",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsketchssm.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "sketchssm.h")
+
+MAMBA2, GDN, KDA = 0, 1, 2
+RULES = {"mamba2": MAMBA2, "gdn": GDN, "kda": KDA}
+IN_BF16, IN_F32 = 0, 1
+
+STATUS = {0: "SSM_OK", 1: "SSM_E_NULL", 2: "SSM_E_SHAPE", 3: "SSM_E_ALIGN", 4: "SSM_E_RANGE",
+          5: "SSM_E_ALIAS", 6: "SSM_E_LAUNCH"}
+
+
+class SSMError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+class Dims(ctypes.Structure):
+    """ssm_dims: rule, in_dtype, batch, heads, d_k, d_v, window, rank."""
+
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("rule", "in_dtype", "batch", "heads", "d_k", "d_v", "window", "rank")]
+
+    @classmethod
+    def make(cls, rule, in_dtype, batch, heads, d_k, d_v, window, rank) -> "Dims":
+        if isinstance(rule, str):
+            rule = RULES[rule]
+        if isinstance(in_dtype, str):
+            in_dtype = {"bf16": IN_BF16, "f32": IN_F32}[in_dtype]
+        return cls(rule, in_dtype, batch, heads, d_k, d_v, window, rank)
+
+    def __repr__(self):
+        return "Dims(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m sketched_recurrent_state_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, dp = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(Dims)
+    lib.ssm_abi_version.restype = i32
+    lib.ssm_abi_version.argtypes = []
+    lib.ssm_status_string.restype = ctypes.c_char_p
+    lib.ssm_status_string.argtypes = [i32]
+    lib.ssm_last_error.restype = ctypes.c_char_p
+    lib.ssm_last_error.argtypes = []
+    lib.ssm_buffer_append.restype = i32
+    lib.ssm_buffer_append.argtypes = [dp] + [vp] * 8 + [i32, vp]
+    lib.ssm_window_update_refresh.restype = i32
+    lib.ssm_window_update_refresh.argtypes = [dp] + [vp] * 7 + [i32, vp]
+    lib.ssm_sketch_decode_step.restype = i32
+    lib.ssm_sketch_decode_step.argtypes = [dp] + [vp] * 11 + [i32, vp, vp]
+    lib.ssm_full_read_decode_step.restype = i32
+    lib.ssm_full_read_decode_step.argtypes = [dp] + [vp] * 10 + [i32, vp, vp]
+    return lib
+
+
+_lib = _load()
+
+
+def declared_symbols(header: str = HEADER):
+    """Function names declared in the C header."""
+    import re
+    text = open(header).read()
+    return sorted(set(re.findall(r"^\s*(?:ssm_status|int32_t|const char\*)\s+(ssm_\w+)\s*\(",
+                                 text, re.M)))
+
+
+def library():
+    return _lib
+
+
+def abi_version() -> int:
+    return int(_lib.ssm_abi_version())
+
+
+# ----------------------------------------------------------------------------
+# marshalling
+# ----------------------------------------------------------------------------
+Ptr = Union["torch.Tensor", int, None]  # noqa: F821
+
+
+def numel(d: Dims) -> dict:
+    """Element count of every array argument for these dimensions."""
+    U = d.batch * d.heads
+    dstr = d.d_k if d.rule == KDA else 1
+    return {
+        "state": U * d.d_k * d.d_v, "sketch": U * d.rank * d.d_v, "basis": d.heads * d.rank * d.d_k,
+        "k_buf": U * d.window * d.d_k, "v_buf": U * d.window * d.d_v,
+        "decay_buf": U * d.window * dstr, "beta_buf": U * d.window,
+        "q": U * d.d_k, "k_t": U * d.d_k, "v_t": U * d.d_v, "decay_t": U * dstr, "beta_t": U,
+        "y": U * d.d_v,
+    }
+
+
+def _addr(x: Ptr, name: str, dtype=None, count: Optional[int] = None) -> Optional[int]:
+    """Device address of a tensor (checked: device, contiguity, dtype, size) or int."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if not x.is_cuda:
+        raise ValueError(f"{name}: expected a device tensor")
+    if not x.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous tensor")
+    if dtype is not None and x.dtype not in dtype:
+        raise TypeError(f"{name}: dtype {x.dtype} not in {dtype}")
+    if count is not None and x.numel() != count:
+        raise ValueError(f"{name}: {x.numel()} elements, the dimensions need {count}")
+    return x.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        if torch.cuda.is_available():
+            return torch.cuda.current_stream().cuda_stream
+        return None
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _in_types(d: Dims):
+    import torch
+    return (torch.bfloat16,) if d.in_dtype == IN_BF16 else (torch.float32,)
+
+
+def _f32():
+    import torch
+    return (torch.float32,)
+
+
+def _check(status: int):
+    if status != 0:
+        raise SSMError(status, _lib.ssm_last_error().decode())
+
+
+def _types(d: Dims, args):
+    """Dtype sets only when tensors are passed (raw ints skip the torch import)."""
+    if all(a is None or isinstance(a, int) for a in args):
+        return None, None
+    return _in_types(d), _f32()
+
+
+# ----------------------------------------------------------------------------
+# entry points (same names as the C ABI, without the ssm_ prefix)
+# ----------------------------------------------------------------------------
+def buffer_append(d: Dims, k_t, v_t, decay_t, beta_t, k_buf, v_buf, decay_buf, beta_buf,
+                  slot: int, stream=None) -> None:
+    tin, f32 = _types(d, (k_t, v_t, decay_t, beta_t, k_buf, v_buf, decay_buf, beta_buf))
+    n = numel(d)
+    _check(_lib.ssm_buffer_append(
+        ctypes.byref(d), _addr(k_t, "k_t", tin, n["k_t"]), _addr(v_t, "v_t", tin, n["v_t"]),
+        _addr(decay_t, "decay_t", f32, n["decay_t"]), _addr(beta_t, "beta_t", f32, n["beta_t"]),
+        _addr(k_buf, "k_buf", tin, n["k_buf"]), _addr(v_buf, "v_buf", tin, n["v_buf"]),
+        _addr(decay_buf, "decay_buf", f32, n["decay_buf"]), _addr(beta_buf, "beta_buf", f32, n["beta_buf"]),
+        int(slot), _stream(stream)))
+
+
+def window_update_refresh(d: Dims, state, sketch, basis, k_buf, v_buf, decay_buf, beta_buf,
+                          n_tokens: int, stream=None) -> None:
+    tin, f32 = _types(d, (state, sketch, basis, k_buf, v_buf, decay_buf, beta_buf))
+    n = numel(d)
+    _check(_lib.ssm_window_update_refresh(
+        ctypes.byref(d), _addr(state, "state", f32, n["state"]), _addr(sketch, "sketch", f32, n["sketch"]),
+        _addr(basis, "basis", f32, n["basis"]), _addr(k_buf, "k_buf", tin, n["k_buf"]), _addr(v_buf, "v_buf", tin, n["v_buf"]),
+        _addr(decay_buf, "decay_buf", f32, n["decay_buf"]), _addr(beta_buf, "beta_buf", f32, n["beta_buf"]),
+        int(n_tokens), _stream(stream)))
+
+
+def sketch_decode_step(d: Dims, sketch, basis, q, k_buf, v_buf, decay_buf, beta_buf, tau: int,
+                       y, *, k_t=None, v_t=None, decay_t=None, beta_t=None, stream=None) -> None:
+    tin, f32 = _types(d, (sketch, basis, q, k_buf, v_buf, decay_buf, beta_buf, y, k_t, v_t))
+    n = numel(d)
+    _check(_lib.ssm_sketch_decode_step(
+        ctypes.byref(d), _addr(sketch, "sketch", f32, n["sketch"]), _addr(basis, "basis", f32, n["basis"]),
+        _addr(q, "q", tin, n["q"]), _addr(k_t, "k_t", tin, n["k_t"]), _addr(v_t, "v_t", tin, n["v_t"]),
+        _addr(decay_t, "decay_t", f32, n["decay_t"]), _addr(beta_t, "beta_t", f32, n["beta_t"]),
+        _addr(k_buf, "k_buf", tin, n["k_buf"]), _addr(v_buf, "v_buf", tin, n["v_buf"]),
+        _addr(decay_buf, "decay_buf", f32, n["decay_buf"]), _addr(beta_buf, "beta_buf", f32, n["beta_buf"]),
+        int(tau), _addr(y, "y", f32, n["y"]), _stream(stream)))
+
+
+def full_read_decode_step(d: Dims, state, q, k_buf, v_buf, decay_buf, beta_buf, tau: int, y, *,
+                          k_t=None, v_t=None, decay_t=None, beta_t=None, stream=None) -> None:
+    tin, f32 = _types(d, (state, q, k_buf, v_buf, decay_buf, beta_buf, y, k_t, v_t))
+    n = numel(d)
+    _check(_lib.ssm_full_read_decode_step(
+        ctypes.byref(d), _addr(state, "state", f32, n["state"]), _addr(q, "q", tin, n["q"]),
+        _addr(k_t, "k_t", tin, n["k_t"]), _addr(v_t, "v_t", tin, n["v_t"]),
+        _addr(decay_t, "decay_t", f32, n["decay_t"]), _addr(beta_t, "beta_t", f32, n["beta_t"]),
+        _addr(k_buf, "k_buf", tin, n["k_buf"]), _addr(v_buf, "v_buf", tin, n["v_buf"]),
+        _addr(decay_buf, "decay_buf", f32, n["decay_buf"]), _addr(beta_buf, "beta_buf", f32, n["beta_buf"]),
+        int(tau), _addr(y, "y", f32, n["y"]), _stream(stream)))

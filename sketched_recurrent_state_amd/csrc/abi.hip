@@ -1,0 +1,293 @@
+// abi.hip -- the extern "C" entry points of libsketchssm.so: argument checks
+// on the host, then one asynchronous launch on the caller's stream. Nothing
+// here allocates, frees or synchronises. See include/sketchssm.h.
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "launch.hpp"
+#include "sketchssm.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+constexpr long long kMaxUnits = 1LL << 24;  // keeps every grid below 2^32 threads
+
+ssm_status fail(ssm_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+ssm_status ok() {
+  g_last_error.clear();
+  return SSM_OK;
+}
+
+bool in_set(int x, std::initializer_list<int> s) {
+  for (int v : s)
+    if (v == x) return true;
+  return false;
+}
+
+ssm_status check_dims(const ssm_dims* d, const char* fn) {
+  if (d == nullptr) return fail(SSM_E_NULL, "%s: dims is NULL", fn);
+  if (d->rule < SSM_MAMBA2 || d->rule > SSM_KDA)
+    return fail(SSM_E_RANGE, "%s: rule %d is not 0 (Mamba-2), 1 (GDN) or 2 (KDA)", fn, d->rule);
+  if (d->in_dtype != SSM_IN_BF16 && d->in_dtype != SSM_IN_F32)
+    return fail(SSM_E_RANGE, "%s: in_dtype %d is not 0 (bf16) or 1 (fp32)", fn, d->in_dtype);
+  if (d->batch < 0) return fail(SSM_E_SHAPE, "%s: batch %d < 0", fn, d->batch);
+  if (d->heads < 1) return fail(SSM_E_SHAPE, "%s: heads %d < 1", fn, d->heads);
+  if (!in_set(d->d_k, {16, 32, 64, 128}))
+    return fail(SSM_E_SHAPE, "%s: d_k %d not in {16, 32, 64, 128}", fn, d->d_k);
+  if (!in_set(d->d_v, {32, 64, 128}))
+    return fail(SSM_E_SHAPE, "%s: d_v %d not in {32, 64, 128}", fn, d->d_v);
+  if (d->window < 1 || d->window > 16)
+    return fail(SSM_E_SHAPE, "%s: window %d not in [1, 16]", fn, d->window);
+  const int rmax = d->d_k < 32 ? d->d_k : 32;
+  if (d->rank < 1 || d->rank > rmax)
+    return fail(SSM_E_SHAPE, "%s: rank %d not in [1, %d]", fn, d->rank, rmax);
+  if ((long long)d->batch * d->heads >= kMaxUnits)
+    return fail(SSM_E_SHAPE, "%s: batch*heads = %lld >= %lld", fn,
+                (long long)d->batch * d->heads, kMaxUnits);
+  return SSM_OK;
+}
+
+struct Arr {
+  const void* p;
+  size_t bytes;
+  bool output;
+  const char* name;
+};
+
+ssm_status check_arrays(const char* fn, std::initializer_list<Arr> arrs) {
+  for (const Arr& a : arrs) {
+    if (a.p != nullptr && (reinterpret_cast<uintptr_t>(a.p) & 15u) != 0)
+      return fail(SSM_E_ALIGN, "%s: %s (%p) is not 16-byte aligned", fn, a.name, a.p);
+  }
+  for (const Arr& a : arrs) {
+    if (a.p == nullptr || a.bytes == 0) continue;
+    for (const Arr& b : arrs) {
+      if (&a == &b || b.p == nullptr || b.bytes == 0) continue;
+      if (!a.output && !b.output) continue;
+      const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), a1 = a0 + a.bytes;
+      const uintptr_t b0 = reinterpret_cast<uintptr_t>(b.p), b1 = b0 + b.bytes;
+      if (a0 < b1 && b0 < a1)
+        return fail(SSM_E_ALIAS, "%s: %s overlaps %s", fn, a.name, b.name);
+    }
+  }
+  return SSM_OK;
+}
+
+struct Sizes {
+  size_t units, elem, state, sketch, basis, kbuf, vbuf, dbuf, bbuf, qk, v, dtok, btok, y;
+};
+
+Sizes sizes_of(const ssm_dims& d) {
+  Sizes z;
+  z.units = (size_t)d.batch * (size_t)d.heads;
+  z.elem = d.in_dtype == SSM_IN_BF16 ? 2 : 4;
+  const size_t dstr = d.rule == SSM_KDA ? (size_t)d.d_k : 1;
+  const size_t W = (size_t)d.window;
+  z.state = z.units * d.d_k * d.d_v * 4;
+  z.sketch = z.units * d.rank * d.d_v * 4;
+  z.basis = (size_t)d.heads * d.rank * d.d_k * 4;
+  z.kbuf = z.units * W * d.d_k * z.elem;
+  z.vbuf = z.units * W * d.d_v * z.elem;
+  z.dbuf = z.units * W * dstr * 4;
+  z.bbuf = z.units * W * 4;
+  z.qk = z.units * d.d_k * z.elem;
+  z.v = z.units * d.d_v * z.elem;
+  z.dtok = z.units * dstr * 4;
+  z.btok = z.units * 4;
+  z.y = z.units * d.d_v * 4;
+  return z;
+}
+
+ssm_status check_beta(const ssm_dims& d, const void* beta, const char* what, const char* fn) {
+  if (d.rule == SSM_MAMBA2 && beta != nullptr)
+    return fail(SSM_E_RANGE, "%s: %s must be NULL for Mamba-2", fn, what);
+  if (d.rule != SSM_MAMBA2 && beta == nullptr)
+    return fail(SSM_E_NULL, "%s: %s is NULL (required by the delta rules)", fn, what);
+  return SSM_OK;
+}
+
+// The current-token pointers of a fused append: all present or all absent.
+ssm_status check_token(const ssm_dims& d, const void* k_t, const void* v_t, const void* d_t,
+                       const void* b_t, const char* fn) {
+  if (k_t == nullptr) {
+    if (v_t != nullptr || d_t != nullptr || b_t != nullptr)
+      return fail(SSM_E_RANGE, "%s: k_t is NULL but v_t/decay_t/beta_t are not", fn);
+    return SSM_OK;
+  }
+  if (v_t == nullptr) return fail(SSM_E_NULL, "%s: v_t is NULL", fn);
+  if (d_t == nullptr) return fail(SSM_E_NULL, "%s: decay_t is NULL", fn);
+  return check_beta(d, b_t, "beta_t", fn);
+}
+
+ssm_status check_buffers(const ssm_dims& d, const void* k_buf, const void* v_buf,
+                         const void* decay_buf, const void* beta_buf, const char* fn) {
+  if (k_buf == nullptr) return fail(SSM_E_NULL, "%s: k_buf is NULL", fn);
+  if (v_buf == nullptr) return fail(SSM_E_NULL, "%s: v_buf is NULL", fn);
+  if (decay_buf == nullptr) return fail(SSM_E_NULL, "%s: decay_buf is NULL", fn);
+  return check_beta(d, beta_buf, "beta_buf", fn);
+}
+
+ssm_status launched(hipError_t e, const char* fn) {
+  if (e != hipSuccess) return fail(SSM_E_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t ssm_abi_version(void) { return SSM_ABI_VERSION; }
+
+const char* ssm_status_string(int32_t status) {
+  switch (status) {
+    case SSM_OK: return "ok";
+    case SSM_E_NULL: return "a required pointer is NULL";
+    case SSM_E_SHAPE: return "unsupported or inconsistent dimensions";
+    case SSM_E_ALIGN: return "a pointer is not 16-byte aligned";
+    case SSM_E_RANGE: return "an argument is out of range";
+    case SSM_E_ALIAS: return "an output overlaps an input";
+    case SSM_E_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+const char* ssm_last_error(void) { return g_last_error.c_str(); }
+
+ssm_status ssm_buffer_append(const ssm_dims* d, const void* k_t, const void* v_t,
+                             const float* decay_t, const float* beta_t, void* k_buf, void* v_buf,
+                             float* decay_buf, float* beta_buf, int32_t slot, void* stream) {
+  static const char* fn = "ssm_buffer_append";
+  ssm_status st = check_dims(d, fn);
+  if (st != SSM_OK) return st;
+  if (slot < 0 || slot >= d->window)
+    return fail(SSM_E_RANGE, "%s: slot %d not in [0, %d)", fn, slot, d->window);
+  if (d->batch == 0) return ok();
+  if (k_t == nullptr) return fail(SSM_E_NULL, "%s: k_t is NULL", fn);
+  if ((st = check_token(*d, k_t, v_t, decay_t, beta_t, fn)) != SSM_OK) return st;
+  if ((st = check_buffers(*d, k_buf, v_buf, decay_buf, beta_buf, fn)) != SSM_OK) return st;
+  const Sizes z = sizes_of(*d);
+  st = check_arrays(fn, {{k_t, z.qk, false, "k_t"}, {v_t, z.v, false, "v_t"},
+                         {decay_t, z.dtok, false, "decay_t"}, {beta_t, z.btok, false, "beta_t"},
+                         {k_buf, z.kbuf, true, "k_buf"}, {v_buf, z.vbuf, true, "v_buf"},
+                         {decay_buf, z.dbuf, true, "decay_buf"},
+                         {beta_buf, z.bbuf, true, "beta_buf"}});
+  if (st != SSM_OK) return st;
+  (void)hipGetLastError();
+  return launched(ssm::launch_buffer_append(*d, k_t, v_t, decay_t, beta_t, k_buf, v_buf,
+                                            decay_buf, beta_buf, slot,
+                                            reinterpret_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+ssm_status ssm_window_update_refresh(const ssm_dims* d, float* state, float* sketch,
+                                     const float* basis, const void* k_buf, const void* v_buf,
+                                     const float* decay_buf, const float* beta_buf,
+                                     int32_t n_tokens, void* stream) {
+  static const char* fn = "ssm_window_update_refresh";
+  ssm_status st = check_dims(d, fn);
+  if (st != SSM_OK) return st;
+  if (n_tokens < 0 || n_tokens > d->window)
+    return fail(SSM_E_RANGE, "%s: n_tokens %d not in [0, %d]", fn, n_tokens, d->window);
+  if (d->batch == 0) return ok();
+  if (state == nullptr) return fail(SSM_E_NULL, "%s: state is NULL", fn);
+  if (sketch != nullptr && basis == nullptr)
+    return fail(SSM_E_NULL, "%s: basis is NULL but a sketch is requested", fn);
+  if (n_tokens > 0) {
+    if ((st = check_buffers(*d, k_buf, v_buf, decay_buf, beta_buf, fn)) != SSM_OK) return st;
+  }
+  if (n_tokens == 0 && sketch == nullptr) return ok();  // nothing to apply, nothing to store
+  const Sizes z = sizes_of(*d);
+  const bool tok = n_tokens > 0;
+  st = check_arrays(fn, {{state, z.state, true, "state"}, {sketch, z.sketch, true, "sketch"},
+                         {basis, z.basis, false, "basis"},
+                         {tok ? k_buf : nullptr, z.kbuf, false, "k_buf"},
+                         {tok ? v_buf : nullptr, z.vbuf, false, "v_buf"},
+                         {tok ? decay_buf : nullptr, z.dbuf, false, "decay_buf"},
+                         {tok ? beta_buf : nullptr, z.bbuf, false, "beta_buf"}});
+  if (st != SSM_OK) return st;
+  (void)hipGetLastError();
+  return launched(ssm::launch_update_refresh(*d, state, sketch, basis, k_buf, v_buf, decay_buf,
+                                             beta_buf, n_tokens,
+                                             reinterpret_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+ssm_status ssm_sketch_decode_step(const ssm_dims* d, const float* sketch, const float* basis,
+                                  const void* q, const void* k_t, const void* v_t,
+                                  const float* decay_t, const float* beta_t, void* k_buf,
+                                  void* v_buf, float* decay_buf, float* beta_buf, int32_t tau,
+                                  float* y, void* stream) {
+  static const char* fn = "ssm_sketch_decode_step";
+  ssm_status st = check_dims(d, fn);
+  if (st != SSM_OK) return st;
+  if (tau < 1 || tau > d->window)
+    return fail(SSM_E_RANGE, "%s: tau %d not in [1, %d]", fn, tau, d->window);
+  if (d->batch == 0) return ok();
+  if (sketch == nullptr) return fail(SSM_E_NULL, "%s: sketch is NULL", fn);
+  if (basis == nullptr) return fail(SSM_E_NULL, "%s: basis is NULL", fn);
+  if (q == nullptr) return fail(SSM_E_NULL, "%s: q is NULL", fn);
+  if (y == nullptr) return fail(SSM_E_NULL, "%s: y is NULL", fn);
+  if ((st = check_token(*d, k_t, v_t, decay_t, beta_t, fn)) != SSM_OK) return st;
+  if ((st = check_buffers(*d, k_buf, v_buf, decay_buf, beta_buf, fn)) != SSM_OK) return st;
+  const Sizes z = sizes_of(*d);
+  const bool fused = k_t != nullptr;
+  st = check_arrays(fn, {{sketch, z.sketch, false, "sketch"}, {basis, z.basis, false, "basis"},
+                         {q, z.qk, false, "q"}, {k_t, z.qk, false, "k_t"}, {v_t, z.v, false, "v_t"},
+                         {decay_t, z.dtok, false, "decay_t"}, {beta_t, z.btok, false, "beta_t"},
+                         {k_buf, z.kbuf, fused, "k_buf"}, {v_buf, z.vbuf, fused, "v_buf"},
+                         {decay_buf, z.dbuf, fused, "decay_buf"},
+                         {beta_buf, z.bbuf, fused, "beta_buf"}, {y, z.y, true, "y"}});
+  if (st != SSM_OK) return st;
+  (void)hipGetLastError();
+  return launched(ssm::launch_sketch_decode(*d, sketch, basis, q, k_t, v_t, decay_t, beta_t,
+                                            k_buf, v_buf, decay_buf, beta_buf, tau, y,
+                                            reinterpret_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+ssm_status ssm_full_read_decode_step(const ssm_dims* d, const float* state, const void* q,
+                                     const void* k_t, const void* v_t, const float* decay_t,
+                                     const float* beta_t, void* k_buf, void* v_buf,
+                                     float* decay_buf, float* beta_buf, int32_t tau, float* y,
+                                     void* stream) {
+  static const char* fn = "ssm_full_read_decode_step";
+  ssm_status st = check_dims(d, fn);
+  if (st != SSM_OK) return st;
+  if (tau < 1 || tau > d->window)
+    return fail(SSM_E_RANGE, "%s: tau %d not in [1, %d]", fn, tau, d->window);
+  if (d->batch == 0) return ok();
+  if (state == nullptr) return fail(SSM_E_NULL, "%s: state is NULL", fn);
+  if (q == nullptr) return fail(SSM_E_NULL, "%s: q is NULL", fn);
+  if (y == nullptr) return fail(SSM_E_NULL, "%s: y is NULL", fn);
+  if ((st = check_token(*d, k_t, v_t, decay_t, beta_t, fn)) != SSM_OK) return st;
+  if ((st = check_buffers(*d, k_buf, v_buf, decay_buf, beta_buf, fn)) != SSM_OK) return st;
+  const Sizes z = sizes_of(*d);
+  const bool fused = k_t != nullptr;
+  st = check_arrays(fn, {{state, z.state, false, "state"}, {q, z.qk, false, "q"},
+                         {k_t, z.qk, false, "k_t"}, {v_t, z.v, false, "v_t"},
+                         {decay_t, z.dtok, false, "decay_t"}, {beta_t, z.btok, false, "beta_t"},
+                         {k_buf, z.kbuf, fused, "k_buf"}, {v_buf, z.vbuf, fused, "v_buf"},
+                         {decay_buf, z.dbuf, fused, "decay_buf"},
+                         {beta_buf, z.bbuf, fused, "beta_buf"}, {y, z.y, true, "y"}});
+  if (st != SSM_OK) return st;
+  (void)hipGetLastError();
+  return launched(ssm::launch_full_read_decode(*d, state, q, k_t, v_t, decay_t, beta_t, k_buf,
+                                               v_buf, decay_buf, beta_buf, tau, y,
+                                               reinterpret_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+}  // extern "C"

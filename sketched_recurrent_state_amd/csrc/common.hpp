@@ -1,0 +1,202 @@
+// common.hpp -- device helpers shared by the SketchSSM kernels (gfx950 only).
+//
+// Lane layouts used by the kernels:
+//  * state tile ("tile"): one workgroup per (sequence, head) unit, one wave per
+//    32-column block of the d_k x d_v state. Lane l owns 4 adjacent columns
+//    (cg = l % 8, one 128-bit load per row) of d_k/8 contiguous rows
+//    (rg = l / 8). A reduction over d_k is a sum over the 8 lanes that share
+//    cg, i.e. over lane bits 3, 4 and 5: DPP row_ror:8 for bit 3 and the
+//    gfx950 permlane16/permlane32 swaps for bits 4 and 5.
+//  * group ("g16"): 16 lanes (one DPP row) per unit, each holding d_k/16 key
+//    elements and d_v/16 value elements; reductions stay inside the row.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssm {
+
+enum Rule { MAMBA2 = 0, GDN = 1, KDA = 2 };
+
+typedef uint16_t bf16_t;  // bf16 bit pattern
+
+// ---------------------------------------------------------------------------
+// input loads: E consecutive elements of T -> float
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+template <typename T, int E>
+struct Vec;
+
+template <int E>
+struct Vec<float, E> {
+  static __device__ __forceinline__ void load(const float* __restrict__ p, float* out) {
+    if constexpr (E % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < E; i += 4) {
+        float4 x = *reinterpret_cast<const float4*>(p + i);
+        out[i] = x.x; out[i + 1] = x.y; out[i + 2] = x.z; out[i + 3] = x.w;
+      }
+    } else if constexpr (E == 2) {
+      float2 x = *reinterpret_cast<const float2*>(p);
+      out[0] = x.x; out[1] = x.y;
+    } else {
+#pragma unroll
+      for (int i = 0; i < E; ++i) out[i] = p[i];
+    }
+  }
+  static __device__ __forceinline__ void store(float* __restrict__ p, const float* in) {
+    if constexpr (E % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < E; i += 4)
+        *reinterpret_cast<float4*>(p + i) = make_float4(in[i], in[i + 1], in[i + 2], in[i + 3]);
+    } else if constexpr (E == 2) {
+      *reinterpret_cast<float2*>(p) = make_float2(in[0], in[1]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < E; ++i) p[i] = in[i];
+    }
+  }
+  static __device__ __forceinline__ void copy(const float* __restrict__ src, float* __restrict__ dst) {
+    if constexpr (E % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < E; i += 4)
+        *reinterpret_cast<float4*>(dst + i) = *reinterpret_cast<const float4*>(src + i);
+    } else if constexpr (E == 2) {
+      *reinterpret_cast<float2*>(dst) = *reinterpret_cast<const float2*>(src);
+    } else {
+#pragma unroll
+      for (int i = 0; i < E; ++i) dst[i] = src[i];
+    }
+  }
+};
+
+template <int E>
+struct Vec<bf16_t, E> {
+  static __device__ __forceinline__ void load(const bf16_t* __restrict__ p, float* out) {
+    if constexpr (E % 8 == 0) {
+#pragma unroll
+      for (int i = 0; i < E; i += 8) {
+        uint4 x = *reinterpret_cast<const uint4*>(p + i);
+        out[i + 0] = bf16_lo(x.x); out[i + 1] = bf16_hi(x.x);
+        out[i + 2] = bf16_lo(x.y); out[i + 3] = bf16_hi(x.y);
+        out[i + 4] = bf16_lo(x.z); out[i + 5] = bf16_hi(x.z);
+        out[i + 6] = bf16_lo(x.w); out[i + 7] = bf16_hi(x.w);
+      }
+    } else if constexpr (E == 4) {
+      uint2 x = *reinterpret_cast<const uint2*>(p);
+      out[0] = bf16_lo(x.x); out[1] = bf16_hi(x.x);
+      out[2] = bf16_lo(x.y); out[3] = bf16_hi(x.y);
+    } else if constexpr (E == 2) {
+      uint32_t x = *reinterpret_cast<const uint32_t*>(p);
+      out[0] = bf16_lo(x); out[1] = bf16_hi(x);
+    } else {
+#pragma unroll
+      for (int i = 0; i < E; ++i) out[i] = __uint_as_float(uint32_t(p[i]) << 16);
+    }
+  }
+  static __device__ __forceinline__ void copy(const bf16_t* __restrict__ src, bf16_t* __restrict__ dst) {
+    if constexpr (E % 8 == 0) {
+#pragma unroll
+      for (int i = 0; i < E; i += 8)
+        *reinterpret_cast<uint4*>(dst + i) = *reinterpret_cast<const uint4*>(src + i);
+    } else if constexpr (E == 4) {
+      *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
+    } else if constexpr (E == 2) {
+      *reinterpret_cast<uint32_t*>(dst) = *reinterpret_cast<const uint32_t*>(src);
+    } else {
+#pragma unroll
+      for (int i = 0; i < E; ++i) dst[i] = src[i];
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// cross-lane primitives
+// ---------------------------------------------------------------------------
+// DPP controls (GCN/CDNA encoding)
+constexpr int DPP_QUAD_1032 = 0xB1;  // quad_perm:[1,0,3,2]
+constexpr int DPP_QUAD_2301 = 0x4E;  // quad_perm:[2,3,0,1]
+constexpr int DPP_ROR4 = 0x124;      // row_ror:4
+constexpr int DPP_ROR8 = 0x128;      // row_ror:8
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// a + (the same register of lane l ^ 16): permlane16_swap exchanges odd rows of
+// the first operand with even rows of the second; summing both results gives
+// every lane the pair sum.
+__device__ __forceinline__ float xsum16(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// a + (the same register of lane l ^ 32), via permlane32_swap.
+__device__ __forceinline__ float xsum32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Halving exchange over lane bit 4: afterwards lanes with bit 4 clear hold
+// lo + partner's lo, lanes with bit 4 set hold hi + partner's hi (in `lo`).
+__device__ __forceinline__ void halve16(float& lo, float hi) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+  lo = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Same over lane bit 5.
+__device__ __forceinline__ void halve32(float& lo, float hi) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+  lo = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Same over lane bit 3 (inside a 16-lane row): row_ror:8 reaches lane l ^ 8.
+__device__ __forceinline__ float halve8(float lo, float hi, bool upper) {
+  float keep = upper ? hi : lo;
+  float send = upper ? lo : hi;
+  return keep + dpp<DPP_ROR8>(send);
+}
+
+// Sum over the 8 lanes that differ in bits 3..5 (the tile layout's d_k split).
+__device__ __forceinline__ float tile_allreduce(float x) {
+  x += dpp<DPP_ROR8>(x);
+  x = xsum16(x);
+  return xsum32(x);
+}
+
+__device__ __forceinline__ float4 tile_allreduce(float4 v) {
+  return make_float4(tile_allreduce(v.x), tile_allreduce(v.y), tile_allreduce(v.z),
+                     tile_allreduce(v.w));
+}
+
+// Sum over the 16 lanes of a DPP row (the g16 layout).
+__device__ __forceinline__ float row_allreduce(float x) {
+  x += dpp<DPP_QUAD_1032>(x);
+  x += dpp<DPP_QUAD_2301>(x);
+  x += dpp<DPP_ROR4>(x);
+  x += dpp<DPP_ROR8>(x);
+  return x;
+}
+
+// ---------------------------------------------------------------------------
+// float4 helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float4 f4(float a) { return make_float4(a, a, a, a); }
+__device__ __forceinline__ float4 add4(float4 a, float4 b) {
+  return make_float4(a.x + b.x, a.y + b.y, a.z + b.z, a.w + b.w);
+}
+__device__ __forceinline__ float4 sub4(float4 a, float4 b) {
+  return make_float4(a.x - b.x, a.y - b.y, a.z - b.z, a.w - b.w);
+}
+__device__ __forceinline__ float4 scale4(float a, float4 b) {
+  return make_float4(a * b.x, a * b.y, a * b.z, a * b.w);
+}
+// a * b + c, componentwise with scalar a
+__device__ __forceinline__ float4 fma4(float a, float4 b, float4 c) {
+  return make_float4(fmaf(a, b.x, c.x), fmaf(a, b.y, c.y), fmaf(a, b.z, c.z), fmaf(a, b.w, c.w));
+}
+
+}  // namespace ssm

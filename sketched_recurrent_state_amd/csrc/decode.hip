@@ -1,0 +1,237 @@
+// decode.hip -- the per-step reads: the sketch read (every decode step of
+// SketchSSM) and the exact read of the window-start state (the comparison
+// path that still reads all of S).
+//
+// Both walk the window buffer newest to oldest from u = q. With token i's
+// transition M_i and write weight b_i (beta, or 1 for Mamba-2):
+//   s_i = k_i . u,  intra += b_i s_i v_i,  u <- M_i^T u
+// which leaves q~ = A^T q in u and R^T q in intra, where S_tau = A S_win + R
+// (within a window only the queries change: agihunt.info summary of SketchSSM,
+// "Mechanism details"). Then
+//   sketch read:  c = B q~,  y = Sk^T c + intra   (readsearch.ai listing of
+//                 arXiv 2609.33051, Abstract: each step combines the stored
+//                 basis outputs with query-dependent coefficients)
+//   exact read:   y = S_win^T q~ + intra.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ssm {
+
+namespace {
+
+// u <- M^T u for one token on E key elements held by this lane, given s = k . u.
+//   Mamba-2: M^T u = a u;  GDN: a (u - beta s k);  KDA: alpha (.) (u - beta s k)
+template <int RULE, int E>
+__device__ __forceinline__ void carry_back(float* u, const float* kk, const float* a, float bs) {
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if constexpr (RULE == MAMBA2) {
+      u[e] = a[0] * u[e];
+    } else if constexpr (RULE == GDN) {
+      u[e] = a[0] * fmaf(-bs, kk[e], u[e]);
+    } else {
+      u[e] = a[e] * fmaf(-bs, kk[e], u[e]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// sketch read: 16 lanes (one DPP row) per unit
+// ---------------------------------------------------------------------------
+template <int RULE, int DK, int DV, typename TIN>
+__global__ void __launch_bounds__(256)
+sketch_decode_kernel(const float* __restrict__ sketch, const float* __restrict__ basis,
+                     const TIN* __restrict__ q, const TIN* __restrict__ k_t,
+                     const TIN* __restrict__ v_t, const float* __restrict__ d_t,
+                     const float* __restrict__ b_t, TIN* __restrict__ kbuf,
+                     TIN* __restrict__ vbuf, float* __restrict__ dbuf, float* __restrict__ bbuf,
+                     float* __restrict__ y, int units, int heads, int window, int rank, int tau) {
+  constexpr int G = 16;
+  constexpr int EK = DK / G, EV = DV / G;
+  constexpr int DSTR = (RULE == KDA) ? DK : 1;
+  constexpr int EA = (RULE == KDA) ? EK : 1;  // gate values per lane and token
+
+  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+  const int unit = gid / G, sub = gid % G;
+  if (unit >= units) return;  // whole 16-lane groups leave together
+  const int head = unit % heads;
+  const size_t slot0 = (size_t)unit * window;
+  const bool fused = (k_t != nullptr);
+
+  float u[EK];
+  Vec<TIN, EK>::load(q + (size_t)unit * DK + sub * EK, u);
+  float acc[EV];
+#pragma unroll
+  for (int e = 0; e < EV; ++e) acc[e] = 0.f;
+
+  for (int i = tau - 1; i >= 0; --i) {
+    const bool cur = fused && (i == tau - 1);
+    const size_t slot = slot0 + i;
+    const TIN* kp = cur ? k_t + (size_t)unit * DK : kbuf + slot * DK;
+    const TIN* vp = cur ? v_t + (size_t)unit * DV : vbuf + slot * DV;
+    const float* dp = cur ? d_t + (size_t)unit * DSTR : dbuf + slot * DSTR;
+    float kk[EK], vv[EV], a[EA];
+    Vec<TIN, EK>::load(kp + sub * EK, kk);
+    Vec<TIN, EV>::load(vp + sub * EV, vv);
+    if constexpr (RULE == KDA) {
+      Vec<float, EK>::load(dp + sub * EK, a);
+    } else {
+      a[0] = dp[0];
+    }
+    float b = 1.f;
+    if constexpr (RULE != MAMBA2) b = cur ? b_t[unit] : bbuf[slot];
+    if (cur) {  // fused token append into slot tau-1
+      Vec<TIN, EK>::copy(kp + sub * EK, kbuf + slot * DK + sub * EK);
+      Vec<TIN, EV>::copy(vp + sub * EV, vbuf + slot * DV + sub * EV);
+      if constexpr (RULE == KDA) {
+        Vec<float, EK>::store(dbuf + slot * DK + sub * EK, a);
+      } else {
+        if (sub == 0) dbuf[slot] = a[0];
+      }
+      if constexpr (RULE != MAMBA2) {
+        if (sub == 0) bbuf[slot] = b;
+      }
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < EK; ++e) s = fmaf(kk[e], u[e], s);
+    s = row_allreduce(s);
+    const float bs = b * s;
+#pragma unroll
+    for (int e = 0; e < EV; ++e) acc[e] = fmaf(bs, vv[e], acc[e]);
+    carry_back<RULE, EK>(u, kk, a, bs);
+  }
+
+  // c_m = b_m . q~ ; y = intra + sum_m c_m Sk[m]
+  const float* Bh = basis + (size_t)head * rank * DK + sub * EK;
+  const float* Sku = sketch + (size_t)unit * rank * DV + sub * EV;
+#pragma unroll 4
+  for (int m = 0; m < rank; ++m) {
+    float bm[EK], sk[EV];
+    Vec<float, EK>::load(Bh + (size_t)m * DK, bm);
+    Vec<float, EV>::load(Sku + (size_t)m * DV, sk);
+    float c = 0.f;
+#pragma unroll
+    for (int e = 0; e < EK; ++e) c = fmaf(bm[e], u[e], c);
+    c = row_allreduce(c);
+#pragma unroll
+    for (int e = 0; e < EV; ++e) acc[e] = fmaf(c, sk[e], acc[e]);
+  }
+  Vec<float, EV>::store(y + (size_t)unit * DV + sub * EV, acc);
+}
+
+// ---------------------------------------------------------------------------
+// exact read of the window-start state: the state tile layout, one workgroup
+// per unit, each wave a 32-column block (it walks the buffer itself).
+// ---------------------------------------------------------------------------
+template <int RULE, int DK, int DV, typename TIN>
+__global__ void __launch_bounds__(2 * DV)
+full_read_kernel(const float* __restrict__ state, const TIN* __restrict__ q,
+                 const TIN* __restrict__ k_t, const TIN* __restrict__ v_t,
+                 const float* __restrict__ d_t, const float* __restrict__ b_t,
+                 TIN* __restrict__ kbuf, TIN* __restrict__ vbuf, float* __restrict__ dbuf,
+                 float* __restrict__ bbuf, float* __restrict__ y, int window, int tau) {
+  constexpr int RPL = DK / 8;
+  constexpr int DSTR = (RULE == KDA) ? DK : 1;
+  constexpr int EA = (RULE == KDA) ? RPL : 1;
+
+  const int unit = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int cg = lane & 7, rg = lane >> 3;
+  const int col = wave * 32 + cg * 4;
+  const int row0 = rg * RPL;
+  const size_t slot0 = (size_t)unit * window;
+  const bool fused = (k_t != nullptr);
+
+  const float* Su = state + (size_t)unit * (DK * DV);
+  float4 s[RPL];
+#pragma unroll
+  for (int m = 0; m < RPL; ++m)
+    s[m] = *reinterpret_cast<const float4*>(Su + (size_t)(row0 + m) * DV + col);
+
+  float u[RPL];
+  Vec<TIN, RPL>::load(q + (size_t)unit * DK + row0, u);
+  float4 acc = f4(0.f);
+  for (int i = tau - 1; i >= 0; --i) {
+    const bool cur = fused && (i == tau - 1);
+    const size_t slot = slot0 + i;
+    const TIN* kp = cur ? k_t + (size_t)unit * DK : kbuf + slot * DK;
+    const TIN* vp = cur ? v_t + (size_t)unit * DV : vbuf + slot * DV;
+    const float* dp = cur ? d_t + (size_t)unit * DSTR : dbuf + slot * DSTR;
+    float kk[RPL], vv[4], a[EA];
+    Vec<TIN, RPL>::load(kp + row0, kk);
+    Vec<TIN, 4>::load(vp + col, vv);
+    if constexpr (RULE == KDA) {
+      Vec<float, RPL>::load(dp + row0, a);
+    } else {
+      a[0] = dp[0];
+    }
+    float b = 1.f;
+    if constexpr (RULE != MAMBA2) b = cur ? b_t[unit] : bbuf[slot];
+    if (cur) {  // fused token append into slot tau-1
+      if (wave == 0 && cg == 0) {
+        Vec<TIN, RPL>::copy(kp + row0, kbuf + slot * DK + row0);
+        if constexpr (RULE == KDA) Vec<float, RPL>::store(dbuf + slot * DK + row0, a);
+      }
+      if (rg == 0) Vec<TIN, 4>::copy(vp + col, vbuf + slot * DV + col);
+      if (tid == 0) {
+        if constexpr (RULE != KDA) dbuf[slot] = a[0];
+        if constexpr (RULE != MAMBA2) bbuf[slot] = b;
+      }
+    }
+    float sd = 0.f;
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) sd = fmaf(kk[m], u[m], sd);
+    sd = tile_allreduce(sd);
+    const float bs = b * sd;
+    acc = fma4(bs, make_float4(vv[0], vv[1], vv[2], vv[3]), acc);
+    carry_back<RULE, RPL>(u, kk, a, bs);
+  }
+
+  float4 out = f4(0.f);
+#pragma unroll
+  for (int m = 0; m < RPL; ++m) out = fma4(u[m], s[m], out);
+  out = add4(tile_allreduce(out), acc);
+  if (rg == 0) *reinterpret_cast<float4*>(y + (size_t)unit * DV + col) = out;
+}
+
+}  // namespace
+
+hipError_t launch_sketch_decode(const ssm_dims& d, const float* sketch, const float* basis,
+                                const void* q, const void* k_t, const void* v_t,
+                                const float* decay_t, const float* beta_t, void* k_buf,
+                                void* v_buf, float* decay_buf, float* beta_buf, int tau, float* y,
+                                hipStream_t stream) {
+  const unsigned units = (unsigned)d.batch * (unsigned)d.heads;
+  const unsigned blocks = (units * 16u + 255u) / 256u;
+  return dispatch(d.rule, d.in_dtype, d.d_k, d.d_v, [&](auto R, auto DK, auto DV, auto T) {
+    using TIN = typename decltype(T)::type;
+    constexpr int kR = decltype(R)::value, kDK = decltype(DK)::value, kDV = decltype(DV)::value;
+    hipLaunchKernelGGL((sketch_decode_kernel<kR, kDK, kDV, TIN>), dim3(blocks), dim3(256), 0,
+                       stream, sketch, basis, static_cast<const TIN*>(q),
+                       static_cast<const TIN*>(k_t), static_cast<const TIN*>(v_t), decay_t,
+                       beta_t, static_cast<TIN*>(k_buf), static_cast<TIN*>(v_buf), decay_buf,
+                       beta_buf, y, (int)units, d.heads, d.window, d.rank, tau);
+    return hipGetLastError();
+  });
+}
+
+hipError_t launch_full_read_decode(const ssm_dims& d, const float* state, const void* q,
+                                   const void* k_t, const void* v_t, const float* decay_t,
+                                   const float* beta_t, void* k_buf, void* v_buf,
+                                   float* decay_buf, float* beta_buf, int tau, float* y,
+                                   hipStream_t stream) {
+  const unsigned units = (unsigned)d.batch * (unsigned)d.heads;
+  return dispatch(d.rule, d.in_dtype, d.d_k, d.d_v, [&](auto R, auto DK, auto DV, auto T) {
+    using TIN = typename decltype(T)::type;
+    constexpr int kR = decltype(R)::value, kDK = decltype(DK)::value, kDV = decltype(DV)::value;
+    hipLaunchKernelGGL((full_read_kernel<kR, kDK, kDV, TIN>), dim3(units), dim3(2 * kDV), 0,
+                       stream, state, static_cast<const TIN*>(q), static_cast<const TIN*>(k_t),
+                       static_cast<const TIN*>(v_t), decay_t, beta_t, static_cast<TIN*>(k_buf),
+                       static_cast<TIN*>(v_buf), decay_buf, beta_buf, y, d.window, tau);
+    return hipGetLastError();
+  });
+}
+
+}  // namespace ssm

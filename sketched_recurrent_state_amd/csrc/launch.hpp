@@ -1,0 +1,78 @@
+// launch.hpp -- internal interface between the C ABI (abi.hip) and the kernel
+// translation units. Arguments here are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+#include "sketchssm.h"
+
+namespace ssm {
+
+template <typename T>
+struct type_tag {
+  using type = T;
+};
+
+// Calls f(rule, d_k, d_v, type_tag<input type>) with compile-time constants for
+// every supported combination; returns hipErrorInvalidValue for anything else.
+template <typename F>
+hipError_t dispatch(int rule, int in_dtype, int dk, int dv, F&& f) {
+  auto with_dv = [&](auto R, auto DK, auto T) -> hipError_t {
+    switch (dv) {
+      case 32: return f(R, DK, std::integral_constant<int, 32>{}, T);
+      case 64: return f(R, DK, std::integral_constant<int, 64>{}, T);
+      case 128: return f(R, DK, std::integral_constant<int, 128>{}, T);
+    }
+    return hipErrorInvalidValue;
+  };
+  auto with_dk = [&](auto R, auto T) -> hipError_t {
+    switch (dk) {
+      case 16: return with_dv(R, std::integral_constant<int, 16>{}, T);
+      case 32: return with_dv(R, std::integral_constant<int, 32>{}, T);
+      case 64: return with_dv(R, std::integral_constant<int, 64>{}, T);
+      case 128: return with_dv(R, std::integral_constant<int, 128>{}, T);
+    }
+    return hipErrorInvalidValue;
+  };
+  auto with_t = [&](auto R) -> hipError_t {
+    if (in_dtype == SSM_IN_BF16) return with_dk(R, type_tag<uint16_t>{});
+    if (in_dtype == SSM_IN_F32) return with_dk(R, type_tag<float>{});
+    return hipErrorInvalidValue;
+  };
+  switch (rule) {
+    case SSM_MAMBA2: return with_t(std::integral_constant<int, SSM_MAMBA2>{});
+    case SSM_GDN: return with_t(std::integral_constant<int, SSM_GDN>{});
+    case SSM_KDA: return with_t(std::integral_constant<int, SSM_KDA>{});
+  }
+  return hipErrorInvalidValue;
+}
+
+// Bytes of dynamic LDS the update kernel needs for n staged tokens.
+size_t update_refresh_lds_bytes(const ssm_dims& d, int n_tokens, bool refresh);
+
+hipError_t launch_update_refresh(const ssm_dims& d, float* state, float* sketch,
+                                 const float* basis, const void* k_buf, const void* v_buf,
+                                 const float* decay_buf, const float* beta_buf, int n_tokens,
+                                 hipStream_t stream);
+
+hipError_t launch_sketch_decode(const ssm_dims& d, const float* sketch, const float* basis,
+                                const void* q, const void* k_t, const void* v_t,
+                                const float* decay_t, const float* beta_t, void* k_buf,
+                                void* v_buf, float* decay_buf, float* beta_buf, int tau, float* y,
+                                hipStream_t stream);
+
+hipError_t launch_full_read_decode(const ssm_dims& d, const float* state, const void* q,
+                                   const void* k_t, const void* v_t, const float* decay_t,
+                                   const float* beta_t, void* k_buf, void* v_buf,
+                                   float* decay_buf, float* beta_buf, int tau, float* y,
+                                   hipStream_t stream);
+
+hipError_t launch_buffer_append(const ssm_dims& d, const void* k_t, const void* v_t,
+                                const float* decay_t, const float* beta_t, void* k_buf,
+                                void* v_buf, float* decay_buf, float* beta_buf, int slot,
+                                hipStream_t stream);
+
+}  // namespace ssm

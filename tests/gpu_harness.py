@@ -1,0 +1,162 @@
+"""Shared machinery of the GPU parity tests: seeded inputs on the device, the
+decode run through the library, the oracle on sampled units, and the
+comparison at the stated tolerances.
+
+Tolerances (fp32 state, bf16 inputs): outputs within 1e-3 relative per
+(unit, step) for both reads, state and sketch within 1e-4 relative per unit
+after every window. The error of an output vector is ||got - ref|| / max(||ref||,
+1e-6 * rms_rows ||ref||); the state's is the Frobenius ratio per unit.
+"""
+from __future__ import annotations
+
+import sys
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import torch
+
+import oracle
+import workloads
+import sketched_recurrent_state_amd as ssm
+from sketched_recurrent_state_amd.decoder import WindowedDecoder
+
+Y_TOL = 1e-3
+S_TOL = 1e-4
+
+
+def note(msg: str) -> None:
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def dims_of(cfg: workloads.Config) -> ssm.Dims:
+    return ssm.Dims.make(cfg.rule, cfg.in_dtype, cfg.batch, cfg.heads, cfg.d_k, cfg.d_v,
+                         cfg.window, cfg.rank)
+
+
+def _to_dev(x: np.ndarray, dev) -> torch.Tensor:
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x)).to(dev)
+
+
+class Inputs:
+    """Every step's inputs on the device ([T][N][H]...) plus host copies of a unit sample."""
+
+    def __init__(self, cfg: workloads.Config, units: np.ndarray, steps: int, dev="cuda",
+                 threads: int = 8):
+        self.cfg, self.units, self.steps = cfg, np.asarray(units), steps
+        U = cfg.units
+        t0 = time.time()
+        with ThreadPoolExecutor(threads) as ex:
+            s0 = list(ex.map(lambda n: workloads.initial_state(cfg, [n]), range(cfg.batch)))
+        S0 = np.concatenate(s0)
+        self.S0 = _to_dev(S0, dev)
+        self.host_S0 = S0.reshape(U, cfg.d_k, cfg.d_v)[self.units].astype(np.float64)
+        del S0, s0
+        B = workloads.basis(cfg)
+        self.basis = _to_dev(B, dev)
+        self.host_basis = B[self.units % cfg.heads].astype(np.float64)
+        self.q, self.k, self.v, self.decay, self.beta = [], [], [], [], []
+        hq, hk, hv, hd, hb = [], [], [], [], []
+        with ThreadPoolExecutor(threads) as ex:
+            for t, si in enumerate(ex.map(lambda t: workloads.step_inputs(cfg, t), range(steps))):
+                self.q.append(_to_dev(si.q, dev))
+                self.k.append(_to_dev(si.k, dev))
+                self.v.append(_to_dev(si.v, dev))
+                self.decay.append(_to_dev(si.decay, dev))
+                self.beta.append(_to_dev(si.beta, dev) if si.beta is not None else None)
+                flat = lambda x, e: x.reshape((U,) + ((e,) if e else ()))[self.units]
+                hq.append(workloads.widen(flat(si.q, cfg.d_k)))
+                hk.append(workloads.widen(flat(si.k, cfg.d_k)))
+                hv.append(workloads.widen(flat(si.v, cfg.d_v)))
+                hd.append(flat(si.decay, cfg.d_k if cfg.per_channel_decay else 0).astype(np.float64))
+                hb.append(flat(si.beta, 0).astype(np.float64) if si.beta is not None else None)
+        self.host = dict(q=np.stack(hq), k=np.stack(hk), v=np.stack(hv), decay=np.stack(hd),
+                         beta=np.stack(hb) if hb[0] is not None else None)
+        note(f"inputs {cfg.name}: {steps} steps, {U} units, {time.time() - t0:.1f}s")
+
+
+def run_gpu(cfg: workloads.Config, inp: Inputs, *, fused: bool = True, check_state_frozen=True):
+    """Decode all steps with both reads; returns sampled outputs and window snapshots."""
+    d = dims_of(cfg)
+    U, W = cfg.units, cfg.window
+    idx = torch.as_tensor(inp.units, device=inp.S0.device)
+    state = inp.S0.clone()
+    dec = WindowedDecoder(d, state, inp.basis, read="both", fused=fused)
+    dec.refresh()
+    ys, yf = [], []
+    S_snap = [state.view(U, -1)[idx].cpu().numpy()]
+    Sk_snap = [dec.sketch.view(U, -1)[idx].cpu().numpy()]
+    frozen_state = state.clone() if check_state_frozen else None
+    frozen_sketch = dec.sketch.clone() if check_state_frozen else None
+    y = torch.empty((cfg.batch, cfg.heads, cfg.d_v), device=state.device)
+    y2 = torch.empty_like(y)
+    for t in range(inp.steps):
+        tau = t % W + 1
+        if tau == W and check_state_frozen:
+            # decode steps never write the state or the sketch
+            assert torch.equal(state, frozen_state), f"state written inside window at step {t}"
+            assert torch.equal(dec.sketch, frozen_sketch), f"sketch written inside window at {t}"
+        dec.step(inp.q[t], inp.k[t], inp.v[t], inp.decay[t], inp.beta[t], y=y, y_full=y2)
+        ys.append(y.view(U, -1)[idx].cpu().numpy())
+        yf.append(y2.view(U, -1)[idx].cpu().numpy())
+        if tau == W:
+            S_snap.append(state.view(U, -1)[idx].cpu().numpy())
+            Sk_snap.append(dec.sketch.view(U, -1)[idx].cpu().numpy())
+            if check_state_frozen:
+                frozen_state.copy_(state)
+                frozen_sketch.copy_(dec.sketch)
+    torch.cuda.synchronize()
+    n = len(inp.units)
+    return dict(y_sketch=np.stack(ys).astype(np.float64), y_full=np.stack(yf).astype(np.float64),
+                S=np.stack(S_snap).reshape(-1, n, cfg.d_k, cfg.d_v).astype(np.float64),
+                Sk=np.stack(Sk_snap).reshape(-1, n, cfg.rank, cfg.d_v).astype(np.float64),
+                final_state=state, sketch=dec.sketch)
+
+
+def run_oracle(cfg: workloads.Config, inp: Inputs, threads: int = 0):
+    h = inp.host
+    return oracle.run(cfg.rule, inp.host_S0, inp.host_basis, h["q"], h["k"], h["v"], h["decay"],
+                      h["beta"], cfg.window, threads=threads)
+
+
+def rel_rows(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per-vector relative error over the last axis."""
+    num = np.linalg.norm(got - ref, axis=-1)
+    nref = np.linalg.norm(ref, axis=-1)
+    floor = 1e-6 * np.sqrt(np.mean(nref ** 2)) if nref.size else 0.0
+    return num / np.maximum(nref, floor)
+
+
+def rel_mats(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    a = got.reshape(got.shape[:2] + (-1,))
+    b = ref.reshape(ref.shape[:2] + (-1,))
+    return rel_rows(a, b)
+
+
+def compare(cfg, got, ref, *, y_tol=Y_TOL, s_tol=S_TOL) -> dict:
+    """Assert parity; returns the error summary."""
+    e_sk = rel_rows(got["y_sketch"], ref["y_sketch"])
+    e_ex = rel_rows(got["y_full"], ref["y_exact"])
+    # element by element, on the row's scale
+    scale = np.maximum(np.max(np.abs(ref["y_exact"]), axis=-1, keepdims=True), 1e-30)
+    el_ex = np.max(np.abs(got["y_full"] - ref["y_exact"]) / scale)
+    scale_s = np.maximum(np.max(np.abs(ref["y_sketch"]), axis=-1, keepdims=True), 1e-30)
+    el_sk = np.max(np.abs(got["y_sketch"] - ref["y_sketch"]) / scale_s)
+    nw = got["S"].shape[0]
+    e_S = rel_mats(got["S"], ref["S_win"][:nw])
+    e_Sk = rel_mats(got["Sk"], ref["Sk"][:nw])
+    approx = rel_rows(ref["y_sketch"], ref["y_exact"])
+    summary = dict(config=cfg.name, y_sketch_max=float(e_sk.max()), y_exact_max=float(e_ex.max()),
+                   y_sketch_elem_max=float(el_sk), y_exact_elem_max=float(el_ex),
+                   S_max=float(e_S.max()), Sk_max=float(e_Sk.max()),
+                   approx_err_mean=float(approx.mean()), approx_err_max=float(approx.max()))
+    note(f"parity {summary}")
+    assert e_sk.max() <= y_tol, f"sketch read: max rel err {e_sk.max():.3e} > {y_tol}"
+    assert e_ex.max() <= y_tol, f"exact read: max rel err {e_ex.max():.3e} > {y_tol}"
+    assert el_sk <= y_tol and el_ex <= y_tol, f"element error {el_sk:.3e}/{el_ex:.3e}"
+    assert e_S.max() <= s_tol, f"state: max rel err {e_S.max():.3e} > {s_tol}"
+    assert e_Sk.max() <= s_tol, f"sketch: max rel err {e_Sk.max():.3e} > {s_tol}"
+    return summary

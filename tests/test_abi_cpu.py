@@ -1,0 +1,215 @@
+"""The C ABI without a GPU: the library loads, exports what the header declares,
+and rejects bad arguments on the host before anything is enqueued.
+
+Every call below is built to fail validation (or to be a declared no-op), so
+no kernel is ever launched; the fake device addresses are never dereferenced.
+"""
+import ctypes
+import shutil
+import subprocess
+
+import pytest
+
+import sketched_recurrent_state_amd as ssm
+
+A = 1 << 32  # a 16-byte aligned fake device address (never dereferenced)
+
+
+def dims(rule="gdn", in_dtype="bf16", batch=2, heads=3, d_k=32, d_v=64, window=4, rank=4):
+    return ssm.Dims.make(rule, in_dtype, batch, heads, d_k, d_v, window, rank)
+
+
+def addrs(n, gap=1 << 28):
+    """n disjoint, aligned fake addresses."""
+    return [A + i * gap for i in range(n)]
+
+
+def status_of(fn, *args, **kw):
+    try:
+        fn(*args, **kw)
+    except ssm.SSMError as e:
+        return e.status, e.detail
+    return 0, ""
+
+
+def test_every_declared_symbol_is_exported():
+    names = ssm.declared_symbols()
+    assert set(names) >= {"ssm_abi_version", "ssm_status_string", "ssm_last_error",
+                          "ssm_buffer_append", "ssm_window_update_refresh",
+                          "ssm_sketch_decode_step", "ssm_full_read_decode_step"}
+    lib = ssm.library()
+    for n in names:
+        assert hasattr(lib, n), n
+    if shutil.which("nm"):
+        out = subprocess.run(["nm", "-D", "--defined-only", ssm.LIB_PATH], capture_output=True,
+                             text=True, check=True).stdout
+        exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+        assert set(names) <= exported
+
+
+def test_version_and_status_strings():
+    assert ssm.abi_version() == 1
+    lib = ssm.library()
+    for code in range(7):
+        assert lib.ssm_status_string(code).decode()
+    assert lib.ssm_status_string(99).decode() == "unknown status"
+
+
+def test_null_dims():
+    lib = ssm.library()
+    st = lib.ssm_window_update_refresh(None, A, A, A, A, A, A, A, 1, None)
+    assert st == 1 and "dims is NULL" in lib.ssm_last_error().decode()
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("rule", 3, 4), ("rule", -1, 4), ("in_dtype", 2, 4),
+    ("batch", -1, 2), ("heads", 0, 2), ("d_k", 48, 2), ("d_k", 256, 2), ("d_v", 16, 2),
+    ("d_v", 256, 2), ("window", 0, 2), ("window", 17, 2), ("rank", 0, 2), ("rank", 33, 2),
+])
+def test_bad_dims(field, value, code):
+    d = dims()
+    setattr(d, field, value)
+    p = addrs(8)
+    st, msg = status_of(ssm.window_update_refresh, d, *p[:7], 1)
+    assert st == code, msg
+    assert field.replace("_", "") in msg.replace("_", "").lower() or field in msg
+
+
+def test_rank_above_d_k():
+    d = dims(d_k=16, rank=17)
+    st, msg = status_of(ssm.window_update_refresh, d, *addrs(7), 1)
+    assert st == 2 and "rank" in msg
+
+
+def test_too_many_units():
+    d = dims(batch=1 << 20, heads=16)
+    st, msg = status_of(ssm.window_update_refresh, d, *addrs(7), 1)
+    assert st == 2 and "batch*heads" in msg
+
+
+@pytest.mark.parametrize("n_tokens", [-1, 5])
+def test_n_tokens_range(n_tokens):
+    st, msg = status_of(ssm.window_update_refresh, dims(window=4), *addrs(7), n_tokens)
+    assert st == 4 and "n_tokens" in msg
+
+
+@pytest.mark.parametrize("tau", [0, 5])
+def test_tau_range(tau):
+    p = addrs(8)
+    st, _ = status_of(ssm.sketch_decode_step, dims(window=4), p[0], p[1], p[2], p[3], p[4], p[5],
+                      p[6], tau, p[7])
+    assert st == 4
+    st, _ = status_of(ssm.full_read_decode_step, dims(window=4), p[0], p[2], p[3], p[4], p[5], p[6],
+                      tau, p[7])
+    assert st == 4
+
+
+@pytest.mark.parametrize("slot", [-1, 4])
+def test_slot_range(slot):
+    st, msg = status_of(ssm.buffer_append, dims(window=4), *addrs(8), slot)
+    assert st == 4 and "slot" in msg
+
+
+def test_empty_batch_is_a_noop():
+    # batch = 0: nothing to do, no pointer is looked at, nothing is launched
+    d = dims(batch=0)
+    assert status_of(ssm.window_update_refresh, d, None, None, None, None, None, None, None, 2)[0] == 0
+    assert status_of(ssm.sketch_decode_step, d, None, None, None, None, None, None, None, 1, None)[0] == 0
+    assert status_of(ssm.full_read_decode_step, d, None, None, None, None, None, None, 1, None)[0] == 0
+    assert status_of(ssm.buffer_append, d, None, None, None, None, None, None, None, None, 0)[0] == 0
+
+
+def test_nothing_to_do_is_a_noop():
+    # no tokens and no sketch requested: no launch
+    p = addrs(7)
+    assert status_of(ssm.window_update_refresh, dims(), p[0], None, None, None, None, None, None, 0)[0] == 0
+
+
+def test_null_pointers():
+    p = addrs(12)
+    d = dims()
+    st, msg = status_of(ssm.window_update_refresh, d, None, p[1], p[2], p[3], p[4], p[5], p[6], 1)
+    assert st == 1 and "state" in msg
+    st, msg = status_of(ssm.window_update_refresh, d, p[0], p[1], None, p[3], p[4], p[5], p[6], 1)
+    assert st == 1 and "basis" in msg
+    st, msg = status_of(ssm.window_update_refresh, d, p[0], p[1], p[2], None, p[4], p[5], p[6], 1)
+    assert st == 1 and "k_buf" in msg
+    st, msg = status_of(ssm.window_update_refresh, d, p[0], p[1], p[2], p[3], p[4], p[5], None, 1)
+    assert st == 1 and "beta_buf" in msg
+    st, msg = status_of(ssm.sketch_decode_step, d, p[0], p[1], None, p[3], p[4], p[5], p[6], 1, p[7])
+    assert st == 1 and "q" in msg
+    st, msg = status_of(ssm.sketch_decode_step, d, p[0], p[1], p[2], p[3], p[4], p[5], p[6], 1, None)
+    assert st == 1 and "y" in msg
+    st, msg = status_of(ssm.full_read_decode_step, d, None, p[2], p[3], p[4], p[5], p[6], 1, p[7])
+    assert st == 1 and "state" in msg
+
+
+def test_beta_rules():
+    p = addrs(8)
+    # Mamba-2 takes no beta
+    st, msg = status_of(ssm.window_update_refresh, dims(rule="mamba2"), *p[:7], 1)
+    assert st == 4 and "Mamba-2" in msg
+    # the delta rules need it
+    st, msg = status_of(ssm.buffer_append, dims(rule="kda"), p[0], p[1], p[2], None, *p[4:8], 0)
+    assert st == 1 and "beta_t" in msg
+
+
+def test_fused_token_all_or_nothing():
+    p = addrs(12)
+    d = dims()
+    st, msg = status_of(ssm.sketch_decode_step, d, *p[:7], 1, p[7], v_t=p[8])
+    assert st == 4 and "k_t is NULL" in msg
+    st, msg = status_of(ssm.sketch_decode_step, d, *p[:7], 1, p[7], k_t=p[8], v_t=p[9])
+    assert st == 1 and "decay_t" in msg
+
+
+def test_alignment():
+    p = addrs(8)
+    st, msg = status_of(ssm.window_update_refresh, dims(), p[0] + 8, *p[1:7], 1)
+    assert st == 3 and "state" in msg
+    st, msg = status_of(ssm.sketch_decode_step, dims(), *p[:6], p[6] + 4, 1, p[7])
+    assert st == 3 and "beta_buf" in msg
+
+
+def test_aliasing():
+    p = addrs(8)
+    # sketch placed inside the state
+    st, msg = status_of(ssm.window_update_refresh, dims(), p[0], p[0] + 256, *p[2:7], 1)
+    assert st == 5 and "overlaps" in msg
+    # y on top of q
+    st, msg = status_of(ssm.sketch_decode_step, dims(), p[0], p[1], p[2], *p[3:7], 1, p[2])
+    assert st == 5 and "overlaps" in msg
+    # fused append writes the buffers: they must not overlap the token inputs
+    st, msg = status_of(ssm.sketch_decode_step, dims(), *p[:7], 1, p[7], k_t=p[3], v_t=A + (40 << 28),
+                        decay_t=A + (41 << 28), beta_t=A + (42 << 28))
+    assert st == 5 and "overlaps" in msg
+    # unfused reads of the same buffer from two arguments are fine to check: inputs may overlap
+    d = dims(rule="mamba2")
+    st, msg = status_of(ssm.full_read_decode_step, d, p[0], p[1], p[1], p[1], p[1], None, 1, p[1])
+    assert st == 5  # but y may not overlap them
+
+
+def test_last_error_is_thread_local_and_cleared():
+    import threading
+    lib = ssm.library()
+    status_of(ssm.window_update_refresh, dims(window=4), *addrs(7), 9)
+    assert "n_tokens" in lib.ssm_last_error().decode()
+    seen = {}
+
+    def other():
+        seen["msg"] = lib.ssm_last_error().decode()
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert seen["msg"] == ""
+    # a successful (no-op) call clears it
+    assert status_of(ssm.window_update_refresh, dims(batch=0), *addrs(7), 0)[0] == 0
+    assert lib.ssm_last_error().decode() == ""
+
+
+def test_binding_checks_tensor_sizes_on_host():
+    torch = pytest.importorskip("torch")
+    # CPU tensors are rejected before anything reaches the library
+    d = dims()
+    with pytest.raises(ValueError, match="device tensor"):
+        ssm.window_update_refresh(d, torch.zeros(4), None, None, None, None, None, None, 0)

@@ -1,0 +1,195 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Small cases (ragged unit counts, every rule, both input dtypes, all tile
+shapes, a trailing partial window) are compared on every unit; the workload
+sizes are compared on a sample of units (always the first and the last) at
+every step and after every window, in the same launch configuration the
+benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+import sketched_recurrent_state_amd as ssm
+from sketched_recurrent_state_amd.decoder import WindowedDecoder
+from tests import gpu_harness as H
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+BASE = {"mamba2": workloads.C2, "gdn": workloads.C3, "kda": workloads.C4}
+
+
+def small(rule, in_dtype="bf16", d_k=128, d_v=128, W=8, r=8, N=3, Hh=5, T=None):
+    cfg = BASE[rule].with_(name=f"small_{rule}_{in_dtype}_{d_k}x{d_v}_w{W}_r{r}",
+                           in_dtype=in_dtype, batch=N, heads=Hh, d_k=d_k, d_v=d_v,
+                           window=W, rank=r)
+    return cfg.with_(steps=T if T is not None else 2 * W + 3)
+
+
+SMALL = [
+    small("mamba2"), small("gdn"), small("kda"),
+    small("mamba2", d_k=128, d_v=64), small("gdn", d_k=64, d_v=32, W=5, r=3),
+    small("kda", d_k=32, d_v=64, W=3, r=32), small("gdn", d_k=16, d_v=32, W=16, r=1),
+    small("kda", d_k=16, d_v=128, W=1, r=16), small("mamba2", d_k=32, d_v=128, W=2, r=9),
+    small("gdn", "f32", d_k=64, d_v=64, W=4, r=16), small("kda", "f32", d_k=128, d_v=32, W=6, r=8),
+    small("mamba2", "f32", d_k=16, d_v=64, W=3, r=16),
+    small("gdn", N=7, Hh=9, W=8, r=8),   # 63 units: a ragged last wave of the sketch read
+]
+
+
+@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+def test_small_all_units(cfg):
+    H.note(f"case {cfg.name}")
+    units = np.arange(cfg.units)
+    inp = H.Inputs(cfg, units, cfg.steps)
+    got = H.run_gpu(cfg, inp)
+    ref = H.run_oracle(cfg, inp)
+    H.compare(cfg, got, ref)
+
+
+def test_c1_tiny_mamba2_fp32():
+    cfg = workloads.C1
+    H.note("case c1")
+    inp = H.Inputs(cfg, np.arange(cfg.units), cfg.steps)
+    H.compare(cfg, H.run_gpu(cfg, inp), H.run_oracle(cfg, inp))
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c4"])
+def test_workload_sampled_units(name):
+    cfg = workloads.get(name)
+    H.note(f"case {name} (sampled units)")
+    units = workloads.sample_units(cfg, 40)
+    inp = H.Inputs(cfg, units, cfg.steps)
+    got = H.run_gpu(cfg, inp)
+    ref = H.run_oracle(cfg, inp)
+    H.compare(cfg, got, ref)
+
+
+@pytest.fixture(scope="module")
+def c5_inputs():
+    cfg = workloads.c5(8, 8)
+    return H.Inputs(cfg, workloads.sample_units(cfg, 16), cfg.steps)
+
+
+@pytest.mark.parametrize("r,W", [(r, W) for r in workloads.C5_RANKS for W in workloads.C5_WINDOWS])
+def test_c5_sweep_sampled_units(c5_inputs, r, W):
+    cfg = workloads.c5(r, W)
+    H.note(f"case {cfg.name} (sampled units)")
+    inp = c5_inputs
+    # the sweep shares one token stream; only the basis follows the rank
+    B = workloads.basis(cfg)
+    inp.basis = torch.from_numpy(B).cuda()
+    inp.host_basis = B[inp.units % cfg.heads].astype(np.float64)
+    got = H.run_gpu(cfg, inp, check_state_frozen=(r == 8 and W == 8))
+    H.compare(cfg, got, H.run_oracle(cfg, inp))
+
+
+def test_fused_append_equals_separate_append():
+    cfg = small("kda", W=4, r=8)
+    H.note("case fused-vs-separate append")
+    inp = H.Inputs(cfg, np.arange(cfg.units), cfg.steps)
+    a = H.run_gpu(cfg, inp, fused=True)
+    b = H.run_gpu(cfg, inp, fused=False)
+    for key in ("y_sketch", "y_full", "S", "Sk"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_two_runs_are_bitwise_equal():
+    cfg = small("gdn", N=16, Hh=8)
+    H.note("case determinism")
+    inp = H.Inputs(cfg, np.arange(cfg.units), cfg.steps)
+    a = H.run_gpu(cfg, inp)
+    b = H.run_gpu(cfg, inp)
+    for key in ("y_sketch", "y_full", "S", "Sk"):
+        assert np.array_equal(a[key], b[key]), key
+    assert torch.equal(a["final_state"], b["final_state"])
+
+
+@pytest.mark.parametrize("rule", ["mamba2", "gdn", "kda"])
+def test_partial_window_flush(rule):
+    """n < W buffered tokens written early: the state equals the recurrence after n tokens."""
+    W, n = 8, 5
+    cfg = small(rule, W=W, T=n)
+    H.note(f"case partial flush {rule}")
+    inp = H.Inputs(cfg, np.arange(cfg.units), n)
+    d = H.dims_of(cfg)
+    state = inp.S0.clone()
+    dec = WindowedDecoder(d, state, inp.basis, read="sketch")
+    dec.refresh()
+    ys = []
+    for t in range(n):
+        ys.append(dec.step(inp.q[t], inp.k[t], inp.v[t], inp.decay[t], inp.beta[t]).clone())
+    dec.flush()
+    torch.cuda.synchronize()
+    ref = H.run_oracle(cfg.with_(window=n), inp)   # one window of n tokens
+    U = cfg.units
+    got_S = state.view(1, U, cfg.d_k, cfg.d_v).cpu().double().numpy()
+    assert H.rel_mats(got_S, ref["S_win"][1:2]).max() <= H.S_TOL
+    got_Sk = dec.sketch.view(1, U, cfg.rank, cfg.d_v).cpu().double().numpy()
+    assert H.rel_mats(got_Sk, ref["Sk"][1:2]).max() <= H.S_TOL
+    got_y = torch.stack(ys).view(n, U, cfg.d_v).cpu().double().numpy()
+    assert H.rel_rows(got_y, ref["y_sketch"]).max() <= H.Y_TOL
+
+
+def test_nan_stays_in_its_unit():
+    """A NaN key in one unit poisons that unit only."""
+    cfg = small("gdn", N=4, Hh=4, W=4, T=8)
+    H.note("case unit isolation")
+    inp = H.Inputs(cfg, np.arange(cfg.units), cfg.steps)
+    clean = H.run_gpu(cfg, inp, check_state_frozen=False)
+    bad_unit = 5
+    k2 = inp.k[2].clone()
+    k2.view(cfg.units, -1)[bad_unit, 3] = float("nan")
+    inp.k[2] = k2
+    dirty = H.run_gpu(cfg, inp, check_state_frozen=False)
+    others = [u for u in range(cfg.units) if u != bad_unit]
+    for key in ("y_sketch", "y_full"):
+        assert np.array_equal(clean[key][:, others], dirty[key][:, others]), key
+        assert np.isnan(dirty[key][2:, bad_unit]).all(), key
+    assert np.array_equal(clean["S"][:, others], dirty["S"][:, others])
+
+
+def test_outputs_stay_inside_their_arrays():
+    """Guard bands around y, the sketch and the state are never written."""
+    cfg = small("kda", N=2, Hh=3, W=4, r=8, T=4)
+    H.note("case guard bands")
+    inp = H.Inputs(cfg, np.arange(cfg.units), cfg.steps)
+    d = H.dims_of(cfg)
+    U = cfg.units
+    pad = 1024
+    sentinel = 12345.0
+
+    def guarded(n):
+        buf = torch.full((n + 2 * pad,), sentinel, device="cuda")
+        return buf, buf[pad:pad + n]
+
+    sbuf, S = guarded(U * cfg.d_k * cfg.d_v)
+    S.copy_(inp.S0.view(-1))
+    kbuf, skv = guarded(U * cfg.rank * cfg.d_v)
+    ybuf, yv = guarded(U * cfg.d_v)
+    y2buf, y2v = guarded(U * cfg.d_v)
+    dec = WindowedDecoder(d, S.view(cfg.batch, cfg.heads, cfg.d_k, cfg.d_v), inp.basis, read="both")
+    dec.sketch = skv.view(cfg.batch, cfg.heads, cfg.rank, cfg.d_v)
+    dec.refresh()
+    for t in range(cfg.steps):
+        dec.step(inp.q[t], inp.k[t], inp.v[t], inp.decay[t], inp.beta[t],
+                 y=yv.view(cfg.batch, cfg.heads, cfg.d_v), y_full=y2v.view(cfg.batch, cfg.heads, cfg.d_v))
+    torch.cuda.synchronize()
+    for buf in (sbuf, kbuf, ybuf, y2buf):
+        assert (buf[:pad] == sentinel).all() and (buf[-pad:] == sentinel).all()
+
+
+def test_empty_batch_on_device():
+    d = ssm.Dims.make("gdn", "bf16", 0, 4, 128, 128, 8, 8)
+    z = torch.empty(0, device="cuda")
+    ssm.window_update_refresh(d, z, z, torch.zeros(4 * 8 * 128, device="cuda"), None, None, None,
+                              None, 0)
+    torch.cuda.synchronize()
