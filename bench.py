@@ -253,6 +253,15 @@ def main() -> int:
               "max": float(e.max()), "steps": 2 * W}
     del st_a, sk_a
 
+    # ---- attainable HBM rate: a plain device copy of 2 GiB (read + write) ---------------
+    n_copy = (2 << 30) // 4
+    src = torch.ones(n_copy, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    copy_ms = kernel_time(lambda i: dst.copy_(src), 5)
+    copy_gbs = 2 * n_copy * 4 / (copy_ms * 1e-3) / 1e9
+    del src, dst
+
     # ---- roofline of the dominant kernel (update + refresh) ---------------------------
     upd_avg_ms = float(np.mean(upd_ms))
     upd_bytes = bm["update"] * U
@@ -322,6 +331,8 @@ def main() -> int:
         "state_bytes_ratio": bm["state_bytes_full"] / bm["state_bytes_sketch"],
         "read_path_bytes_ratio": bm["full_step"] / bm["sketch_step"],
         "approx_error": approx,
+        "copy_probe_gbs": copy_gbs,
+        "update_refresh_frac_of_copy": achieved / copy_gbs,
         "input_gen_s": gen_s,
         "device": torch.cuda.get_device_name(0),
     }

@@ -59,6 +59,10 @@ class Dims(ctypes.Structure):
 
 
 def _load():
+    # The tensors handed to the library come from PyTorch's HIP runtime, and the
+    # process must hold exactly one HIP runtime: load torch first so that the
+    # library's libamdhip64.so.7 dependency resolves to the copy torch loaded.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it with `python -m sketched_recurrent_state_amd.build`")

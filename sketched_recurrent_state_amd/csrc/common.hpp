@@ -7,8 +7,9 @@
 //    (rg = l / 8). A reduction over d_k is a sum over the 8 lanes that share
 //    cg, i.e. over lane bits 3, 4 and 5: DPP row_ror:8 for bit 3 and the
 //    gfx950 permlane16/permlane32 swaps for bits 4 and 5.
-//  * group ("g16"): 16 lanes (one DPP row) per unit, each holding d_k/16 key
-//    elements and d_v/16 value elements; reductions stay inside the row.
+//  * group: G = 16 or 32 consecutive lanes per unit, each holding d_k/G key
+//    elements and d_v/G value elements; reductions are DPP row operations plus,
+//    for G = 32, one permlane16 swap.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -112,6 +113,56 @@ struct Vec<bf16_t, E> {
   }
 };
 
+// E elements of T held as raw 32-bit words (bf16 stays packed two per word)
+// from the load until unpack(): halves the registers of in-flight bf16 data.
+template <typename T, int E>
+struct Packed {
+  static constexpr int BYTES = E * (int)sizeof(T);
+  static constexpr int NW = (BYTES + 3) / 4;
+  uint32_t w[NW];
+
+  __device__ __forceinline__ void load(const T* __restrict__ p) {
+    if constexpr (BYTES % 16 == 0) {
+#pragma unroll
+      for (int i = 0; i < BYTES / 16; ++i) {
+        uint4 x = reinterpret_cast<const uint4*>(p)[i];
+        w[4 * i] = x.x; w[4 * i + 1] = x.y; w[4 * i + 2] = x.z; w[4 * i + 3] = x.w;
+      }
+    } else if constexpr (BYTES == 8) {
+      uint2 x = *reinterpret_cast<const uint2*>(p);
+      w[0] = x.x; w[1] = x.y;
+    } else if constexpr (BYTES == 4) {
+      w[0] = *reinterpret_cast<const uint32_t*>(p);
+    } else {
+      static_assert(BYTES == 2, "unsupported width");
+      w[0] = *reinterpret_cast<const uint16_t*>(p);
+    }
+  }
+  __device__ __forceinline__ void store(T* __restrict__ p) const {
+    if constexpr (BYTES % 16 == 0) {
+#pragma unroll
+      for (int i = 0; i < BYTES / 16; ++i)
+        reinterpret_cast<uint4*>(p)[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+    } else if constexpr (BYTES == 8) {
+      *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+    } else if constexpr (BYTES == 4) {
+      *reinterpret_cast<uint32_t*>(p) = w[0];
+    } else {
+      *reinterpret_cast<uint16_t*>(p) = (uint16_t)w[0];
+    }
+  }
+  __device__ __forceinline__ void unpack(float* out) const {
+#pragma unroll
+    for (int i = 0; i < E; ++i) {
+      if constexpr (sizeof(T) == 4) {
+        out[i] = __uint_as_float(w[i]);
+      } else {
+        out[i] = (i & 1) ? bf16_hi(w[i >> 1]) : bf16_lo(w[i >> 1]);
+      }
+    }
+  }
+};
+
 // ---------------------------------------------------------------------------
 // cross-lane primitives
 // ---------------------------------------------------------------------------
@@ -172,12 +223,22 @@ __device__ __forceinline__ float4 tile_allreduce(float4 v) {
                      tile_allreduce(v.w));
 }
 
-// Sum over the 16 lanes of a DPP row (the g16 layout).
+// Sum over the 16 lanes of a DPP row.
 __device__ __forceinline__ float row_allreduce(float x) {
   x += dpp<DPP_QUAD_1032>(x);
   x += dpp<DPP_QUAD_2301>(x);
   x += dpp<DPP_ROR4>(x);
   x += dpp<DPP_ROR8>(x);
+  return x;
+}
+
+// Sum over an aligned group of G consecutive lanes (G = 16, 32 or 64).
+template <int G>
+__device__ __forceinline__ float group_allreduce(float x) {
+  static_assert(G == 16 || G == 32 || G == 64, "group size");
+  x = row_allreduce(x);
+  if constexpr (G >= 32) x = xsum16(x);
+  if constexpr (G >= 64) x = xsum32(x);
   return x;
 }
 
@@ -197,6 +258,80 @@ __device__ __forceinline__ float4 scale4(float a, float4 b) {
 // a * b + c, componentwise with scalar a
 __device__ __forceinline__ float4 fma4(float a, float4 b, float4 c) {
   return make_float4(fmaf(a, b.x, c.x), fmaf(a, b.y, c.y), fmaf(a, b.z, c.z), fmaf(a, b.w, c.w));
+}
+
+// ---------------------------------------------------------------------------
+// window staging: the first n buffered tokens of one unit -> LDS as fp32
+// ---------------------------------------------------------------------------
+__host__ __device__ inline int pad4(int x) { return (x + 3) & ~3; }
+
+// One unit's window buffer (slot 0 of each array) and, for a fused append, its
+// current token (kt == nullptr: not fused, the buffers are only read).
+template <typename TIN>
+struct UnitWindow {
+  TIN* k;
+  TIN* v;
+  float* d;
+  float* b;
+  const TIN* kt;
+  const TIN* vt;
+  const float* dt;
+  const float* bt;
+};
+
+// LDS floats needed for n staged tokens: k [n][DK] | v [n][DV] | gates | beta.
+template <int RULE, int DK, int DV>
+__host__ __device__ inline int window_lds_floats(int n) {
+  constexpr int DSTR = (RULE == KDA) ? DK : 1;
+  return n * DK + n * DV + pad4(n * DSTR) + ((RULE == MAMBA2) ? 0 : pad4(n));
+}
+
+// Cooperative copy by the NT threads of a workgroup. With a fused append the
+// newest slot (n - 1) is read from the current token and also written into
+// the buffer. The caller synchronises the workgroup before reading the LDS.
+template <int RULE, int DK, int DV, typename TIN, int NT>
+__device__ __forceinline__ void stage_window(float* lds, const UnitWindow<TIN>& uw, int n,
+                                             int tid) {
+  constexpr int DSTR = (RULE == KDA) ? DK : 1;
+  constexpr int VIN = 16 / sizeof(TIN);
+  float* lk = lds;
+  float* lv = lk + n * DK;
+  float* ld = lv + n * DV;
+  float* lb = ld + pad4(n * DSTR);
+  const bool fused = uw.kt != nullptr;
+  const int last = n - 1;
+  for (int e = tid * VIN; e < n * DK; e += NT * VIN) {
+    const bool cur = fused && (e / DK == last);
+    Packed<TIN, VIN> x;
+    x.load(cur ? uw.kt + (e - last * DK) : uw.k + e);
+    if (cur) x.store(uw.k + e);
+    float f[VIN];
+    x.unpack(f);
+    Vec<float, VIN>::store(lk + e, f);
+  }
+  for (int e = tid * VIN; e < n * DV; e += NT * VIN) {
+    const bool cur = fused && (e / DV == last);
+    Packed<TIN, VIN> x;
+    x.load(cur ? uw.vt + (e - last * DV) : uw.v + e);
+    if (cur) x.store(uw.v + e);
+    float f[VIN];
+    x.unpack(f);
+    Vec<float, VIN>::store(lv + e, f);
+  }
+  for (int e = tid; e < n * DSTR; e += NT) {
+    const bool cur = fused && (e / DSTR == last);
+    const float x = cur ? uw.dt[e - last * DSTR] : uw.d[e];
+    if (cur) uw.d[e] = x;
+    ld[e] = x;
+  }
+  if constexpr (RULE != MAMBA2) {
+    for (int e = tid; e < n; e += NT) {
+      const bool cur = fused && (e == last);
+      const float x = cur ? uw.bt[0] : uw.b[e];
+      if (cur) uw.b[e] = x;
+      lb[e] = x;
+    }
+  }
 }
 
 }  // namespace ssm

@@ -36,9 +36,16 @@ __device__ __forceinline__ void carry_back(float* u, const float* kk, const floa
 }
 
 // ---------------------------------------------------------------------------
-// sketch read: 16 lanes (one DPP row) per unit
+// sketch read: G consecutive lanes per unit (G = 32, or 16 when d_k = 16).
+// Every load of the step (query, the tau buffered tokens, the first eight
+// basis rows and sketch rows) is issued before any arithmetic, so a step pays
+// one memory latency instead of one per token and one per basis vector.
+// WMAX >= W bounds the unrolled token slots.
 // ---------------------------------------------------------------------------
-template <int RULE, int DK, int DV, typename TIN>
+template <int DK>
+constexpr int sketch_group() { return DK >= 32 ? 32 : 16; }
+
+template <int RULE, int DK, int DV, typename TIN, int WMAX>
 __global__ void __launch_bounds__(256)
 sketch_decode_kernel(const float* __restrict__ sketch, const float* __restrict__ basis,
                      const TIN* __restrict__ q, const TIN* __restrict__ k_t,
@@ -46,83 +53,126 @@ sketch_decode_kernel(const float* __restrict__ sketch, const float* __restrict__
                      const float* __restrict__ b_t, TIN* __restrict__ kbuf,
                      TIN* __restrict__ vbuf, float* __restrict__ dbuf, float* __restrict__ bbuf,
                      float* __restrict__ y, int units, int heads, int window, int rank, int tau) {
-  constexpr int G = 16;
+  constexpr int G = sketch_group<DK>();
   constexpr int EK = DK / G, EV = DV / G;
   constexpr int DSTR = (RULE == KDA) ? DK : 1;
   constexpr int EA = (RULE == KDA) ? EK : 1;  // gate values per lane and token
+  constexpr int RCH = 8;                      // basis rows fetched ahead of the walk
 
   const int gid = blockIdx.x * blockDim.x + threadIdx.x;
   const int unit = gid / G, sub = gid % G;
-  if (unit >= units) return;  // whole 16-lane groups leave together
+  if (unit >= units) return;  // whole G-lane groups leave together
   const int head = unit % heads;
   const size_t slot0 = (size_t)unit * window;
   const bool fused = (k_t != nullptr);
 
-  float u[EK];
-  Vec<TIN, EK>::load(q + (size_t)unit * DK + sub * EK, u);
-  float acc[EV];
+  // ---- issue every load ----
+  Packed<TIN, EK> qr;
+  qr.load(q + (size_t)unit * DK + sub * EK);
+  Packed<TIN, EK> kr[WMAX];
+  Packed<TIN, EV> vr[WMAX];
+  float ar[WMAX][EA], br[WMAX];
 #pragma unroll
-  for (int e = 0; e < EV; ++e) acc[e] = 0.f;
-
-  for (int i = tau - 1; i >= 0; --i) {
-    const bool cur = fused && (i == tau - 1);
-    const size_t slot = slot0 + i;
-    const TIN* kp = cur ? k_t + (size_t)unit * DK : kbuf + slot * DK;
-    const TIN* vp = cur ? v_t + (size_t)unit * DV : vbuf + slot * DV;
-    const float* dp = cur ? d_t + (size_t)unit * DSTR : dbuf + slot * DSTR;
-    float kk[EK], vv[EV], a[EA];
-    Vec<TIN, EK>::load(kp + sub * EK, kk);
-    Vec<TIN, EV>::load(vp + sub * EV, vv);
-    if constexpr (RULE == KDA) {
-      Vec<float, EK>::load(dp + sub * EK, a);
-    } else {
-      a[0] = dp[0];
-    }
-    float b = 1.f;
-    if constexpr (RULE != MAMBA2) b = cur ? b_t[unit] : bbuf[slot];
-    if (cur) {  // fused token append into slot tau-1
-      Vec<TIN, EK>::copy(kp + sub * EK, kbuf + slot * DK + sub * EK);
-      Vec<TIN, EV>::copy(vp + sub * EV, vbuf + slot * DV + sub * EV);
+  for (int i = 0; i < WMAX; ++i) {
+    if (i < tau) {
+      const bool cur = fused && (i == tau - 1);
+      const size_t slot = slot0 + i;
+      kr[i].load((cur ? k_t + (size_t)unit * DK : kbuf + slot * DK) + sub * EK);
+      vr[i].load((cur ? v_t + (size_t)unit * DV : vbuf + slot * DV) + sub * EV);
+      const float* dp = cur ? d_t + (size_t)unit * DSTR : dbuf + slot * DSTR;
       if constexpr (RULE == KDA) {
-        Vec<float, EK>::store(dbuf + slot * DK + sub * EK, a);
+        Vec<float, EK>::load(dp + sub * EK, ar[i]);
       } else {
-        if (sub == 0) dbuf[slot] = a[0];
+        ar[i][0] = dp[0];
       }
-      if constexpr (RULE != MAMBA2) {
-        if (sub == 0) bbuf[slot] = b;
-      }
+      br[i] = 1.f;
+      if constexpr (RULE != MAMBA2) br[i] = cur ? b_t[unit] : bbuf[slot];
     }
-    float s = 0.f;
-#pragma unroll
-    for (int e = 0; e < EK; ++e) s = fmaf(kk[e], u[e], s);
-    s = row_allreduce(s);
-    const float bs = b * s;
-#pragma unroll
-    for (int e = 0; e < EV; ++e) acc[e] = fmaf(bs, vv[e], acc[e]);
-    carry_back<RULE, EK>(u, kk, a, bs);
   }
-
-  // c_m = b_m . q~ ; y = intra + sum_m c_m Sk[m]
   const float* Bh = basis + (size_t)head * rank * DK + sub * EK;
   const float* Sku = sketch + (size_t)unit * rank * DV + sub * EV;
-#pragma unroll 4
-  for (int m = 0; m < rank; ++m) {
-    float bm[EK], sk[EV];
-    Vec<float, EK>::load(Bh + (size_t)m * DK, bm);
-    Vec<float, EV>::load(Sku + (size_t)m * DV, sk);
-    float c = 0.f;
+  float bm[RCH][EK], sk[RCH][EV];
 #pragma unroll
-    for (int e = 0; e < EK; ++e) c = fmaf(bm[e], u[e], c);
-    c = row_allreduce(c);
+  for (int m = 0; m < RCH; ++m) {
+    if (m < rank) {
+      Vec<float, EK>::load(Bh + (size_t)m * DK, bm[m]);
+      Vec<float, EV>::load(Sku + (size_t)m * DV, sk[m]);
+    }
+  }
+
+  // ---- fused append: the current token into slot tau-1 ----
+  if (fused) {
 #pragma unroll
-    for (int e = 0; e < EV; ++e) acc[e] = fmaf(c, sk[e], acc[e]);
+    for (int i = 0; i < WMAX; ++i) {
+      if (i == tau - 1) {
+        const size_t slot = slot0 + i;
+        kr[i].store(kbuf + slot * DK + sub * EK);
+        vr[i].store(vbuf + slot * DV + sub * EV);
+        if constexpr (RULE == KDA) {
+          Vec<float, EK>::store(dbuf + slot * DK + sub * EK, ar[i]);
+        } else {
+          if (sub == 0) dbuf[slot] = ar[i][0];
+        }
+        if constexpr (RULE != MAMBA2) {
+          if (sub == 0) bbuf[slot] = br[i];
+        }
+      }
+    }
+  }
+
+  // ---- walk the window newest to oldest ----
+  float u[EK], acc[EV];
+  qr.unpack(u);
+#pragma unroll
+  for (int e = 0; e < EV; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int i = WMAX - 1; i >= 0; --i) {
+    if (i < tau) {
+      float kk[EK], vv[EV];
+      kr[i].unpack(kk);
+      vr[i].unpack(vv);
+      float s = 0.f;
+#pragma unroll
+      for (int e = 0; e < EK; ++e) s = fmaf(kk[e], u[e], s);
+      s = group_allreduce<G>(s);
+      const float bs = br[i] * s;
+#pragma unroll
+      for (int e = 0; e < EV; ++e) acc[e] = fmaf(bs, vv[e], acc[e]);
+      carry_back<RULE, EK>(u, kk, ar[i], bs);
+    }
+  }
+
+  // ---- c_m = b_m . q~ ; y = intra + sum_m c_m Sk[m] ----
+  for (int m0 = 0; m0 < rank; m0 += RCH) {
+    if (m0 > 0) {
+#pragma unroll
+      for (int m = 0; m < RCH; ++m) {
+        if (m0 + m < rank) {
+          Vec<float, EK>::load(Bh + (size_t)(m0 + m) * DK, bm[m]);
+          Vec<float, EV>::load(Sku + (size_t)(m0 + m) * DV, sk[m]);
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < RCH; ++m) {
+      if (m0 + m < rank) {
+        float c = 0.f;
+#pragma unroll
+        for (int e = 0; e < EK; ++e) c = fmaf(bm[m][e], u[e], c);
+        c = group_allreduce<G>(c);
+#pragma unroll
+        for (int e = 0; e < EV; ++e) acc[e] = fmaf(c, sk[m][e], acc[e]);
+      }
+    }
   }
   Vec<float, EV>::store(y + (size_t)unit * DV + sub * EV, acc);
 }
 
 // ---------------------------------------------------------------------------
 // exact read of the window-start state: the state tile layout, one workgroup
-// per unit, each wave a 32-column block (it walks the buffer itself).
+// per unit. The state loads are issued first; the window is staged in LDS
+// meanwhile and every wave walks it on its own (no synchronisation after the
+// staging barrier).
 // ---------------------------------------------------------------------------
 template <int RULE, int DK, int DV, typename TIN>
 __global__ void __launch_bounds__(2 * DV)
@@ -132,8 +182,12 @@ full_read_kernel(const float* __restrict__ state, const TIN* __restrict__ q,
                  TIN* __restrict__ kbuf, TIN* __restrict__ vbuf, float* __restrict__ dbuf,
                  float* __restrict__ bbuf, float* __restrict__ y, int window, int tau) {
   constexpr int RPL = DK / 8;
+  constexpr int NT = 2 * DV;
   constexpr int DSTR = (RULE == KDA) ? DK : 1;
   constexpr int EA = (RULE == KDA) ? RPL : 1;
+
+  extern __shared__ float4 lds4[];
+  float* lds = reinterpret_cast<float*>(lds4);
 
   const int unit = blockIdx.x;
   const int tid = threadIdx.x;
@@ -149,43 +203,40 @@ full_read_kernel(const float* __restrict__ state, const TIN* __restrict__ q,
 #pragma unroll
   for (int m = 0; m < RPL; ++m)
     s[m] = *reinterpret_cast<const float4*>(Su + (size_t)(row0 + m) * DV + col);
-
   float u[RPL];
   Vec<TIN, RPL>::load(q + (size_t)unit * DK + row0, u);
+
+  UnitWindow<TIN> uw{kbuf + slot0 * DK, vbuf + slot0 * DV, dbuf + slot0 * DSTR,
+                     (RULE == MAMBA2) ? nullptr : bbuf + slot0,
+                     fused ? k_t + (size_t)unit * DK : nullptr,
+                     fused ? v_t + (size_t)unit * DV : nullptr,
+                     fused ? d_t + (size_t)unit * DSTR : nullptr,
+                     (fused && RULE != MAMBA2) ? b_t + unit : nullptr};
+  stage_window<RULE, DK, DV, TIN, NT>(lds, uw, tau, tid);
+  __syncthreads();
+  const float* lk = lds;
+  const float* lv = lk + tau * DK;
+  const float* ld = lv + tau * DV;
+  const float* lb = ld + pad4(tau * DSTR);
+
   float4 acc = f4(0.f);
+#pragma unroll 2
   for (int i = tau - 1; i >= 0; --i) {
-    const bool cur = fused && (i == tau - 1);
-    const size_t slot = slot0 + i;
-    const TIN* kp = cur ? k_t + (size_t)unit * DK : kbuf + slot * DK;
-    const TIN* vp = cur ? v_t + (size_t)unit * DV : vbuf + slot * DV;
-    const float* dp = cur ? d_t + (size_t)unit * DSTR : dbuf + slot * DSTR;
-    float kk[RPL], vv[4], a[EA];
-    Vec<TIN, RPL>::load(kp + row0, kk);
-    Vec<TIN, 4>::load(vp + col, vv);
+    float kk[RPL], a[EA];
+    Vec<float, RPL>::load(lk + i * DK + row0, kk);
+    const float4 vv = *reinterpret_cast<const float4*>(lv + i * DV + col);
     if constexpr (RULE == KDA) {
-      Vec<float, RPL>::load(dp + row0, a);
+      Vec<float, RPL>::load(ld + i * DK + row0, a);
     } else {
-      a[0] = dp[0];
+      a[0] = ld[i];
     }
-    float b = 1.f;
-    if constexpr (RULE != MAMBA2) b = cur ? b_t[unit] : bbuf[slot];
-    if (cur) {  // fused token append into slot tau-1
-      if (wave == 0 && cg == 0) {
-        Vec<TIN, RPL>::copy(kp + row0, kbuf + slot * DK + row0);
-        if constexpr (RULE == KDA) Vec<float, RPL>::store(dbuf + slot * DK + row0, a);
-      }
-      if (rg == 0) Vec<TIN, 4>::copy(vp + col, vbuf + slot * DV + col);
-      if (tid == 0) {
-        if constexpr (RULE != KDA) dbuf[slot] = a[0];
-        if constexpr (RULE != MAMBA2) bbuf[slot] = b;
-      }
-    }
+    const float b = (RULE == MAMBA2) ? 1.f : lb[i];
     float sd = 0.f;
 #pragma unroll
     for (int m = 0; m < RPL; ++m) sd = fmaf(kk[m], u[m], sd);
     sd = tile_allreduce(sd);
     const float bs = b * sd;
-    acc = fma4(bs, make_float4(vv[0], vv[1], vv[2], vv[3]), acc);
+    acc = fma4(bs, vv, acc);
     carry_back<RULE, RPL>(u, kk, a, bs);
   }
 
@@ -204,16 +255,22 @@ hipError_t launch_sketch_decode(const ssm_dims& d, const float* sketch, const fl
                                 void* v_buf, float* decay_buf, float* beta_buf, int tau, float* y,
                                 hipStream_t stream) {
   const unsigned units = (unsigned)d.batch * (unsigned)d.heads;
-  const unsigned blocks = (units * 16u + 255u) / 256u;
   return dispatch(d.rule, d.in_dtype, d.d_k, d.d_v, [&](auto R, auto DK, auto DV, auto T) {
     using TIN = typename decltype(T)::type;
     constexpr int kR = decltype(R)::value, kDK = decltype(DK)::value, kDV = decltype(DV)::value;
-    hipLaunchKernelGGL((sketch_decode_kernel<kR, kDK, kDV, TIN>), dim3(blocks), dim3(256), 0,
-                       stream, sketch, basis, static_cast<const TIN*>(q),
-                       static_cast<const TIN*>(k_t), static_cast<const TIN*>(v_t), decay_t,
-                       beta_t, static_cast<TIN*>(k_buf), static_cast<TIN*>(v_buf), decay_buf,
-                       beta_buf, y, (int)units, d.heads, d.window, d.rank, tau);
-    return hipGetLastError();
+    constexpr unsigned G = sketch_group<kDK>();
+    const unsigned blocks = (units * G + 255u) / 256u;
+    auto go = [&](auto kernel) {
+      hipLaunchKernelGGL(kernel, dim3(blocks), dim3(256), 0, stream, sketch, basis,
+                         static_cast<const TIN*>(q), static_cast<const TIN*>(k_t),
+                         static_cast<const TIN*>(v_t), decay_t, beta_t, static_cast<TIN*>(k_buf),
+                         static_cast<TIN*>(v_buf), decay_buf, beta_buf, y, (int)units, d.heads,
+                         d.window, d.rank, tau);
+      return hipGetLastError();
+    };
+    if (d.window <= 4) return go(sketch_decode_kernel<kR, kDK, kDV, TIN, 4>);
+    if (d.window <= 8) return go(sketch_decode_kernel<kR, kDK, kDV, TIN, 8>);
+    return go(sketch_decode_kernel<kR, kDK, kDV, TIN, 16>);
   });
 }
 
@@ -226,7 +283,8 @@ hipError_t launch_full_read_decode(const ssm_dims& d, const float* state, const 
   return dispatch(d.rule, d.in_dtype, d.d_k, d.d_v, [&](auto R, auto DK, auto DV, auto T) {
     using TIN = typename decltype(T)::type;
     constexpr int kR = decltype(R)::value, kDK = decltype(DK)::value, kDV = decltype(DV)::value;
-    hipLaunchKernelGGL((full_read_kernel<kR, kDK, kDV, TIN>), dim3(units), dim3(2 * kDV), 0,
+    const size_t lds = (size_t)window_lds_floats<kR, kDK, kDV>(tau) * sizeof(float);
+    hipLaunchKernelGGL((full_read_kernel<kR, kDK, kDV, TIN>), dim3(units), dim3(2 * kDV), lds,
                        stream, state, static_cast<const TIN*>(q), static_cast<const TIN*>(k_t),
                        static_cast<const TIN*>(v_t), decay_t, beta_t, static_cast<TIN*>(k_buf),
                        static_cast<TIN*>(v_buf), decay_buf, beta_buf, y, d.window, tau);

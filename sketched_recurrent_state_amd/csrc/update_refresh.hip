@@ -18,13 +18,6 @@ namespace ssm {
 
 namespace {
 
-template <int RULE, int DK>
-struct Layout {
-  static constexpr int DSTR = (RULE == KDA) ? DK : 1;  // gate floats per token
-};
-
-__host__ __device__ inline int pad4(int x) { return (x + 3) & ~3; }
-
 template <int RULE, int DK, int DV, typename TIN>
 __global__ void __launch_bounds__(2 * DV)
 update_refresh_kernel(float* __restrict__ state, float* __restrict__ sketch,
@@ -33,8 +26,7 @@ update_refresh_kernel(float* __restrict__ state, float* __restrict__ sketch,
                       const float* __restrict__ bbuf, int heads, int window, int rank, int n) {
   constexpr int RPL = DK / 8;          // rows of S per lane
   constexpr int NT = 2 * DV;           // threads per unit: d_v/32 waves
-  constexpr int DSTR = Layout<RULE, DK>::DSTR;
-  constexpr int VIN = 16 / sizeof(TIN);  // input elements per 16-byte load
+  constexpr int DSTR = (RULE == KDA) ? DK : 1;
 
   extern __shared__ float4 lds4[];
   float* lds = reinterpret_cast<float*>(lds4);
@@ -55,86 +47,43 @@ update_refresh_kernel(float* __restrict__ state, float* __restrict__ sketch,
     s[m] = *reinterpret_cast<const float4*>(Su + (size_t)(row0 + m) * DV + col);
 
   // 2. stage the window (and the basis) in LDS as fp32
-  float* lk = lds;                          // [n][DK]
-  float* lv = lk + n * DK;                  // [n][DV]
-  float* ld = lv + n * DV;                  // [n][DSTR]
-  float* lb = ld + pad4(n * DSTR);          // [n]      (delta rules)
-  float* lB = lb + ((RULE == MAMBA2) ? 0 : pad4(n));  // [rank][DK]
   const size_t slot0 = (size_t)unit * window;
-  {
-    const TIN* ku = kbuf + slot0 * DK;
-    for (int e = tid * VIN; e < n * DK; e += NT * VIN) {
-      float x[VIN];
-      Vec<TIN, VIN>::load(ku + e, x);
-      Vec<float, VIN>::store(lk + e, x);
-    }
-    const TIN* vu = vbuf + slot0 * DV;
-    for (int e = tid * VIN; e < n * DV; e += NT * VIN) {
-      float x[VIN];
-      Vec<TIN, VIN>::load(vu + e, x);
-      Vec<float, VIN>::store(lv + e, x);
-    }
-    const float* du = dbuf + slot0 * DSTR;
-    for (int e = tid; e < n * DSTR; e += NT) ld[e] = du[e];
-    if constexpr (RULE != MAMBA2) {
-      for (int e = tid; e < n; e += NT) lb[e] = bbuf[slot0 + e];
-    }
-    if (sketch != nullptr) {
-      const float* Bh = basis + (size_t)head * rank * DK;
-      for (int e = tid * 4; e < rank * DK; e += NT * 4)
-        *reinterpret_cast<float4*>(lB + e) = *reinterpret_cast<const float4*>(Bh + e);
-    }
+  UnitWindow<TIN> uw{const_cast<TIN*>(kbuf) + slot0 * DK, const_cast<TIN*>(vbuf) + slot0 * DV,
+                     const_cast<float*>(dbuf) + slot0 * DSTR,
+                     (RULE == MAMBA2) ? nullptr : const_cast<float*>(bbuf) + slot0,
+                     nullptr, nullptr, nullptr, nullptr};
+  if (n > 0) stage_window<RULE, DK, DV, TIN, NT>(lds, uw, n, tid);
+  const float* lk = lds;
+  const float* lv = lk + n * DK;
+  const float* ld = lv + n * DV;
+  const float* lb = ld + pad4(n * DSTR);
+  float* lB = lds + window_lds_floats<RULE, DK, DV>(n);  // [rank][DK]
+  if (sketch != nullptr) {
+    const float* Bh = basis + (size_t)head * rank * DK;
+    for (int e = tid * 4; e < rank * DK; e += NT * 4)
+      *reinterpret_cast<float4*>(lB + e) = *reinterpret_cast<const float4*>(Bh + e);
   }
   __syncthreads();
 
   // 3. the window's tokens, in order: S <- M_t S + b_t k_t v_t^T on the
   //    register-resident piece; the k^T S reduction over d_k crosses the 8
   //    lanes that share this lane's columns.
-  for (int t = 0; t < n; ++t) {
-    float kr[RPL];
-    Vec<float, RPL>::load(lk + t * DK + row0, kr);
-    const float4 vv = *reinterpret_cast<const float4*>(lv + t * DV + col);
-    if constexpr (RULE == MAMBA2) {
-      const float a = ld[t];
-#pragma unroll
-      for (int m = 0; m < RPL; ++m) s[m] = fma4(kr[m], vv, scale4(a, s[m]));
-    } else if constexpr (RULE == GDN) {
-      const float a = ld[t], b = lb[t];
-      float4 p = f4(0.f);
-#pragma unroll
-      for (int m = 0; m < RPL; ++m) p = fma4(kr[m], s[m], p);
-      p = tile_allreduce(p);  // p = S^T k for this lane's 4 columns
-      const float4 w = scale4(b, sub4(vv, scale4(a, p)));
-#pragma unroll
-      for (int m = 0; m < RPL; ++m) s[m] = fma4(kr[m], w, scale4(a, s[m]));
-    } else {
-      const float b = lb[t];
-      float ar[RPL];
-      Vec<float, RPL>::load(ld + t * DK + row0, ar);
-      float4 p = f4(0.f);
-#pragma unroll
-      for (int m = 0; m < RPL; ++m) {
-        s[m] = scale4(ar[m], s[m]);  // Diag(alpha) S
-        p = fma4(kr[m], s[m], p);
-      }
-      p = tile_allreduce(p);
-      const float4 w = scale4(b, sub4(vv, p));
-#pragma unroll
-      for (int m = 0; m < RPL; ++m) s[m] = fma4(kr[m], w, s[m]);
-    }
-  }
-
-  // 4. write the state back (the only HBM write of S)
-  if (n > 0) {
-#pragma unroll
-    for (int m = 0; m < RPL; ++m)
-      *reinterpret_cast<float4*>(Su + (size_t)(row0 + m) * DV + col) = s[m];
-  }
-
-  // 5. sketch refresh from the register-resident state: Sk[m] = S^T b_m.
+  //    Mamba-2 and GDN decay the whole state by one scalar per token, so the
+  //    piece is kept as S = sigma * St: the decay multiplies sigma and each
+  //    token costs one FMA per element (St += k (w / sigma)^T) instead of a
+  //    multiply and an FMA. KDA decays rows by different gates and updates S
+  //    directly.
+  // 4. write the state back (the only HBM write of S), then
+  // 5. refresh the sketch from the register-resident state: Sk[m] = S^T b_m.
   //    Eight basis rows at a time; the d_k reduction is a reduce-scatter over
   //    the 8 row groups, after which lane group rg holds basis row m0 + rg.
-  if (sketch != nullptr) {
+  auto finish = [&]() {
+    if (n > 0) {
+#pragma unroll
+      for (int m = 0; m < RPL; ++m)
+        *reinterpret_cast<float4*>(Su + (size_t)(row0 + m) * DV + col) = s[m];
+    }
+    if (sketch == nullptr) return;
     float* Sku = sketch + (size_t)unit * rank * DV;
     const bool b3 = (lane >> 3) & 1;
     for (int m0 = 0; m0 < rank; m0 += 8) {
@@ -171,16 +120,75 @@ update_refresh_kernel(float* __restrict__ state, float* __restrict__ sketch,
       const int m = m0 + rg;
       if (m < rank) *reinterpret_cast<float4*>(Sku + (size_t)m * DV + col) = res;
     }
+  };
+
+  if constexpr (RULE == KDA) {
+#pragma unroll 1
+    for (int t = 0; t < n; ++t) {
+      float kr[RPL], ar[RPL];
+      Vec<float, RPL>::load(lk + t * DK + row0, kr);
+      Vec<float, RPL>::load(ld + t * DK + row0, ar);
+      const float4 vv = *reinterpret_cast<const float4*>(lv + t * DV + col);
+      const float b = lb[t];
+      float4 p = f4(0.f);
+#pragma unroll
+      for (int m = 0; m < RPL; ++m) {
+        s[m] = scale4(ar[m], s[m]);  // Diag(alpha) S
+        p = fma4(kr[m], s[m], p);
+      }
+      p = tile_allreduce(p);
+      const float4 w = scale4(b, sub4(vv, p));
+#pragma unroll
+      for (int m = 0; m < RPL; ++m) s[m] = fma4(kr[m], w, s[m]);
+    }
+    finish();
+  } else {
+    // Mamba-2 and GDN decay the whole state by one scalar a_t per token. With
+    // rho_t = a_{t+1} ... a_{n-1} (the decay still to come after token t), the
+    // tile carries X_t = rho_t S_t instead of S_t:
+    //   X_{-1} = rho_{-1} S_win,   X_t = X_{t-1} + k_t (rho_t w_t)^T,   X_{n-1} = S,
+    // with rho_t w_t = rho_t v_t (Mamba-2) or b_t (rho_t v_t - X_{t-1}^T k_t)
+    // (GDN, since rho_t a_t = rho_{t-1}). Each token then costs one FMA per
+    // element for the write (plus one for the GDN reduction); the decay is a
+    // single scaling of the tile per window. No division: rho is a product of
+    // gates, a zero gate simply clears what came before it.
+    // Lane L holds rho_{L-1} = a_L ... a_{n-1} (lanes >= n hold 1).
+    float rho = 1.f;
+    for (int j = lane; j < n; ++j) rho *= ld[j];
+    const float rho_start = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rho), 0));
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) s[m] = scale4(rho_start, s[m]);
+#pragma unroll 1
+    for (int t = 0; t < n; ++t) {
+      float kr[RPL];
+      Vec<float, RPL>::load(lk + t * DK + row0, kr);
+      const float4 vv = *reinterpret_cast<const float4*>(lv + t * DV + col);
+      const float rho_t = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(rho), t + 1));
+      float4 w = scale4(rho_t, vv);
+      if constexpr (RULE == GDN) {
+        float4 p = f4(0.f);
+#pragma unroll
+        for (int m = 0; m < RPL; ++m) p = fma4(kr[m], s[m], p);
+        p = tile_allreduce(p);  // X_{t-1}^T k for this lane's 4 columns
+        w = scale4(lb[t], sub4(w, p));
+      }
+#pragma unroll
+      for (int m = 0; m < RPL; ++m) s[m] = fma4(kr[m], w, s[m]);
+    }
+    finish();
   }
 }
 
 }  // namespace
 
 size_t update_refresh_lds_bytes(const ssm_dims& d, int n, bool refresh) {
-  const int dstr = (d.rule == SSM_KDA) ? d.d_k : 1;
-  size_t floats = (size_t)n * d.d_k + (size_t)n * d.d_v + pad4(n * dstr) +
-                  ((d.rule == SSM_MAMBA2) ? 0 : pad4(n)) + (refresh ? (size_t)d.rank * d.d_k : 0);
-  return floats * sizeof(float);
+  size_t floats = 0;
+  dispatch(d.rule, SSM_IN_F32, d.d_k, d.d_v, [&](auto R, auto DK, auto DV, auto) {
+    floats = (size_t)window_lds_floats<decltype(R)::value, decltype(DK)::value,
+                                       decltype(DV)::value>(n);
+    return hipSuccess;
+  });
+  return (floats + (refresh ? (size_t)d.rank * d.d_k : 0)) * sizeof(float);
 }
 
 hipError_t launch_update_refresh(const ssm_dims& d, float* state, float* sketch,

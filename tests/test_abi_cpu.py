@@ -213,3 +213,14 @@ def test_binding_checks_tensor_sizes_on_host():
     d = dims()
     with pytest.raises(ValueError, match="device tensor"):
         ssm.window_update_refresh(d, torch.zeros(4), None, None, None, None, None, None, 0)
+
+
+def test_one_hip_runtime_in_the_process():
+    """The library shares PyTorch's HIP runtime: two runtimes in one process
+    leave the second one without a device."""
+    import os
+    maps = open("/proc/self/maps").read().splitlines()
+    hip = {os.path.realpath(l.split()[-1]) for l in maps if "libamdhip64" in l}
+    hsa = {os.path.realpath(l.split()[-1]) for l in maps if "libhsa-runtime64" in l}
+    assert len(hip) == 1, hip
+    assert len(hsa) <= 1, hsa
