@@ -7,7 +7,10 @@ sketch rank r=8. One timed step is one decode step of the whole layer: the
 current token is appended to the window buffer and the output is read from
 the sketch (one fused launch); after every W-th step the fused update +
 refresh writes the state once and stores the new sketch. K must be a multiple
-of W so that every window's state write is inside the timed region.
+of W so that every window's state write is inside the timed region. The K
+timed steps are captured once into a HIP graph and the headline times one
+replay of it; the same steps launched one by one are timed too (eager), with
+HIP events around every update + refresh launch for the roofline.
 
 Prints one JSON line. Extra fields: per-kernel times, the exact full-read path
 on the same tokens (the comparison), the byte model, the sketch's
@@ -141,36 +144,44 @@ def main() -> int:
     y = torch.empty((cfg.batch, cfg.heads, cfg.d_v), device=dev)
     stream = torch.cuda.current_stream()
 
-    def run_sketch(state, sketch, t_lo, t_hi, upd_events=None, only=None):
+    # Raw device addresses: the timed loops go straight through the C ABI.
+    P = lambda x: None if x is None else x.data_ptr()
+    ptrs = [tuple(P(x) for x in step) for step in inputs]
+    kb, vb, db, bb = (P(x) for x in bufs)
+    yp, bp = P(y), P(basis)
+
+    def run_sketch(state_p, sketch_p, t_lo, t_hi, sp, upd_events=None, only=None):
+        """Sketch path: fused append + sketch read per step, update + refresh per window."""
         for t in range(t_lo, t_hi):
-            q, k, v, dc, b = inputs[t]
+            q, k, v, dc, b = ptrs[t]
             tau = t % W + 1
             if only in (None, "sketch"):
-                ssm.sketch_decode_step(d, sketch, basis, q, *bufs, tau, y, k_t=k, v_t=v,
-                                       decay_t=dc, beta_t=b, stream=stream)
+                ssm.sketch_decode_step(d, sketch_p, bp, q, kb, vb, db, bb, tau, yp, k_t=k, v_t=v,
+                                       decay_t=dc, beta_t=b, stream=sp)
             elif only == "update":  # keep the buffer fed without the read
-                ssm.buffer_append(d, k, v, dc, b, *bufs, tau - 1, stream=stream)
+                ssm.buffer_append(d, k, v, dc, b, kb, vb, db, bb, tau - 1, stream=sp)
             if tau == W and only in (None, "update"):
                 if upd_events is not None:
                     upd_events.append((torch.cuda.Event(enable_timing=True),
                                        torch.cuda.Event(enable_timing=True)))
                     upd_events[-1][0].record(stream)
-                ssm.window_update_refresh(d, state, sketch, basis, *bufs, W, stream=stream)
+                ssm.window_update_refresh(d, state_p, sketch_p, bp, kb, vb, db, bb, W, stream=sp)
                 if upd_events is not None:
                     upd_events[-1][1].record(stream)
 
-    def run_full(state, t_lo, t_hi, upd_events=None):
+    def run_full(state_p, t_lo, t_hi, sp, upd_events=None):
+        """Exact buffered path: fused append + full-state read per step, update per window."""
         for t in range(t_lo, t_hi):
-            q, k, v, dc, b = inputs[t]
+            q, k, v, dc, b = ptrs[t]
             tau = t % W + 1
-            ssm.full_read_decode_step(d, state, q, *bufs, tau, y, k_t=k, v_t=v, decay_t=dc,
-                                      beta_t=b, stream=stream)
+            ssm.full_read_decode_step(d, state_p, q, kb, vb, db, bb, tau, yp, k_t=k, v_t=v,
+                                      decay_t=dc, beta_t=b, stream=sp)
             if tau == W:
                 if upd_events is not None:
                     upd_events.append((torch.cuda.Event(enable_timing=True),
                                        torch.cuda.Event(enable_timing=True)))
                     upd_events[-1][0].record(stream)
-                ssm.window_update_refresh(d, state, None, None, *bufs, W, stream=stream)
+                ssm.window_update_refresh(d, state_p, None, None, kb, vb, db, bb, W, stream=sp)
                 if upd_events is not None:
                     upd_events[-1][1].record(stream)
 
@@ -183,52 +194,74 @@ def main() -> int:
         e1.record(stream)
         torch.cuda.synchronize()
         wall = time.perf_counter() - w0
-        return e0.elapsed_time(e1) / 1e3, wall
+        return max(e0.elapsed_time(e1) / 1e3, wall)
 
-    # ---- the sketch path (headline) ---------------------------------------------------
-    state = S0_dev.clone()
-    sketch = torch.empty((cfg.batch, cfg.heads, cfg.rank, cfg.d_v), device=dev)
-    ssm.window_update_refresh(d, state, sketch, basis, None, None, None, None, 0, stream=stream)
-    run_sketch(state, sketch, 0, a.warmup, only=a.only)
-    upd_ev = []
-    gpu_s, wall_s = timed(lambda: run_sketch(state, sketch, a.warmup, total, upd_ev, only=a.only))
-    elapsed = max(gpu_s, wall_s)
-    upd_ms = [s.elapsed_time(e) for s, e in upd_ev]
+    def graph_timed(enqueue):
+        """Capture the K timed steps into one HIP graph, replay once untimed, then time a replay."""
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=cap):
+            enqueue(cap.cuda_stream)
+        torch.cuda.synchronize()
+        g.replay()
+        return timed(g.replay), g
+
+    sp = stream.cuda_stream
     bm = bytes_model(cfg)
 
+    # ---- the sketch path, eager launches (update kernel timed by HIP events) ---------
+    state = S0_dev.clone()
+    sketch = torch.empty((cfg.batch, cfg.heads, cfg.rank, cfg.d_v), device=dev)
+    st_p, sk_p = P(state), P(sketch)
+    ssm.window_update_refresh(d, st_p, sk_p, bp, None, None, None, None, 0, stream=sp)
+    run_sketch(st_p, sk_p, 0, a.warmup, sp, only=a.only)
+    upd_ev = []
+    eager_s = timed(lambda: run_sketch(st_p, sk_p, a.warmup, total, sp, upd_ev, only=a.only))
+    upd_ms = [s_.elapsed_time(e_) for s_, e_ in upd_ev]
+
     if a.only is not None:  # profiling runs stop here
-        print(json.dumps({"only": a.only, "steps": a.steps, "ms_per_step": elapsed * 1e3 / a.steps}))
+        print(json.dumps({"only": a.only, "steps": a.steps, "ms_per_step": eager_s * 1e3 / a.steps}))
         return 0
+
+    # ---- the sketch path as one HIP graph (headline) -----------------------------------
+    graph_s, g_sketch = graph_timed(lambda cs: run_sketch(st_p, sk_p, a.warmup, total, cs))
+    elapsed = graph_s
+    del g_sketch
 
     # ---- per-kernel time of the sketch read (events around each launch) ---------------
     def kernel_time(launch, reps):
         evs = []
         for i in range(reps):
-            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            s.record(stream)
+            s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s_.record(stream)
             launch(i)
-            e.record(stream)
-            evs.append((s, e))
+            e_.record(stream)
+            evs.append((s_, e_))
         torch.cuda.synchronize()
-        return float(np.mean([s.elapsed_time(e) for s, e in evs]))
+        return float(np.mean([s_.elapsed_time(e_) for s_, e_ in evs]))
 
     tau_mid = W // 2 + 1
-    q0 = inputs[0][0]
-    sketch_ms = kernel_time(lambda i: ssm.sketch_decode_step(d, sketch, basis, q0, *bufs, tau_mid, y,
-                                                             stream=stream), 20)
-    full_ms = kernel_time(lambda i: ssm.full_read_decode_step(d, state, q0, *bufs, tau_mid, y,
-                                                              stream=stream), 10)
+    q0 = ptrs[0][0]
+    sketch_ms = kernel_time(lambda i: ssm.sketch_decode_step(d, sk_p, bp, q0, kb, vb, db, bb,
+                                                             tau_mid, yp, stream=sp), 20)
+    full_ms = kernel_time(lambda i: ssm.full_read_decode_step(d, st_p, q0, kb, vb, db, bb,
+                                                              tau_mid, yp, stream=sp), 10)
 
     # ---- the exact full-read path on the same tokens (comparison) ----------------------
     full = None
     if not a.no_compare:
         state_f = S0_dev.clone()
-        run_full(state_f, 0, a.warmup)
+        sf_p = P(state_f)
+        run_full(sf_p, 0, a.warmup, sp)
         upd_f = []
-        gpu_f, wall_f = timed(lambda: run_full(state_f, a.warmup, total, upd_f))
-        el_f = max(gpu_f, wall_f)
-        full = {"steps_per_s": a.steps / el_f, "ms_per_step": el_f * 1e3 / a.steps,
-                "update_no_refresh_ms": float(np.mean([s.elapsed_time(e) for s, e in upd_f]))}
+        eager_f = timed(lambda: run_full(sf_p, a.warmup, total, sp, upd_f))
+        graph_f, g_full = graph_timed(lambda cs: run_full(sf_p, a.warmup, total, cs))
+        del g_full
+        full = {"steps_per_s": a.steps / graph_f, "ms_per_step": graph_f * 1e3 / a.steps,
+                "eager_steps_per_s": a.steps / eager_f,
+                "update_no_refresh_ms": float(np.mean([s_.elapsed_time(e_) for s_, e_ in upd_f]))}
         del state_f
 
     # ---- approximation error of the sketch read vs the exact read (untimed) -----------
@@ -324,6 +357,7 @@ def main() -> int:
                        "full_read_decode": full_ms},
         "sketch_decode_gbs": bm["sketch_step"] * U / (sketch_ms * 1e-3) / 1e9,
         "full_read_decode_gbs": bm["full_step"] * U / (full_ms * 1e-3) / 1e9,
+        "eager_steps_per_s": a.steps / eager_s,
         "full_read_path": full,
         "speedup_vs_full_read": (value / full["steps_per_s"]) if full else None,
         "bytes_per_unit": {k: bm[k] for k in ("state_bytes_sketch", "state_bytes_full", "sketch_step",

@@ -4,7 +4,9 @@ A thin ctypes binding over ``libsketchssm.so`` (C ABI in
 ``include/sketchssm.h``). Each function here marshals its arguments and calls
 the library entry point of the same name; every step of the decode path runs
 in the library's HIP kernels. Tensors are PyTorch device tensors (PyTorch
-provides memory and streams only) or raw device addresses as ``int``.
+provides memory and streams only) or raw device addresses as ``int``; a call
+whose pointers and stream are all ``int`` goes straight to the library (the
+library still checks the arguments, but not their sizes).
 
 If the library has not been built this module raises on import: there is no
 fallback path.
@@ -173,11 +175,19 @@ def _types(d: Dims, args):
     return _in_types(d), _f32()
 
 
+def _all_raw(args) -> bool:
+    return all(a is None or isinstance(a, int) for a in args)
+
+
 # ----------------------------------------------------------------------------
 # entry points (same names as the C ABI, without the ssm_ prefix)
 # ----------------------------------------------------------------------------
 def buffer_append(d: Dims, k_t, v_t, decay_t, beta_t, k_buf, v_buf, decay_buf, beta_buf,
                   slot: int, stream=None) -> None:
+    if isinstance(stream, int) and _all_raw((k_t, v_t, decay_t, beta_t, k_buf, v_buf, decay_buf,
+                                             beta_buf)):
+        return _check(_lib.ssm_buffer_append(ctypes.byref(d), k_t, v_t, decay_t, beta_t, k_buf,
+                                             v_buf, decay_buf, beta_buf, slot, stream))
     tin, f32 = _types(d, (k_t, v_t, decay_t, beta_t, k_buf, v_buf, decay_buf, beta_buf))
     n = numel(d)
     _check(_lib.ssm_buffer_append(
@@ -190,6 +200,10 @@ def buffer_append(d: Dims, k_t, v_t, decay_t, beta_t, k_buf, v_buf, decay_buf, b
 
 def window_update_refresh(d: Dims, state, sketch, basis, k_buf, v_buf, decay_buf, beta_buf,
                           n_tokens: int, stream=None) -> None:
+    if isinstance(stream, int) and _all_raw((state, sketch, basis, k_buf, v_buf, decay_buf,
+                                             beta_buf)):
+        return _check(_lib.ssm_window_update_refresh(ctypes.byref(d), state, sketch, basis, k_buf,
+                                                     v_buf, decay_buf, beta_buf, n_tokens, stream))
     tin, f32 = _types(d, (state, sketch, basis, k_buf, v_buf, decay_buf, beta_buf))
     n = numel(d)
     _check(_lib.ssm_window_update_refresh(
@@ -201,6 +215,11 @@ def window_update_refresh(d: Dims, state, sketch, basis, k_buf, v_buf, decay_buf
 
 def sketch_decode_step(d: Dims, sketch, basis, q, k_buf, v_buf, decay_buf, beta_buf, tau: int,
                        y, *, k_t=None, v_t=None, decay_t=None, beta_t=None, stream=None) -> None:
+    if isinstance(stream, int) and _all_raw((sketch, basis, q, k_buf, v_buf, decay_buf, beta_buf,
+                                             y, k_t, v_t, decay_t, beta_t)):
+        return _check(_lib.ssm_sketch_decode_step(ctypes.byref(d), sketch, basis, q, k_t, v_t,
+                                                  decay_t, beta_t, k_buf, v_buf, decay_buf,
+                                                  beta_buf, tau, y, stream))
     tin, f32 = _types(d, (sketch, basis, q, k_buf, v_buf, decay_buf, beta_buf, y, k_t, v_t))
     n = numel(d)
     _check(_lib.ssm_sketch_decode_step(
@@ -214,6 +233,11 @@ def sketch_decode_step(d: Dims, sketch, basis, q, k_buf, v_buf, decay_buf, beta_
 
 def full_read_decode_step(d: Dims, state, q, k_buf, v_buf, decay_buf, beta_buf, tau: int, y, *,
                           k_t=None, v_t=None, decay_t=None, beta_t=None, stream=None) -> None:
+    if isinstance(stream, int) and _all_raw((state, q, k_buf, v_buf, decay_buf, beta_buf, y, k_t,
+                                             v_t, decay_t, beta_t)):
+        return _check(_lib.ssm_full_read_decode_step(ctypes.byref(d), state, q, k_t, v_t, decay_t,
+                                                     beta_t, k_buf, v_buf, decay_buf, beta_buf,
+                                                     tau, y, stream))
     tin, f32 = _types(d, (state, q, k_buf, v_buf, decay_buf, beta_buf, y, k_t, v_t))
     n = numel(d)
     _check(_lib.ssm_full_read_decode_step(

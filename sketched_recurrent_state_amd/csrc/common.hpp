@@ -243,6 +243,24 @@ __device__ __forceinline__ float group_allreduce(float x) {
 }
 
 // ---------------------------------------------------------------------------
+// streaming (non-temporal) 128-bit accesses: for data touched once per window
+// (the full state), so it does not push the sketch and the window buffer,
+// which every step re-reads, out of the caches.
+// ---------------------------------------------------------------------------
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 load_stream(const float* p) {
+  const v4f v = __builtin_nontemporal_load(reinterpret_cast<const v4f*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void store_stream(float* p, float4 x) {
+  v4f v;
+  v.x = x.x; v.y = x.y; v.z = x.z; v.w = x.w;
+  __builtin_nontemporal_store(v, reinterpret_cast<v4f*>(p));
+}
+
+// ---------------------------------------------------------------------------
 // float4 helpers
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float4 f4(float a) { return make_float4(a, a, a, a); }

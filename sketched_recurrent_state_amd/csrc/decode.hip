@@ -37,10 +37,13 @@ __device__ __forceinline__ void carry_back(float* u, const float* kk, const floa
 
 // ---------------------------------------------------------------------------
 // sketch read: G consecutive lanes per unit (G = 32, or 16 when d_k = 16).
-// Every load of the step (query, the tau buffered tokens, the first eight
-// basis rows and sketch rows) is issued before any arithmetic, so a step pays
-// one memory latency instead of one per token and one per basis vector.
-// WMAX >= W bounds the unrolled token slots.
+// A workgroup serves 256/G sequences of ONE head, so the head's basis is
+// staged once in LDS for all of them. Every global load of the step (query,
+// the tau buffered tokens, the first eight sketch rows, the basis) is issued
+// before any arithmetic: a step pays one memory latency instead of one per
+// token and one per basis vector. WMAX >= W bounds the unrolled token slots.
+// Scalar gates stay one per lane (lane i of a unit holds token i's) and are
+// broadcast when the walk reaches that token.
 // ---------------------------------------------------------------------------
 template <int DK>
 constexpr int sketch_group() { return DK >= 32 ? 32 : 16; }
@@ -52,120 +55,131 @@ sketch_decode_kernel(const float* __restrict__ sketch, const float* __restrict__
                      const TIN* __restrict__ v_t, const float* __restrict__ d_t,
                      const float* __restrict__ b_t, TIN* __restrict__ kbuf,
                      TIN* __restrict__ vbuf, float* __restrict__ dbuf, float* __restrict__ bbuf,
-                     float* __restrict__ y, int units, int heads, int window, int rank, int tau) {
+                     float* __restrict__ y, int batch, int heads, int window, int rank, int tau) {
   constexpr int G = sketch_group<DK>();
+  static_assert(WMAX <= G, "one gate per lane");
+  constexpr int UPB = 256 / G;                // sequences per workgroup
   constexpr int EK = DK / G, EV = DV / G;
-  constexpr int DSTR = (RULE == KDA) ? DK : 1;
-  constexpr int EA = (RULE == KDA) ? EK : 1;  // gate values per lane and token
-  constexpr int RCH = 8;                      // basis rows fetched ahead of the walk
+  constexpr int RCH = 8;                      // sketch rows fetched ahead of the walk
 
-  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
-  const int unit = gid / G, sub = gid % G;
-  if (unit >= units) return;  // whole G-lane groups leave together
-  const int head = unit % heads;
-  const size_t slot0 = (size_t)unit * window;
+  extern __shared__ float4 lds4[];
+  float* lB = reinterpret_cast<float*>(lds4);  // [rank][DK]
+
+  const int head = blockIdx.x % heads;
+  const int seq = (blockIdx.x / heads) * UPB + threadIdx.x / G;
+  const int sub = threadIdx.x % G;
+  const bool active = seq < batch;            // whole G-lane groups
+  const size_t unit = (size_t)seq * heads + head;
+  const size_t slot0 = unit * window;
   const bool fused = (k_t != nullptr);
 
   // ---- issue every load ----
-  Packed<TIN, EK> qr;
-  qr.load(q + (size_t)unit * DK + sub * EK);
-  Packed<TIN, EK> kr[WMAX];
+  Packed<TIN, EK> qr, kr[WMAX];
   Packed<TIN, EV> vr[WMAX];
-  float ar[WMAX][EA], br[WMAX];
-#pragma unroll
-  for (int i = 0; i < WMAX; ++i) {
-    if (i < tau) {
-      const bool cur = fused && (i == tau - 1);
-      const size_t slot = slot0 + i;
-      kr[i].load((cur ? k_t + (size_t)unit * DK : kbuf + slot * DK) + sub * EK);
-      vr[i].load((cur ? v_t + (size_t)unit * DV : vbuf + slot * DV) + sub * EV);
-      const float* dp = cur ? d_t + (size_t)unit * DSTR : dbuf + slot * DSTR;
-      if constexpr (RULE == KDA) {
-        Vec<float, EK>::load(dp + sub * EK, ar[i]);
-      } else {
-        ar[i][0] = dp[0];
-      }
-      br[i] = 1.f;
-      if constexpr (RULE != MAMBA2) br[i] = cur ? b_t[unit] : bbuf[slot];
-    }
-  }
-  const float* Bh = basis + (size_t)head * rank * DK + sub * EK;
-  const float* Sku = sketch + (size_t)unit * rank * DV + sub * EV;
-  float bm[RCH][EK], sk[RCH][EV];
-#pragma unroll
-  for (int m = 0; m < RCH; ++m) {
-    if (m < rank) {
-      Vec<float, EK>::load(Bh + (size_t)m * DK, bm[m]);
-      Vec<float, EV>::load(Sku + (size_t)m * DV, sk[m]);
-    }
-  }
-
-  // ---- fused append: the current token into slot tau-1 ----
-  if (fused) {
+  float ak[(RULE == KDA) ? WMAX : 1][EK];     // KDA: per-channel gates of each token
+  float a_lane = 1.f, b_lane = 1.f;           // scalar gates of token `sub`
+  float sk[RCH][EV];
+  const float* Sku = sketch + unit * rank * DV + sub * EV;
+  if (active) {
+    qr.load(q + unit * DK + sub * EK);
 #pragma unroll
     for (int i = 0; i < WMAX; ++i) {
-      if (i == tau - 1) {
+      if (i < tau) {
+        const bool cur = fused && (i == tau - 1);
         const size_t slot = slot0 + i;
-        kr[i].store(kbuf + slot * DK + sub * EK);
-        vr[i].store(vbuf + slot * DV + sub * EV);
+        kr[i].load((cur ? k_t + unit * DK : kbuf + slot * DK) + sub * EK);
+        vr[i].load((cur ? v_t + unit * DV : vbuf + slot * DV) + sub * EV);
+        if constexpr (RULE == KDA)
+          Vec<float, EK>::load((cur ? d_t + unit * DK : dbuf + slot * DK) + sub * EK, ak[i]);
+      }
+    }
+    if (sub < tau) {
+      const bool cur = fused && (sub == tau - 1);
+      if constexpr (RULE != KDA) a_lane = cur ? d_t[unit] : dbuf[slot0 + sub];
+      if constexpr (RULE != MAMBA2) b_lane = cur ? b_t[unit] : bbuf[slot0 + sub];
+    }
+#pragma unroll
+    for (int m = 0; m < RCH; ++m)
+      if (m < rank) Vec<float, EV>::load(Sku + (size_t)m * DV, sk[m]);
+  }
+  {
+    const float* Bh = basis + (size_t)head * rank * DK;
+    for (int e = threadIdx.x * 4; e < rank * DK; e += 256 * 4)
+      *reinterpret_cast<float4*>(lB + e) = *reinterpret_cast<const float4*>(Bh + e);
+  }
+
+  float u[EK], acc[EV];
+#pragma unroll
+  for (int e = 0; e < EV; ++e) acc[e] = 0.f;
+  if (active) {
+    // ---- fused append: the current token into slot tau-1 ----
+    if (fused) {
+      const size_t slot = slot0 + tau - 1;
+#pragma unroll
+      for (int i = 0; i < WMAX; ++i) {
+        if (i == tau - 1) {
+          kr[i].store(kbuf + slot * DK + sub * EK);
+          vr[i].store(vbuf + slot * DV + sub * EV);
+          if constexpr (RULE == KDA) Vec<float, EK>::store(dbuf + slot * DK + sub * EK, ak[i]);
+        }
+      }
+      if (sub == tau - 1) {
+        if constexpr (RULE != KDA) dbuf[slot] = a_lane;
+        if constexpr (RULE != MAMBA2) bbuf[slot] = b_lane;
+      }
+    }
+
+    // ---- walk the window newest to oldest ----
+    qr.unpack(u);
+#pragma unroll
+    for (int i = WMAX - 1; i >= 0; --i) {
+      if (i < tau) {
+        float kk[EK], vv[EV], a[(RULE == KDA) ? EK : 1];
+        kr[i].unpack(kk);
+        vr[i].unpack(vv);
         if constexpr (RULE == KDA) {
-          Vec<float, EK>::store(dbuf + slot * DK + sub * EK, ar[i]);
+#pragma unroll
+          for (int e = 0; e < EK; ++e) a[e] = ak[i][e];
         } else {
-          if (sub == 0) dbuf[slot] = ar[i][0];
+          a[0] = __shfl(a_lane, i, G);
         }
-        if constexpr (RULE != MAMBA2) {
-          if (sub == 0) bbuf[slot] = br[i];
-        }
+        const float b = (RULE == MAMBA2) ? 1.f : __shfl(b_lane, i, G);
+        float s = 0.f;
+#pragma unroll
+        for (int e = 0; e < EK; ++e) s = fmaf(kk[e], u[e], s);
+        s = group_allreduce<G>(s);
+        const float bs = b * s;
+#pragma unroll
+        for (int e = 0; e < EV; ++e) acc[e] = fmaf(bs, vv[e], acc[e]);
+        carry_back<RULE, EK>(u, kk, a, bs);
       }
     }
   }
-
-  // ---- walk the window newest to oldest ----
-  float u[EK], acc[EV];
-  qr.unpack(u);
-#pragma unroll
-  for (int e = 0; e < EV; ++e) acc[e] = 0.f;
-#pragma unroll
-  for (int i = WMAX - 1; i >= 0; --i) {
-    if (i < tau) {
-      float kk[EK], vv[EV];
-      kr[i].unpack(kk);
-      vr[i].unpack(vv);
-      float s = 0.f;
-#pragma unroll
-      for (int e = 0; e < EK; ++e) s = fmaf(kk[e], u[e], s);
-      s = group_allreduce<G>(s);
-      const float bs = br[i] * s;
-#pragma unroll
-      for (int e = 0; e < EV; ++e) acc[e] = fmaf(bs, vv[e], acc[e]);
-      carry_back<RULE, EK>(u, kk, ar[i], bs);
-    }
-  }
+  __syncthreads();  // the basis is in LDS
+  if (!active) return;
 
   // ---- c_m = b_m . q~ ; y = intra + sum_m c_m Sk[m] ----
   for (int m0 = 0; m0 < rank; m0 += RCH) {
     if (m0 > 0) {
 #pragma unroll
-      for (int m = 0; m < RCH; ++m) {
-        if (m0 + m < rank) {
-          Vec<float, EK>::load(Bh + (size_t)(m0 + m) * DK, bm[m]);
-          Vec<float, EV>::load(Sku + (size_t)(m0 + m) * DV, sk[m]);
-        }
-      }
+      for (int m = 0; m < RCH; ++m)
+        if (m0 + m < rank) Vec<float, EV>::load(Sku + (size_t)(m0 + m) * DV, sk[m]);
     }
 #pragma unroll
     for (int m = 0; m < RCH; ++m) {
       if (m0 + m < rank) {
+        float bm[EK];
+        Vec<float, EK>::load(lB + (m0 + m) * DK + sub * EK, bm);
         float c = 0.f;
 #pragma unroll
-        for (int e = 0; e < EK; ++e) c = fmaf(bm[m][e], u[e], c);
+        for (int e = 0; e < EK; ++e) c = fmaf(bm[e], u[e], c);
         c = group_allreduce<G>(c);
 #pragma unroll
         for (int e = 0; e < EV; ++e) acc[e] = fmaf(c, sk[m][e], acc[e]);
       }
     }
   }
-  Vec<float, EV>::store(y + (size_t)unit * DV + sub * EV, acc);
+  Vec<float, EV>::store(y + unit * DV + sub * EV, acc);
 }
 
 // ---------------------------------------------------------------------------
@@ -202,7 +216,7 @@ full_read_kernel(const float* __restrict__ state, const TIN* __restrict__ q,
   float4 s[RPL];
 #pragma unroll
   for (int m = 0; m < RPL; ++m)
-    s[m] = *reinterpret_cast<const float4*>(Su + (size_t)(row0 + m) * DV + col);
+    s[m] = load_stream(Su + (size_t)(row0 + m) * DV + col);
   float u[RPL];
   Vec<TIN, RPL>::load(q + (size_t)unit * DK + row0, u);
 
@@ -254,17 +268,17 @@ hipError_t launch_sketch_decode(const ssm_dims& d, const float* sketch, const fl
                                 const float* decay_t, const float* beta_t, void* k_buf,
                                 void* v_buf, float* decay_buf, float* beta_buf, int tau, float* y,
                                 hipStream_t stream) {
-  const unsigned units = (unsigned)d.batch * (unsigned)d.heads;
   return dispatch(d.rule, d.in_dtype, d.d_k, d.d_v, [&](auto R, auto DK, auto DV, auto T) {
     using TIN = typename decltype(T)::type;
     constexpr int kR = decltype(R)::value, kDK = decltype(DK)::value, kDV = decltype(DV)::value;
-    constexpr unsigned G = sketch_group<kDK>();
-    const unsigned blocks = (units * G + 255u) / 256u;
+    constexpr unsigned UPB = 256u / sketch_group<kDK>();
+    const unsigned blocks = (unsigned)d.heads * (((unsigned)d.batch + UPB - 1) / UPB);
+    const size_t lds = (size_t)d.rank * kDK * sizeof(float);
     auto go = [&](auto kernel) {
-      hipLaunchKernelGGL(kernel, dim3(blocks), dim3(256), 0, stream, sketch, basis,
+      hipLaunchKernelGGL(kernel, dim3(blocks), dim3(256), lds, stream, sketch, basis,
                          static_cast<const TIN*>(q), static_cast<const TIN*>(k_t),
                          static_cast<const TIN*>(v_t), decay_t, beta_t, static_cast<TIN*>(k_buf),
-                         static_cast<TIN*>(v_buf), decay_buf, beta_buf, y, (int)units, d.heads,
+                         static_cast<TIN*>(v_buf), decay_buf, beta_buf, y, d.batch, d.heads,
                          d.window, d.rank, tau);
       return hipGetLastError();
     };

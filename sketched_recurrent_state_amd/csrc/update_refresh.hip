@@ -44,7 +44,7 @@ update_refresh_kernel(float* __restrict__ state, float* __restrict__ sketch,
   float4 s[RPL];
 #pragma unroll
   for (int m = 0; m < RPL; ++m)
-    s[m] = *reinterpret_cast<const float4*>(Su + (size_t)(row0 + m) * DV + col);
+    s[m] = load_stream(Su + (size_t)(row0 + m) * DV + col);
 
   // 2. stage the window (and the basis) in LDS as fp32
   const size_t slot0 = (size_t)unit * window;
@@ -81,7 +81,7 @@ update_refresh_kernel(float* __restrict__ state, float* __restrict__ sketch,
     if (n > 0) {
 #pragma unroll
       for (int m = 0; m < RPL; ++m)
-        *reinterpret_cast<float4*>(Su + (size_t)(row0 + m) * DV + col) = s[m];
+        store_stream(Su + (size_t)(row0 + m) * DV + col, s[m]);
     }
     if (sketch == nullptr) return;
     float* Sku = sketch + (size_t)unit * rank * DV;
