@@ -33,7 +33,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, HERE)
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
-TRAFFIC_FILE = os.path.join(HERE, "profiles", "update_refresh_gdn_n256_h32_128x128_w8_r8.traffic.json")
+# rocprofv3 FETCH_SIZE / WRITE_SIZE summary of the update + refresh kernel on this workload
+TRAFFIC_FILE = os.path.join(HERE, "profiles", "update_refresh_gdn_n256_h32_128x128_w8_r8.pmc.md")
 KERNEL_SOURCES = ["common.hpp", "update_refresh.hip"]
 
 
@@ -301,10 +302,15 @@ def main() -> int:
     achieved = upd_bytes / (upd_avg_ms * 1e-3) / 1e9
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
+        tr = {}
         with open(TRAFFIC_FILE) as fh:
-            tr = json.load(fh)
+            for line in fh:
+                key, sep, val = line.strip().partition(": ")
+                if sep and key in ("config", "kernel_source_hash", "bytes_per_launch"):
+                    tr[key] = val
+        # counters taken on another kernel version do not describe this one
         if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("config") == cfg.name:
-            traffic = tr.get("bytes_per_launch")
+            traffic = float(tr["bytes_per_launch"])
 
     # ---- CPU baseline: the oracle on a bounded sample --------------------------------
     cpu = None
