@@ -12,9 +12,11 @@ timed steps are captured once into a HIP graph and the headline times one
 replay of it; the same steps launched one by one are timed too (eager), with
 HIP events around every update + refresh launch for the roofline.
 
-Prints one JSON line. Extra fields: per-kernel times, the exact full-read path
-on the same tokens (the comparison), the byte model, the sketch's
-approximation error, and the oracle's CPU rate on a bounded sample.
+Prints one JSON line. Extra fields: per-kernel times, two comparison paths on
+the same tokens (the exact buffered full read, and the per-token recurrent
+decode that updates and reads the whole state every step), the byte model,
+the sketch's approximation error, and the oracle's CPU rate on a bounded
+sample.
 
     python bench.py [--steps 64] [--warmup 16] [--config c3]
 """
@@ -65,6 +67,14 @@ def bytes_model(cfg) -> dict:
                 state_bytes_sketch=4 * r * dv, state_bytes_full=4 * dk * dv,
                 amortized_sketch=sketch_step + update / W,
                 amortized_full=full_step + update_no_refresh / W)
+
+
+def metric_name(cfg) -> str:
+    if cfg.name == "c3":
+        return "decode steps/sec and achieved HBM GB/s (% roofline), GDN 128×128 state, B=256, r=8"
+    rule = {"mamba2": "Mamba-2", "gdn": "GDN", "kda": "KDA"}[cfg.rule]
+    return (f"decode steps/sec and achieved HBM GB/s (% roofline), {rule} {cfg.d_k}×{cfg.d_v} "
+            f"state, B={cfg.batch}, H={cfg.heads}, W={cfg.window}, r={cfg.rank}")
 
 
 def main() -> int:
@@ -265,6 +275,31 @@ def main() -> int:
                 "update_no_refresh_ms": float(np.mean([s_.elapsed_time(e_) for s_, e_ in upd_f]))}
         del state_f
 
+    # ---- the per-token recurrent decode (the standard baseline) on the same tokens -----
+    per_token = None
+    if not a.no_compare:
+        state_r = S0_dev.clone()
+        sr_p = P(state_r)
+
+        def run_rec(state_p, t_lo, t_hi, sp_):
+            for t in range(t_lo, t_hi):
+                q, k, v, dc, b = ptrs[t]
+                ssm.recurrent_decode_step(d, state_p, q, k, v, dc, b, yp, stream=sp_)
+
+        run_rec(sr_p, 0, a.warmup, sp)
+        eager_r = timed(lambda: run_rec(sr_p, a.warmup, total, sp))
+        graph_r, g_rec = graph_timed(lambda cs: run_rec(sr_p, a.warmup, total, cs))
+        del g_rec
+        q0_, k0_, v0_, d0_, b0_ = ptrs[0]
+        rec_ms = kernel_time(lambda i: ssm.recurrent_decode_step(d, sr_p, q0_, k0_, v0_, d0_, b0_,
+                                                                 yp, stream=sp), 10)
+        rec_bytes = U * (8 * cfg.d_k * cfg.d_v + bm["tok"] + cfg.d_k * (2 if cfg.in_dtype == "bf16" else 4)
+                         + 4 * cfg.d_v)
+        per_token = {"steps_per_s": a.steps / graph_r, "ms_per_step": graph_r * 1e3 / a.steps,
+                     "eager_steps_per_s": a.steps / eager_r, "kernel_ms": rec_ms,
+                     "kernel_gbs": rec_bytes / (rec_ms * 1e-3) / 1e9}
+        del state_r
+
     # ---- approximation error of the sketch read vs the exact read (untimed) -----------
     st_a = S0_dev.clone()
     sk_a = torch.empty_like(sketch)
@@ -338,7 +373,7 @@ def main() -> int:
 
     value = a.steps / elapsed
     out = {
-        "metric": "decode steps/sec and achieved HBM GB/s (% roofline), GDN 128×128 state, B=256, r=8",
+        "metric": metric_name(cfg),
         "value": value,
         "unit": "decode steps/s",
         "n_gpus": 1,
@@ -366,6 +401,8 @@ def main() -> int:
         "eager_steps_per_s": a.steps / eager_s,
         "full_read_path": full,
         "speedup_vs_full_read": (value / full["steps_per_s"]) if full else None,
+        "per_token_path": per_token,
+        "speedup_vs_per_token": (value / per_token["steps_per_s"]) if per_token else None,
         "bytes_per_unit": {k: bm[k] for k in ("state_bytes_sketch", "state_bytes_full", "sketch_step",
                                               "full_step", "amortized_sketch", "amortized_full")},
         "state_bytes_ratio": bm["state_bytes_full"] / bm["state_bytes_sketch"],

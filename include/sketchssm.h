@@ -170,6 +170,21 @@ ssm_status ssm_full_read_decode_step(const ssm_dims* d,
                                      void* k_buf, void* v_buf, float* decay_buf, float* beta_buf,
                                      int32_t tau, float* y, void* stream);
 
+/*
+ * Per-token recurrent decode step (the standard decode SketchSSM is compared
+ * against: readsearch.ai listing, Abstract, kernel speedups over the standard
+ * vLLM baseline; agihunt.info "Confirmed", background bullet: every step reads
+ * the full state). For every unit, with the current token (k_t, v_t, decay_t,
+ * beta_t): S <- M S + b k v^T, S is written back, and y = S^T q is read from
+ * the updated state. No window buffer and no sketch; d->window and d->rank are
+ * checked but not used. Outputs: state (in/out), y.
+ */
+ssm_status ssm_recurrent_decode_step(const ssm_dims* d,
+                                     float* state, const void* q,
+                                     const void* k_t, const void* v_t,
+                                     const float* decay_t, const float* beta_t,
+                                     float* y, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

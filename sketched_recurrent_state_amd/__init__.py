@@ -20,7 +20,7 @@ from typing import Optional, Union
 __all__ = [
     "Dims", "SSMError", "MAMBA2", "GDN", "KDA", "IN_BF16", "IN_F32", "RULES",
     "abi_version", "buffer_append", "window_update_refresh", "sketch_decode_step",
-    "full_read_decode_step", "LIB_PATH", "HEADER", "declared_symbols",
+    "full_read_decode_step", "recurrent_decode_step", "LIB_PATH", "HEADER", "declared_symbols",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -67,7 +67,7 @@ def _load():
     import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m sketched_recurrent_state_amd.build`")
+            f"{LIB_PATH} is missing: build it with `python sketched_recurrent_state_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, dp = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(Dims)
     lib.ssm_abi_version.restype = i32
@@ -82,6 +82,8 @@ def _load():
     lib.ssm_window_update_refresh.argtypes = [dp] + [vp] * 7 + [i32, vp]
     lib.ssm_sketch_decode_step.restype = i32
     lib.ssm_sketch_decode_step.argtypes = [dp] + [vp] * 11 + [i32, vp, vp]
+    lib.ssm_recurrent_decode_step.restype = i32
+    lib.ssm_recurrent_decode_step.argtypes = [dp] + [vp] * 7 + [vp]
     lib.ssm_full_read_decode_step.restype = i32
     lib.ssm_full_read_decode_step.argtypes = [dp] + [vp] * 10 + [i32, vp, vp]
     return lib
@@ -247,3 +249,16 @@ def full_read_decode_step(d: Dims, state, q, k_buf, v_buf, decay_buf, beta_buf, 
         _addr(k_buf, "k_buf", tin, n["k_buf"]), _addr(v_buf, "v_buf", tin, n["v_buf"]),
         _addr(decay_buf, "decay_buf", f32, n["decay_buf"]), _addr(beta_buf, "beta_buf", f32, n["beta_buf"]),
         int(tau), _addr(y, "y", f32, n["y"]), _stream(stream)))
+
+
+def recurrent_decode_step(d: Dims, state, q, k_t, v_t, decay_t, beta_t, y, stream=None) -> None:
+    if isinstance(stream, int) and _all_raw((state, q, k_t, v_t, decay_t, beta_t, y)):
+        return _check(_lib.ssm_recurrent_decode_step(ctypes.byref(d), state, q, k_t, v_t, decay_t,
+                                                     beta_t, y, stream))
+    tin, f32 = _types(d, (state, q, k_t, v_t, decay_t, beta_t, y))
+    n = numel(d)
+    _check(_lib.ssm_recurrent_decode_step(
+        ctypes.byref(d), _addr(state, "state", f32, n["state"]), _addr(q, "q", tin, n["q"]),
+        _addr(k_t, "k_t", tin, n["k_t"]), _addr(v_t, "v_t", tin, n["v_t"]),
+        _addr(decay_t, "decay_t", f32, n["decay_t"]), _addr(beta_t, "beta_t", f32, n["beta_t"]),
+        _addr(y, "y", f32, n["y"]), _stream(stream)))

@@ -1,6 +1,6 @@
 """Build libsketchssm.so in-tree with hipcc for gfx950.
 
-    python -m sketched_recurrent_state_amd.build [-j JOBS] [--save-temps]
+    python sketched_recurrent_state_amd/build.py [-j JOBS] [--save-temps]
 
 Each HIP source compiles to its own object under ``_build/`` (in parallel),
 then hipcc links the shared library next to this file.
@@ -20,7 +20,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsketchssm.so")
-SOURCES = ["abi.hip", "update_refresh.hip", "decode.hip", "append.hip"]
+SOURCES = ["abi.hip", "update_refresh.hip", "decode.hip", "append.hip", "recurrent.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

@@ -290,4 +290,28 @@ ssm_status ssm_full_read_decode_step(const ssm_dims* d, const float* state, cons
                   fn);
 }
 
+ssm_status ssm_recurrent_decode_step(const ssm_dims* d, float* state, const void* q,
+                                     const void* k_t, const void* v_t, const float* decay_t,
+                                     const float* beta_t, float* y, void* stream) {
+  static const char* fn = "ssm_recurrent_decode_step";
+  ssm_status st = check_dims(d, fn);
+  if (st != SSM_OK) return st;
+  if (d->batch == 0) return ok();
+  if (state == nullptr) return fail(SSM_E_NULL, "%s: state is NULL", fn);
+  if (q == nullptr) return fail(SSM_E_NULL, "%s: q is NULL", fn);
+  if (y == nullptr) return fail(SSM_E_NULL, "%s: y is NULL", fn);
+  if (k_t == nullptr) return fail(SSM_E_NULL, "%s: k_t is NULL", fn);
+  if ((st = check_token(*d, k_t, v_t, decay_t, beta_t, fn)) != SSM_OK) return st;
+  const Sizes z = sizes_of(*d);
+  st = check_arrays(fn, {{state, z.state, true, "state"}, {q, z.qk, false, "q"},
+                         {k_t, z.qk, false, "k_t"}, {v_t, z.v, false, "v_t"},
+                         {decay_t, z.dtok, false, "decay_t"}, {beta_t, z.btok, false, "beta_t"},
+                         {y, z.y, true, "y"}});
+  if (st != SSM_OK) return st;
+  (void)hipGetLastError();
+  return launched(ssm::launch_recurrent_step(*d, state, q, k_t, v_t, decay_t, beta_t, y,
+                                             reinterpret_cast<hipStream_t>(stream)),
+                  fn);
+}
+
 }  // extern "C"

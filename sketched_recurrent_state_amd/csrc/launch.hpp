@@ -75,4 +75,8 @@ hipError_t launch_buffer_append(const ssm_dims& d, const void* k_t, const void* 
                                 void* v_buf, float* decay_buf, float* beta_buf, int slot,
                                 hipStream_t stream);
 
+hipError_t launch_recurrent_step(const ssm_dims& d, float* state, const void* q, const void* k_t,
+                                 const void* v_t, const float* decay_t, const float* beta_t,
+                                 float* y, hipStream_t stream);
+
 }  // namespace ssm

@@ -1,0 +1,97 @@
+// recurrent.hip -- the per-token recurrent decode step: the standard decode
+// of a linear-attention layer that SketchSSM's kernel speedups are measured
+// against (readsearch.ai listing of arXiv 2609.33051, Abstract: speedups over
+// the standard vLLM baseline; agihunt.info summary, "Background": every decode
+// step reads the full recurrent state). Each step applies the current token to
+// the full state, writes the state back and reads y = S^T q.
+//
+// Same state-tile layout as the windowed update: one workgroup per unit,
+// d_v/32 waves, 4 columns x d_k/8 rows per lane, d_k reductions over lane bits
+// 3..5 (DPP row_ror:8 and the gfx950 permlane swaps).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ssm {
+
+namespace {
+
+template <int RULE, int DK, int DV, typename TIN>
+__global__ void __launch_bounds__(2 * DV)
+recurrent_step_kernel(float* __restrict__ state, const TIN* __restrict__ q,
+                      const TIN* __restrict__ k_t, const TIN* __restrict__ v_t,
+                      const float* __restrict__ d_t, const float* __restrict__ b_t,
+                      float* __restrict__ y) {
+  constexpr int RPL = DK / 8;
+  const int unit = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cg = lane & 7, rg = lane >> 3;
+  const int col = wave * 32 + cg * 4;
+  const int row0 = rg * RPL;
+
+  float* Su = state + (size_t)unit * (DK * DV);
+  float4 s[RPL];
+#pragma unroll
+  for (int m = 0; m < RPL; ++m) s[m] = load_stream(Su + (size_t)(row0 + m) * DV + col);
+  float kr[RPL], qr[RPL], vv[4];
+  Vec<TIN, RPL>::load(k_t + (size_t)unit * DK + row0, kr);
+  Vec<TIN, RPL>::load(q + (size_t)unit * DK + row0, qr);
+  Vec<TIN, 4>::load(v_t + (size_t)unit * DV + col, vv);
+  const float4 v4 = make_float4(vv[0], vv[1], vv[2], vv[3]);
+
+  // S <- M S + b k v^T
+  if constexpr (RULE == MAMBA2) {
+    const float a = d_t[unit];
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) s[m] = fma4(kr[m], v4, scale4(a, s[m]));
+  } else if constexpr (RULE == GDN) {
+    const float a = d_t[unit], b = b_t[unit];
+    float4 p = f4(0.f);
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) p = fma4(kr[m], s[m], p);
+    p = tile_allreduce(p);  // S^T k
+    const float4 w = scale4(b, sub4(v4, scale4(a, p)));
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) s[m] = fma4(kr[m], w, scale4(a, s[m]));
+  } else {
+    float ar[RPL];
+    Vec<float, RPL>::load(d_t + (size_t)unit * DK + row0, ar);
+    const float b = b_t[unit];
+    float4 p = f4(0.f);
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) {
+      s[m] = scale4(ar[m], s[m]);
+      p = fma4(kr[m], s[m], p);
+    }
+    p = tile_allreduce(p);
+    const float4 w = scale4(b, sub4(v4, p));
+#pragma unroll
+    for (int m = 0; m < RPL; ++m) s[m] = fma4(kr[m], w, s[m]);
+  }
+#pragma unroll
+  for (int m = 0; m < RPL; ++m) store_stream(Su + (size_t)(row0 + m) * DV + col, s[m]);
+
+  // y = S^T q on the updated state
+  float4 out = f4(0.f);
+#pragma unroll
+  for (int m = 0; m < RPL; ++m) out = fma4(qr[m], s[m], out);
+  out = tile_allreduce(out);
+  if (rg == 0) *reinterpret_cast<float4*>(y + (size_t)unit * DV + col) = out;
+}
+
+}  // namespace
+
+hipError_t launch_recurrent_step(const ssm_dims& d, float* state, const void* q, const void* k_t,
+                                 const void* v_t, const float* decay_t, const float* beta_t,
+                                 float* y, hipStream_t stream) {
+  const unsigned units = (unsigned)d.batch * (unsigned)d.heads;
+  return dispatch(d.rule, d.in_dtype, d.d_k, d.d_v, [&](auto R, auto DK, auto DV, auto T) {
+    using TIN = typename decltype(T)::type;
+    constexpr int kR = decltype(R)::value, kDK = decltype(DK)::value, kDV = decltype(DV)::value;
+    hipLaunchKernelGGL((recurrent_step_kernel<kR, kDK, kDV, TIN>), dim3(units), dim3(2 * kDV), 0,
+                       stream, state, static_cast<const TIN*>(q), static_cast<const TIN*>(k_t),
+                       static_cast<const TIN*>(v_t), decay_t, beta_t, y);
+    return hipGetLastError();
+  });
+}
+
+}  // namespace ssm

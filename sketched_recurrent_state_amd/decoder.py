@@ -20,8 +20,8 @@ from typing import Optional
 
 import torch
 
-from . import (Dims, GDN, IN_BF16, KDA, MAMBA2, buffer_append, full_read_decode_step,
-               sketch_decode_step, window_update_refresh)
+from . import (Dims, IN_BF16, KDA, MAMBA2, buffer_append, full_read_decode_step,
+               recurrent_decode_step, sketch_decode_step, window_update_refresh)
 
 
 class WindowedDecoder:
@@ -102,3 +102,19 @@ class WindowedDecoder:
         if self.read == "both":
             return y, y_full
         return y if self.read == "sketch" else y_full
+
+
+class RecurrentDecoder:
+    """The per-token recurrent decode (the baseline SketchSSM is compared against):
+    every step writes the token into the full state and reads y = S^T q from it."""
+
+    def __init__(self, dims: Dims, state: torch.Tensor):
+        self.d = dims
+        self.state = state
+
+    def step(self, q, k, v, decay, beta=None, *, y=None):
+        d = self.d
+        if y is None:
+            y = torch.empty((d.batch, d.heads, d.d_v), device=q.device, dtype=torch.float32)
+        recurrent_decode_step(d, self.state, q, k, v, decay, beta, y)
+        return y

@@ -160,3 +160,35 @@ def compare(cfg, got, ref, *, y_tol=Y_TOL, s_tol=S_TOL) -> dict:
     assert e_S.max() <= s_tol, f"state: max rel err {e_S.max():.3e} > {s_tol}"
     assert e_Sk.max() <= s_tol, f"sketch: max rel err {e_Sk.max():.3e} > {s_tol}"
     return summary
+
+
+def run_gpu_recurrent(cfg: workloads.Config, inp: Inputs):
+    """The per-token recurrent decode: sampled outputs and states after every token."""
+    from sketched_recurrent_state_amd.decoder import RecurrentDecoder
+    d = dims_of(cfg)
+    U = cfg.units
+    idx = torch.as_tensor(inp.units, device=inp.S0.device)
+    state = inp.S0.clone()
+    dec = RecurrentDecoder(d, state)
+    y = torch.empty((cfg.batch, cfg.heads, cfg.d_v), device=state.device)
+    ys, Ss = [], [state.view(U, -1)[idx].cpu().numpy()]
+    for t in range(inp.steps):
+        dec.step(inp.q[t], inp.k[t], inp.v[t], inp.decay[t], inp.beta[t], y=y)
+        ys.append(y.view(U, -1)[idx].cpu().numpy())
+        Ss.append(state.view(U, -1)[idx].cpu().numpy())
+    torch.cuda.synchronize()
+    n = len(inp.units)
+    return dict(y=np.stack(ys).astype(np.float64),
+                S=np.stack(Ss).reshape(-1, n, cfg.d_k, cfg.d_v).astype(np.float64))
+
+
+def compare_recurrent(cfg, got, inp, *, y_tol=Y_TOL, s_tol=S_TOL) -> dict:
+    """Per-token path vs the oracle's exact read and its state after every token (W = 1)."""
+    ref = run_oracle(cfg.with_(window=1), inp)
+    e_y = rel_rows(got["y"], ref["y_exact"])
+    e_S = rel_mats(got["S"], ref["S_win"])
+    summary = dict(config=cfg.name, y_max=float(e_y.max()), S_max=float(e_S.max()))
+    note(f"recurrent parity {summary}")
+    assert e_y.max() <= y_tol, f"recurrent read: max rel err {e_y.max():.3e}"
+    assert e_S.max() <= s_tol, f"recurrent state: max rel err {e_S.max():.3e}"
+    return summary

@@ -224,3 +224,17 @@ def test_one_hip_runtime_in_the_process():
     hsa = {os.path.realpath(l.split()[-1]) for l in maps if "libhsa-runtime64" in l}
     assert len(hip) == 1, hip
     assert len(hsa) <= 1, hsa
+
+
+def test_recurrent_step_validation():
+    p = addrs(8)
+    d = dims()
+    st, msg = status_of(ssm.recurrent_decode_step, d, None, *p[1:7])
+    assert st == 1 and "state" in msg
+    st, msg = status_of(ssm.recurrent_decode_step, d, p[0], p[1], None, p[3], p[4], p[5], p[6])
+    assert st == 1 and "k_t" in msg
+    st, msg = status_of(ssm.recurrent_decode_step, dims(rule="mamba2"), *p[:7])
+    assert st == 4 and "Mamba-2" in msg
+    st, msg = status_of(ssm.recurrent_decode_step, d, p[0], p[1], p[2], p[3], p[4], p[5], p[0] + 64)
+    assert st == 5 and "overlaps" in msg
+    assert status_of(ssm.recurrent_decode_step, dims(batch=0), *([None] * 7))[0] == 0

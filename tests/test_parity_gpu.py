@@ -193,3 +193,23 @@ def test_empty_batch_on_device():
     ssm.window_update_refresh(d, z, z, torch.zeros(4 * 8 * 128, device="cuda"), None, None, None,
                               None, 0)
     torch.cuda.synchronize()
+
+
+RECURRENT = [small("mamba2"), small("gdn"), small("kda"), small("gdn", "f32", d_k=64, d_v=32),
+             small("kda", d_k=16, d_v=128), small("mamba2", "f32", d_k=32, d_v=64)]
+
+
+@pytest.mark.parametrize("cfg", RECURRENT, ids=lambda c: c.name)
+def test_recurrent_step_small(cfg):
+    """The per-token baseline: exact read of the state after each token, state written each step."""
+    H.note(f"case recurrent {cfg.name}")
+    inp = H.Inputs(cfg, np.arange(cfg.units), cfg.steps)
+    H.compare_recurrent(cfg, H.run_gpu_recurrent(cfg, inp), inp)
+
+
+@pytest.mark.parametrize("name", ["c3", "c4"])
+def test_recurrent_step_workload_sampled(name):
+    cfg = workloads.get(name).with_(steps=24)
+    H.note(f"case recurrent {name} (sampled units, 24 steps)")
+    inp = H.Inputs(cfg, workloads.sample_units(cfg, 24), cfg.steps)
+    H.compare_recurrent(cfg, H.run_gpu_recurrent(cfg, inp), inp)
