@@ -89,6 +89,8 @@ def main() -> int:
     ap.add_argument("--cpu-steps", type=int, default=16, help="oracle sample: decode steps")
     ap.add_argument("--only", choices=["sketch", "full", "update"], default=None,
                     help="profiling: run only this leg's launches")
+    ap.add_argument("--per-head-ranks", choices=["avg8"], default=None,
+                    help="per-head sketch ranks (avg8: 2, 4, 8, 18 cycled over heads, mean 8)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="profiling: copy MIB MiB with a plain device copy kernel, then exit")
     a = ap.parse_args()
@@ -141,7 +143,14 @@ def main() -> int:
         S0 = np.concatenate(list(ex.map(lambda n: workloads.initial_state(cfg, [n]), range(cfg.batch))))
         steps_host = list(ex.map(lambda t: workloads.step_inputs(cfg, t), range(total)))
     S0_dev = to_dev(S0)
-    basis = to_dev(workloads.basis(cfg))
+    ranks = workloads.average_rank_8(cfg.heads) if a.per_head_ranks == "avg8" else None
+    if ranks is not None:
+        basis = to_dev(workloads.basis_ranked(cfg, ranks))
+        offsets = ssm.rank_offsets(ranks)
+        d_r = ssm.Dims.make(cfg.rule, cfg.in_dtype, cfg.batch, cfg.heads, cfg.d_k, cfg.d_v, W,
+                            max(ranks))
+    else:
+        basis = to_dev(workloads.basis(cfg))
     inputs = [(to_dev(s.q), to_dev(s.k), to_dev(s.v), to_dev(s.decay), to_dev(s.beta))
               for s in steps_host]
     gen_s = time.time() - t0
@@ -161,14 +170,21 @@ def main() -> int:
     kb, vb, db, bb = (P(x) for x in bufs)
     yp, bp = P(y), P(basis)
 
+    if ranks is None:
+        sketch_step = lambda *x, **kw: ssm.sketch_decode_step(d, *x, **kw)
+        update_refresh = lambda *x, **kw: ssm.window_update_refresh(d, *x, **kw)
+    else:
+        sketch_step = lambda *x, **kw: ssm.sketch_decode_step_ranked(d_r, offsets, *x, **kw)
+        update_refresh = lambda *x, **kw: ssm.window_update_refresh_ranked(d_r, offsets, *x, **kw)
+
     def run_sketch(state_p, sketch_p, t_lo, t_hi, sp, upd_events=None, only=None):
         """Sketch path: fused append + sketch read per step, update + refresh per window."""
         for t in range(t_lo, t_hi):
             q, k, v, dc, b = ptrs[t]
             tau = t % W + 1
             if only in (None, "sketch"):
-                ssm.sketch_decode_step(d, sketch_p, bp, q, kb, vb, db, bb, tau, yp, k_t=k, v_t=v,
-                                       decay_t=dc, beta_t=b, stream=sp)
+                sketch_step(sketch_p, bp, q, kb, vb, db, bb, tau, yp, k_t=k, v_t=v,
+                            decay_t=dc, beta_t=b, stream=sp)
             elif only == "update":  # keep the buffer fed without the read
                 ssm.buffer_append(d, k, v, dc, b, kb, vb, db, bb, tau - 1, stream=sp)
             if tau == W and only in (None, "update"):
@@ -176,7 +192,7 @@ def main() -> int:
                     upd_events.append((torch.cuda.Event(enable_timing=True),
                                        torch.cuda.Event(enable_timing=True)))
                     upd_events[-1][0].record(stream)
-                ssm.window_update_refresh(d, state_p, sketch_p, bp, kb, vb, db, bb, W, stream=sp)
+                update_refresh(state_p, sketch_p, bp, kb, vb, db, bb, W, stream=sp)
                 if upd_events is not None:
                     upd_events[-1][1].record(stream)
 
@@ -224,9 +240,10 @@ def main() -> int:
 
     # ---- the sketch path, eager launches (update kernel timed by HIP events) ---------
     state = S0_dev.clone()
-    sketch = torch.empty((cfg.batch, cfg.heads, cfg.rank, cfg.d_v), device=dev)
+    sk_rows = cfg.heads * cfg.rank if ranks is None else sum(ranks)
+    sketch = torch.empty((cfg.batch, sk_rows, cfg.d_v), device=dev)
     st_p, sk_p = P(state), P(sketch)
-    ssm.window_update_refresh(d, st_p, sk_p, bp, None, None, None, None, 0, stream=sp)
+    update_refresh(st_p, sk_p, bp, None, None, None, None, 0, stream=sp)
     run_sketch(st_p, sk_p, 0, a.warmup, sp, only=a.only)
     upd_ev = []
     eager_s = timed(lambda: run_sketch(st_p, sk_p, a.warmup, total, sp, upd_ev, only=a.only))
@@ -255,8 +272,8 @@ def main() -> int:
 
     tau_mid = W // 2 + 1
     q0 = ptrs[0][0]
-    sketch_ms = kernel_time(lambda i: ssm.sketch_decode_step(d, sk_p, bp, q0, kb, vb, db, bb,
-                                                             tau_mid, yp, stream=sp), 20)
+    sketch_ms = kernel_time(lambda i: sketch_step(sk_p, bp, q0, kb, vb, db, bb, tau_mid, yp,
+                                                  stream=sp), 20)
     full_ms = kernel_time(lambda i: ssm.full_read_decode_step(d, st_p, q0, kb, vb, db, bb,
                                                               tau_mid, yp, stream=sp), 10)
 
@@ -303,20 +320,20 @@ def main() -> int:
     # ---- approximation error of the sketch read vs the exact read (untimed) -----------
     st_a = S0_dev.clone()
     sk_a = torch.empty_like(sketch)
-    ssm.window_update_refresh(d, st_a, sk_a, basis, None, None, None, None, 0, stream=stream)
+    update_refresh(st_a, sk_a, basis, None, None, None, None, 0, stream=stream)
     errs = []
     y_f = torch.empty_like(y)
     for t in range(2 * W):
         q, k, v, dc, b = inputs[t]
         tau = t % W + 1
-        ssm.sketch_decode_step(d, sk_a, basis, q, *bufs, tau, y, k_t=k, v_t=v, decay_t=dc, beta_t=b,
+        sketch_step(sk_a, basis, q, *bufs, tau, y, k_t=k, v_t=v, decay_t=dc, beta_t=b,
                                stream=stream)
         ssm.full_read_decode_step(d, st_a, q, *bufs, tau, y_f, stream=stream)
         num = (y - y_f).view(U, -1).norm(dim=1)
         den = y_f.view(U, -1).norm(dim=1)
         errs.append((num / den.clamp_min(1e-30)).cpu())
         if tau == W:
-            ssm.window_update_refresh(d, st_a, sk_a, basis, *bufs, W, stream=stream)
+            update_refresh(st_a, sk_a, basis, *bufs, W, stream=stream)
     e = torch.cat(errs).double().numpy()
     approx = {"mean": float(e.mean()), "p50": float(np.median(e)), "p99": float(np.quantile(e, 0.99)),
               "max": float(e.max()), "steps": 2 * W}
@@ -387,7 +404,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": cfg.description, "rule": cfg.rule, "batch": cfg.batch,
                    "heads": cfg.heads, "d_k": cfg.d_k, "d_v": cfg.d_v, "window": W,
-                   "rank": cfg.rank, "inputs": cfg.in_dtype, "state": "f32"},
+                   "rank": cfg.rank if ranks is None else f"per head {sorted(set(ranks))}, mean "
+                   f"{sum(ranks) / len(ranks):g}", "inputs": cfg.in_dtype, "state": "f32"},
         "roofline": {"bound": "hbm", "kernel": "update_refresh_kernel", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "bytes_per_launch": upd_bytes,

@@ -171,6 +171,32 @@ ssm_status ssm_full_read_decode_step(const ssm_dims* d,
                                      int32_t tau, float* y, void* stream);
 
 /*
+ * Heterogeneous sketch ranks per head (the pages report an average sketch rank
+ * of 8: agihunt.info "Results"), for ssm_window_update_refresh_ranked and
+ * ssm_sketch_decode_step_ranked. rank_offsets is a HOST array of H + 1 int32
+ * prefix offsets: head h has rank r_h = rank_offsets[h+1] - rank_offsets[h],
+ * 1 <= r_h <= min(d_k, 32), rank_offsets[0] = 0, H <= 256; the array is read
+ * during the call only. With R = rank_offsets[H]:
+ *   basis   fp32 [R][d_k]       rows rank_offsets[h] .. +r_h are head h's basis
+ *   sketch  fp32 [N][R][d_v]    rows rank_offsets[h] .. +r_h of sequence n are
+ *                               the outputs of head h's basis vectors
+ * d->rank must still be a valid rank (the table decides the sizes). Every other
+ * argument and behaviour is that of the uniform-rank entry point.
+ */
+ssm_status ssm_window_update_refresh_ranked(const ssm_dims* d, const int32_t* rank_offsets,
+                                            float* state, float* sketch, const float* basis,
+                                            const void* k_buf, const void* v_buf,
+                                            const float* decay_buf, const float* beta_buf,
+                                            int32_t n_tokens, void* stream);
+
+ssm_status ssm_sketch_decode_step_ranked(const ssm_dims* d, const int32_t* rank_offsets,
+                                         const float* sketch, const float* basis, const void* q,
+                                         const void* k_t, const void* v_t,
+                                         const float* decay_t, const float* beta_t,
+                                         void* k_buf, void* v_buf, float* decay_buf,
+                                         float* beta_buf, int32_t tau, float* y, void* stream);
+
+/*
  * Per-token recurrent decode step (the standard decode SketchSSM is compared
  * against: readsearch.ai listing, Abstract, kernel speedups over the standard
  * vLLM baseline; agihunt.info "Confirmed", background bullet: every step reads

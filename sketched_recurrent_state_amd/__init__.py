@@ -20,7 +20,8 @@ from typing import Optional, Union
 __all__ = [
     "Dims", "SSMError", "MAMBA2", "GDN", "KDA", "IN_BF16", "IN_F32", "RULES",
     "abi_version", "buffer_append", "window_update_refresh", "sketch_decode_step",
-    "full_read_decode_step", "recurrent_decode_step", "LIB_PATH", "HEADER", "declared_symbols",
+    "full_read_decode_step", "recurrent_decode_step", "window_update_refresh_ranked",
+    "sketch_decode_step_ranked", "rank_offsets", "LIB_PATH", "HEADER", "declared_symbols",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -82,6 +83,11 @@ def _load():
     lib.ssm_window_update_refresh.argtypes = [dp] + [vp] * 7 + [i32, vp]
     lib.ssm_sketch_decode_step.restype = i32
     lib.ssm_sketch_decode_step.argtypes = [dp] + [vp] * 11 + [i32, vp, vp]
+    ip = ctypes.POINTER(ctypes.c_int32)
+    lib.ssm_window_update_refresh_ranked.restype = i32
+    lib.ssm_window_update_refresh_ranked.argtypes = [dp, ip] + [vp] * 7 + [i32, vp]
+    lib.ssm_sketch_decode_step_ranked.restype = i32
+    lib.ssm_sketch_decode_step_ranked.argtypes = [dp, ip] + [vp] * 11 + [i32, vp, vp]
     lib.ssm_recurrent_decode_step.restype = i32
     lib.ssm_recurrent_decode_step.argtypes = [dp] + [vp] * 7 + [vp]
     lib.ssm_full_read_decode_step.restype = i32
@@ -262,3 +268,73 @@ def recurrent_decode_step(d: Dims, state, q, k_t, v_t, decay_t, beta_t, y, strea
         _addr(k_t, "k_t", tin, n["k_t"]), _addr(v_t, "v_t", tin, n["v_t"]),
         _addr(decay_t, "decay_t", f32, n["decay_t"]), _addr(beta_t, "beta_t", f32, n["beta_t"]),
         _addr(y, "y", f32, n["y"]), _stream(stream)))
+
+
+# ----------------------------------------------------------------------------
+# heterogeneous per-head sketch ranks
+# ----------------------------------------------------------------------------
+def rank_offsets(ranks) -> "ctypes.Array":
+    """Host int32 prefix offsets (H + 1 values) for per-head ranks."""
+    off = [0]
+    for r in ranks:
+        off.append(off[-1] + int(r))
+    return (ctypes.c_int32 * len(off))(*off)
+
+
+def _ranked_numel(d: Dims, offsets) -> dict:
+    n = numel(d)
+    R = int(offsets[d.heads]) if len(offsets) > d.heads else 0
+    n["sketch"] = d.batch * R * d.d_v
+    n["basis"] = R * d.d_k
+    return n
+
+
+def _offsets_arg(d: Dims, offsets):
+    if not isinstance(offsets, ctypes.Array):
+        offsets = rank_offsets(offsets) if len(offsets) == d.heads else \
+            (ctypes.c_int32 * len(offsets))(*[int(x) for x in offsets])
+    if len(offsets) != d.heads + 1:
+        raise ValueError(f"rank_offsets: {len(offsets)} entries, need heads + 1 = {d.heads + 1}")
+    return offsets
+
+
+def window_update_refresh_ranked(d: Dims, offsets, state, sketch, basis, k_buf, v_buf,
+                                 decay_buf, beta_buf, n_tokens: int, stream=None) -> None:
+    """ssm_window_update_refresh_ranked. `offsets`: H + 1 prefix offsets, or H per-head ranks."""
+    off = _offsets_arg(d, offsets)
+    if isinstance(stream, int) and _all_raw((state, sketch, basis, k_buf, v_buf, decay_buf,
+                                             beta_buf)):
+        return _check(_lib.ssm_window_update_refresh_ranked(
+            ctypes.byref(d), off, state, sketch, basis, k_buf, v_buf, decay_buf, beta_buf,
+            n_tokens, stream))
+    tin, f32 = _types(d, (state, sketch, basis, k_buf, v_buf, decay_buf, beta_buf))
+    n = _ranked_numel(d, off)
+    _check(_lib.ssm_window_update_refresh_ranked(
+        ctypes.byref(d), off, _addr(state, "state", f32, n["state"]),
+        _addr(sketch, "sketch", f32, n["sketch"]), _addr(basis, "basis", f32, n["basis"]),
+        _addr(k_buf, "k_buf", tin, n["k_buf"]), _addr(v_buf, "v_buf", tin, n["v_buf"]),
+        _addr(decay_buf, "decay_buf", f32, n["decay_buf"]),
+        _addr(beta_buf, "beta_buf", f32, n["beta_buf"]), int(n_tokens), _stream(stream)))
+
+
+def sketch_decode_step_ranked(d: Dims, offsets, sketch, basis, q, k_buf, v_buf, decay_buf,
+                              beta_buf, tau: int, y, *, k_t=None, v_t=None, decay_t=None,
+                              beta_t=None, stream=None) -> None:
+    """ssm_sketch_decode_step_ranked. `offsets`: H + 1 prefix offsets, or H per-head ranks."""
+    off = _offsets_arg(d, offsets)
+    if isinstance(stream, int) and _all_raw((sketch, basis, q, k_buf, v_buf, decay_buf, beta_buf,
+                                             y, k_t, v_t, decay_t, beta_t)):
+        return _check(_lib.ssm_sketch_decode_step_ranked(
+            ctypes.byref(d), off, sketch, basis, q, k_t, v_t, decay_t, beta_t, k_buf, v_buf,
+            decay_buf, beta_buf, tau, y, stream))
+    tin, f32 = _types(d, (sketch, basis, q, k_buf, v_buf, decay_buf, beta_buf, y, k_t, v_t))
+    n = _ranked_numel(d, off)
+    _check(_lib.ssm_sketch_decode_step_ranked(
+        ctypes.byref(d), off, _addr(sketch, "sketch", f32, n["sketch"]),
+        _addr(basis, "basis", f32, n["basis"]), _addr(q, "q", tin, n["q"]),
+        _addr(k_t, "k_t", tin, n["k_t"]), _addr(v_t, "v_t", tin, n["v_t"]),
+        _addr(decay_t, "decay_t", f32, n["decay_t"]), _addr(beta_t, "beta_t", f32, n["beta_t"]),
+        _addr(k_buf, "k_buf", tin, n["k_buf"]), _addr(v_buf, "v_buf", tin, n["v_buf"]),
+        _addr(decay_buf, "decay_buf", f32, n["decay_buf"]),
+        _addr(beta_buf, "beta_buf", f32, n["beta_buf"]), int(tau), _addr(y, "y", f32, n["y"]),
+        _stream(stream)))

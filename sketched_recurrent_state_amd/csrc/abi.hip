@@ -140,6 +140,30 @@ ssm_status check_buffers(const ssm_dims& d, const void* k_buf, const void* v_buf
   return check_beta(d, beta_buf, "beta_buf", fn);
 }
 
+// Per-head rank table (host array of heads + 1 prefix offsets).
+ssm_status check_rank_offsets(const ssm_dims& d, const int32_t* off, const char* fn) {
+  if (off == nullptr) return fail(SSM_E_NULL, "%s: rank_offsets is NULL", fn);
+  if (d.heads > ssm::kMaxRankedHeads)
+    return fail(SSM_E_SHAPE, "%s: %d heads > %d supported with per-head ranks", fn, d.heads,
+                ssm::kMaxRankedHeads);
+  if (off[0] != 0) return fail(SSM_E_RANGE, "%s: rank_offsets[0] = %d, not 0", fn, off[0]);
+  const int rmax = d.d_k < 32 ? d.d_k : 32;
+  for (int h = 0; h < d.heads; ++h) {
+    const long long r = (long long)off[h + 1] - off[h];
+    if (r < 1 || r > rmax)
+      return fail(SSM_E_RANGE, "%s: head %d has rank %lld, not in [1, %d]", fn, h, r, rmax);
+  }
+  return SSM_OK;
+}
+
+// Sketch and basis bytes for a per-head rank table (or the uniform rank when off is NULL).
+void apply_ranks(const ssm_dims& d, const int32_t* off, Sizes& z) {
+  if (off == nullptr) return;
+  const size_t R = (size_t)off[d.heads];
+  z.sketch = z.units / (size_t)d.heads * R * d.d_v * 4;
+  z.basis = R * d.d_k * 4;
+}
+
 ssm_status launched(hipError_t e, const char* fn) {
   if (e != hipSuccess) return fail(SSM_E_LAUNCH, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
@@ -192,13 +216,13 @@ ssm_status ssm_buffer_append(const ssm_dims* d, const void* k_t, const void* v_t
                   fn);
 }
 
-ssm_status ssm_window_update_refresh(const ssm_dims* d, float* state, float* sketch,
-                                     const float* basis, const void* k_buf, const void* v_buf,
-                                     const float* decay_buf, const float* beta_buf,
-                                     int32_t n_tokens, void* stream) {
-  static const char* fn = "ssm_window_update_refresh";
+static ssm_status update_refresh_impl(const char* fn, const ssm_dims* d, const int32_t* rank_offsets,
+                               float* state, float* sketch, const float* basis, const void* k_buf,
+                               const void* v_buf, const float* decay_buf, const float* beta_buf,
+                               int32_t n_tokens, void* stream, bool ranked) {
   ssm_status st = check_dims(d, fn);
   if (st != SSM_OK) return st;
+  if (ranked && (st = check_rank_offsets(*d, rank_offsets, fn)) != SSM_OK) return st;
   if (n_tokens < 0 || n_tokens > d->window)
     return fail(SSM_E_RANGE, "%s: n_tokens %d not in [0, %d]", fn, n_tokens, d->window);
   if (d->batch == 0) return ok();
@@ -209,7 +233,8 @@ ssm_status ssm_window_update_refresh(const ssm_dims* d, float* state, float* ske
     if ((st = check_buffers(*d, k_buf, v_buf, decay_buf, beta_buf, fn)) != SSM_OK) return st;
   }
   if (n_tokens == 0 && sketch == nullptr) return ok();  // nothing to apply, nothing to store
-  const Sizes z = sizes_of(*d);
+  Sizes z = sizes_of(*d);
+  apply_ranks(*d, rank_offsets, z);
   const bool tok = n_tokens > 0;
   st = check_arrays(fn, {{state, z.state, true, "state"}, {sketch, z.sketch, true, "sketch"},
                          {basis, z.basis, false, "basis"},
@@ -219,20 +244,20 @@ ssm_status ssm_window_update_refresh(const ssm_dims* d, float* state, float* ske
                          {tok ? beta_buf : nullptr, z.bbuf, false, "beta_buf"}});
   if (st != SSM_OK) return st;
   (void)hipGetLastError();
-  return launched(ssm::launch_update_refresh(*d, state, sketch, basis, k_buf, v_buf, decay_buf,
+  return launched(ssm::launch_update_refresh(*d, rank_offsets, state, sketch, basis, k_buf, v_buf, decay_buf,
                                              beta_buf, n_tokens,
                                              reinterpret_cast<hipStream_t>(stream)),
                   fn);
 }
 
-ssm_status ssm_sketch_decode_step(const ssm_dims* d, const float* sketch, const float* basis,
-                                  const void* q, const void* k_t, const void* v_t,
-                                  const float* decay_t, const float* beta_t, void* k_buf,
-                                  void* v_buf, float* decay_buf, float* beta_buf, int32_t tau,
-                                  float* y, void* stream) {
-  static const char* fn = "ssm_sketch_decode_step";
+static ssm_status sketch_decode_impl(const char* fn, const ssm_dims* d, const int32_t* rank_offsets,
+                              const float* sketch, const float* basis, const void* q,
+                              const void* k_t, const void* v_t, const float* decay_t,
+                              const float* beta_t, void* k_buf, void* v_buf, float* decay_buf,
+                              float* beta_buf, int32_t tau, float* y, void* stream, bool ranked) {
   ssm_status st = check_dims(d, fn);
   if (st != SSM_OK) return st;
+  if (ranked && (st = check_rank_offsets(*d, rank_offsets, fn)) != SSM_OK) return st;
   if (tau < 1 || tau > d->window)
     return fail(SSM_E_RANGE, "%s: tau %d not in [1, %d]", fn, tau, d->window);
   if (d->batch == 0) return ok();
@@ -242,7 +267,8 @@ ssm_status ssm_sketch_decode_step(const ssm_dims* d, const float* sketch, const 
   if (y == nullptr) return fail(SSM_E_NULL, "%s: y is NULL", fn);
   if ((st = check_token(*d, k_t, v_t, decay_t, beta_t, fn)) != SSM_OK) return st;
   if ((st = check_buffers(*d, k_buf, v_buf, decay_buf, beta_buf, fn)) != SSM_OK) return st;
-  const Sizes z = sizes_of(*d);
+  Sizes z = sizes_of(*d);
+  apply_ranks(*d, rank_offsets, z);
   const bool fused = k_t != nullptr;
   st = check_arrays(fn, {{sketch, z.sketch, false, "sketch"}, {basis, z.basis, false, "basis"},
                          {q, z.qk, false, "q"}, {k_t, z.qk, false, "k_t"}, {v_t, z.v, false, "v_t"},
@@ -252,7 +278,7 @@ ssm_status ssm_sketch_decode_step(const ssm_dims* d, const float* sketch, const 
                          {beta_buf, z.bbuf, fused, "beta_buf"}, {y, z.y, true, "y"}});
   if (st != SSM_OK) return st;
   (void)hipGetLastError();
-  return launched(ssm::launch_sketch_decode(*d, sketch, basis, q, k_t, v_t, decay_t, beta_t,
+  return launched(ssm::launch_sketch_decode(*d, rank_offsets, sketch, basis, q, k_t, v_t, decay_t, beta_t,
                                             k_buf, v_buf, decay_buf, beta_buf, tau, y,
                                             reinterpret_cast<hipStream_t>(stream)),
                   fn);
@@ -312,6 +338,44 @@ ssm_status ssm_recurrent_decode_step(const ssm_dims* d, float* state, const void
   return launched(ssm::launch_recurrent_step(*d, state, q, k_t, v_t, decay_t, beta_t, y,
                                              reinterpret_cast<hipStream_t>(stream)),
                   fn);
+}
+
+ssm_status ssm_window_update_refresh(const ssm_dims* d, float* state, float* sketch,
+                                     const float* basis, const void* k_buf, const void* v_buf,
+                                     const float* decay_buf, const float* beta_buf,
+                                     int32_t n_tokens, void* stream) {
+  return update_refresh_impl("ssm_window_update_refresh", d, nullptr, state, sketch, basis, k_buf,
+                             v_buf, decay_buf, beta_buf, n_tokens, stream, false);
+}
+
+ssm_status ssm_window_update_refresh_ranked(const ssm_dims* d, const int32_t* rank_offsets,
+                                            float* state, float* sketch, const float* basis,
+                                            const void* k_buf, const void* v_buf,
+                                            const float* decay_buf, const float* beta_buf,
+                                            int32_t n_tokens, void* stream) {
+  return update_refresh_impl("ssm_window_update_refresh_ranked", d, rank_offsets, state, sketch,
+                             basis, k_buf, v_buf, decay_buf, beta_buf, n_tokens, stream, true);
+}
+
+ssm_status ssm_sketch_decode_step(const ssm_dims* d, const float* sketch, const float* basis,
+                                  const void* q, const void* k_t, const void* v_t,
+                                  const float* decay_t, const float* beta_t, void* k_buf,
+                                  void* v_buf, float* decay_buf, float* beta_buf, int32_t tau,
+                                  float* y, void* stream) {
+  return sketch_decode_impl("ssm_sketch_decode_step", d, nullptr, sketch, basis, q, k_t, v_t,
+                            decay_t, beta_t, k_buf, v_buf, decay_buf, beta_buf, tau, y, stream,
+                            false);
+}
+
+ssm_status ssm_sketch_decode_step_ranked(const ssm_dims* d, const int32_t* rank_offsets,
+                                         const float* sketch, const float* basis, const void* q,
+                                         const void* k_t, const void* v_t, const float* decay_t,
+                                         const float* beta_t, void* k_buf, void* v_buf,
+                                         float* decay_buf, float* beta_buf, int32_t tau, float* y,
+                                         void* stream) {
+  return sketch_decode_impl("ssm_sketch_decode_step_ranked", d, rank_offsets, sketch, basis, q,
+                            k_t, v_t, decay_t, beta_t, k_buf, v_buf, decay_buf, beta_buf, tau, y,
+                            stream, true);
 }
 
 }  // extern "C"

@@ -279,6 +279,27 @@ __device__ __forceinline__ float4 fma4(float a, float4 b, float4 c) {
 }
 
 // ---------------------------------------------------------------------------
+// sketch rank per head. Basis rows of head h: [offset(h), offset(h) + rank(h));
+// the sketch of sequence n holds total() rows, head h's at the same offsets.
+// ---------------------------------------------------------------------------
+struct UniformRank {  // every head has rank r
+  int r, heads;
+  __device__ __forceinline__ int rank(int) const { return r; }
+  __device__ __forceinline__ int offset(int h) const { return h * r; }
+  __device__ __forceinline__ int total() const { return heads * r; }
+};
+
+constexpr int kMaxRankedHeads = 256;
+
+struct RankTable {  // per-head ranks: off[h + 1] - off[h], off[0] = 0 (checked on the host)
+  int heads;
+  int off[kMaxRankedHeads + 1];
+  __device__ __forceinline__ int rank(int h) const { return off[h + 1] - off[h]; }
+  __device__ __forceinline__ int offset(int h) const { return off[h]; }
+  __device__ __forceinline__ int total() const { return off[heads]; }
+};
+
+// ---------------------------------------------------------------------------
 // window staging: the first n buffered tokens of one unit -> LDS as fp32
 // ---------------------------------------------------------------------------
 __host__ __device__ inline int pad4(int x) { return (x + 3) & ~3; }

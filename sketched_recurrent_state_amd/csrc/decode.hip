@@ -48,14 +48,15 @@ __device__ __forceinline__ void carry_back(float* u, const float* kk, const floa
 template <int DK>
 constexpr int sketch_group() { return DK >= 32 ? 32 : 16; }
 
-template <int RULE, int DK, int DV, typename TIN, int WMAX>
+template <int RULE, int DK, int DV, typename TIN, int WMAX, typename RT>
 __global__ void __launch_bounds__(256)
 sketch_decode_kernel(const float* __restrict__ sketch, const float* __restrict__ basis,
                      const TIN* __restrict__ q, const TIN* __restrict__ k_t,
                      const TIN* __restrict__ v_t, const float* __restrict__ d_t,
                      const float* __restrict__ b_t, TIN* __restrict__ kbuf,
                      TIN* __restrict__ vbuf, float* __restrict__ dbuf, float* __restrict__ bbuf,
-                     float* __restrict__ y, int batch, int heads, int window, int rank, int tau) {
+                     float* __restrict__ y, int batch, int heads, int window, const RT rt,
+                     int tau) {
   constexpr int G = sketch_group<DK>();
   static_assert(WMAX <= G, "one gate per lane");
   constexpr int UPB = 256 / G;                // sequences per workgroup
@@ -66,6 +67,7 @@ sketch_decode_kernel(const float* __restrict__ sketch, const float* __restrict__
   float* lB = reinterpret_cast<float*>(lds4);  // [rank][DK]
 
   const int head = blockIdx.x % heads;
+  const int rank = rt.rank(head);
   const int seq = (blockIdx.x / heads) * UPB + threadIdx.x / G;
   const int sub = threadIdx.x % G;
   const bool active = seq < batch;            // whole G-lane groups
@@ -79,7 +81,7 @@ sketch_decode_kernel(const float* __restrict__ sketch, const float* __restrict__
   float ak[(RULE == KDA) ? WMAX : 1][EK];     // KDA: per-channel gates of each token
   float a_lane = 1.f, b_lane = 1.f;           // scalar gates of token `sub`
   float sk[RCH][EV];
-  const float* Sku = sketch + unit * rank * DV + sub * EV;
+  const float* Sku = sketch + ((size_t)seq * rt.total() + rt.offset(head)) * DV + sub * EV;
   if (active) {
     qr.load(q + unit * DK + sub * EK);
 #pragma unroll
@@ -103,7 +105,7 @@ sketch_decode_kernel(const float* __restrict__ sketch, const float* __restrict__
       if (m < rank) Vec<float, EV>::load(Sku + (size_t)m * DV, sk[m]);
   }
   {
-    const float* Bh = basis + (size_t)head * rank * DK;
+    const float* Bh = basis + (size_t)rt.offset(head) * DK;
     for (int e = threadIdx.x * 4; e < rank * DK; e += 256 * 4)
       *reinterpret_cast<float4*>(lB + e) = *reinterpret_cast<const float4*>(Bh + e);
   }
@@ -263,28 +265,35 @@ full_read_kernel(const float* __restrict__ state, const TIN* __restrict__ q,
 
 }  // namespace
 
-hipError_t launch_sketch_decode(const ssm_dims& d, const float* sketch, const float* basis,
-                                const void* q, const void* k_t, const void* v_t,
-                                const float* decay_t, const float* beta_t, void* k_buf,
-                                void* v_buf, float* decay_buf, float* beta_buf, int tau, float* y,
-                                hipStream_t stream) {
+hipError_t launch_sketch_decode(const ssm_dims& d, const int32_t* rank_offsets,
+                                const float* sketch, const float* basis, const void* q,
+                                const void* k_t, const void* v_t, const float* decay_t,
+                                const float* beta_t, void* k_buf, void* v_buf, float* decay_buf,
+                                float* beta_buf, int tau, float* y, hipStream_t stream) {
+  const int max_rank = rank_offsets ? max_rank_of(rank_offsets, d.heads) : d.rank;
   return dispatch(d.rule, d.in_dtype, d.d_k, d.d_v, [&](auto R, auto DK, auto DV, auto T) {
     using TIN = typename decltype(T)::type;
     constexpr int kR = decltype(R)::value, kDK = decltype(DK)::value, kDV = decltype(DV)::value;
     constexpr unsigned UPB = 256u / sketch_group<kDK>();
     const unsigned blocks = (unsigned)d.heads * (((unsigned)d.batch + UPB - 1) / UPB);
-    const size_t lds = (size_t)d.rank * kDK * sizeof(float);
-    auto go = [&](auto kernel) {
-      hipLaunchKernelGGL(kernel, dim3(blocks), dim3(256), lds, stream, sketch, basis,
+    const size_t lds = (size_t)max_rank * kDK * sizeof(float);
+    auto go = [&](auto wmax, auto rt) {
+      constexpr int kW = decltype(wmax)::value;
+      hipLaunchKernelGGL((sketch_decode_kernel<kR, kDK, kDV, TIN, kW, decltype(rt)>),
+                         dim3(blocks), dim3(256), lds, stream, sketch, basis,
                          static_cast<const TIN*>(q), static_cast<const TIN*>(k_t),
                          static_cast<const TIN*>(v_t), decay_t, beta_t, static_cast<TIN*>(k_buf),
                          static_cast<TIN*>(v_buf), decay_buf, beta_buf, y, d.batch, d.heads,
-                         d.window, d.rank, tau);
+                         d.window, rt, tau);
       return hipGetLastError();
     };
-    if (d.window <= 4) return go(sketch_decode_kernel<kR, kDK, kDV, TIN, 4>);
-    if (d.window <= 8) return go(sketch_decode_kernel<kR, kDK, kDV, TIN, 8>);
-    return go(sketch_decode_kernel<kR, kDK, kDV, TIN, 16>);
+    auto with_rank = [&](auto wmax) {
+      if (rank_offsets == nullptr) return go(wmax, UniformRank{d.rank, d.heads});
+      return go(wmax, make_rank_table(rank_offsets, d.heads));
+    };
+    if (d.window <= 4) return with_rank(std::integral_constant<int, 4>{});
+    if (d.window <= 8) return with_rank(std::integral_constant<int, 8>{});
+    return with_rank(std::integral_constant<int, 16>{});
   });
 }
 

@@ -7,9 +7,17 @@
 
 #include <type_traits>
 
+#include "common.hpp"
 #include "sketchssm.h"
 
 namespace ssm {
+
+inline RankTable make_rank_table(const int32_t* rank_offsets, int heads) {
+  RankTable t;
+  t.heads = heads;
+  for (int h = 0; h <= heads; ++h) t.off[h] = rank_offsets[h];
+  return t;
+}
 
 template <typename T>
 struct type_tag {
@@ -50,15 +58,27 @@ hipError_t dispatch(int rule, int in_dtype, int dk, int dv, F&& f) {
   return hipErrorInvalidValue;
 }
 
-// Bytes of dynamic LDS the update kernel needs for n staged tokens.
-size_t update_refresh_lds_bytes(const ssm_dims& d, int n_tokens, bool refresh);
+// Per-head ranks: rank_offsets is a host array of heads + 1 prefix offsets (checked by the
+// caller), or nullptr for the uniform rank d.rank.
+inline int max_rank_of(const int32_t* rank_offsets, int heads) {
+  int m = 0;
+  for (int h = 0; h < heads; ++h) {
+    const int r = rank_offsets[h + 1] - rank_offsets[h];
+    m = r > m ? r : m;
+  }
+  return m;
+}
 
-hipError_t launch_update_refresh(const ssm_dims& d, float* state, float* sketch,
-                                 const float* basis, const void* k_buf, const void* v_buf,
-                                 const float* decay_buf, const float* beta_buf, int n_tokens,
-                                 hipStream_t stream);
+// Bytes of dynamic LDS the update kernel needs for n staged tokens and a basis of max_rank rows.
+size_t update_refresh_lds_bytes(const ssm_dims& d, int n_tokens, int max_rank);
 
-hipError_t launch_sketch_decode(const ssm_dims& d, const float* sketch, const float* basis,
+hipError_t launch_update_refresh(const ssm_dims& d, const int32_t* rank_offsets, float* state,
+                                 float* sketch, const float* basis, const void* k_buf,
+                                 const void* v_buf, const float* decay_buf, const float* beta_buf,
+                                 int n_tokens, hipStream_t stream);
+
+hipError_t launch_sketch_decode(const ssm_dims& d, const int32_t* rank_offsets,
+                                const float* sketch, const float* basis,
                                 const void* q, const void* k_t, const void* v_t,
                                 const float* decay_t, const float* beta_t, void* k_buf,
                                 void* v_buf, float* decay_buf, float* beta_buf, int tau, float* y,

@@ -18,12 +18,12 @@ namespace ssm {
 
 namespace {
 
-template <int RULE, int DK, int DV, typename TIN>
+template <int RULE, int DK, int DV, typename TIN, typename RT>
 __global__ void __launch_bounds__(2 * DV)
 update_refresh_kernel(float* __restrict__ state, float* __restrict__ sketch,
                       const float* __restrict__ basis, const TIN* __restrict__ kbuf,
                       const TIN* __restrict__ vbuf, const float* __restrict__ dbuf,
-                      const float* __restrict__ bbuf, int heads, int window, int rank, int n) {
+                      const float* __restrict__ bbuf, int heads, int window, const RT rt, int n) {
   constexpr int RPL = DK / 8;          // rows of S per lane
   constexpr int NT = 2 * DV;           // threads per unit: d_v/32 waves
   constexpr int DSTR = (RULE == KDA) ? DK : 1;
@@ -32,7 +32,8 @@ update_refresh_kernel(float* __restrict__ state, float* __restrict__ sketch,
   float* lds = reinterpret_cast<float*>(lds4);
 
   const int unit = blockIdx.x;
-  const int head = unit % heads;
+  const int head = unit % heads, seq = unit / heads;
+  const int rank = rt.rank(head);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int cg = lane & 7, rg = lane >> 3;
@@ -59,7 +60,7 @@ update_refresh_kernel(float* __restrict__ state, float* __restrict__ sketch,
   const float* lb = ld + pad4(n * DSTR);
   float* lB = lds + window_lds_floats<RULE, DK, DV>(n);  // [rank][DK]
   if (sketch != nullptr) {
-    const float* Bh = basis + (size_t)head * rank * DK;
+    const float* Bh = basis + (size_t)rt.offset(head) * DK;
     for (int e = tid * 4; e < rank * DK; e += NT * 4)
       *reinterpret_cast<float4*>(lB + e) = *reinterpret_cast<const float4*>(Bh + e);
   }
@@ -84,7 +85,7 @@ update_refresh_kernel(float* __restrict__ state, float* __restrict__ sketch,
         store_stream(Su + (size_t)(row0 + m) * DV + col, s[m]);
     }
     if (sketch == nullptr) return;
-    float* Sku = sketch + (size_t)unit * rank * DV;
+    float* Sku = sketch + ((size_t)seq * rt.total() + rt.offset(head)) * DV;
     const bool b3 = (lane >> 3) & 1;
     for (int m0 = 0; m0 < rank; m0 += 8) {
       float4 P[8];
@@ -181,30 +182,36 @@ update_refresh_kernel(float* __restrict__ state, float* __restrict__ sketch,
 
 }  // namespace
 
-size_t update_refresh_lds_bytes(const ssm_dims& d, int n, bool refresh) {
+size_t update_refresh_lds_bytes(const ssm_dims& d, int n, int max_rank) {
   size_t floats = 0;
   dispatch(d.rule, SSM_IN_F32, d.d_k, d.d_v, [&](auto R, auto DK, auto DV, auto) {
     floats = (size_t)window_lds_floats<decltype(R)::value, decltype(DK)::value,
                                        decltype(DV)::value>(n);
     return hipSuccess;
   });
-  return (floats + (refresh ? (size_t)d.rank * d.d_k : 0)) * sizeof(float);
+  return (floats + (size_t)max_rank * d.d_k) * sizeof(float);
 }
 
-hipError_t launch_update_refresh(const ssm_dims& d, float* state, float* sketch,
-                                 const float* basis, const void* k_buf, const void* v_buf,
-                                 const float* decay_buf, const float* beta_buf, int n,
-                                 hipStream_t stream) {
+hipError_t launch_update_refresh(const ssm_dims& d, const int32_t* rank_offsets, float* state,
+                                 float* sketch, const float* basis, const void* k_buf,
+                                 const void* v_buf, const float* decay_buf, const float* beta_buf,
+                                 int n, hipStream_t stream) {
   const unsigned units = (unsigned)d.batch * (unsigned)d.heads;
-  const size_t lds = update_refresh_lds_bytes(d, n, sketch != nullptr);
+  int max_rank = 0;
+  if (sketch != nullptr) max_rank = rank_offsets ? max_rank_of(rank_offsets, d.heads) : d.rank;
+  const size_t lds = update_refresh_lds_bytes(d, n, max_rank);
   return dispatch(d.rule, d.in_dtype, d.d_k, d.d_v, [&](auto R, auto DK, auto DV, auto T) {
     using TIN = typename decltype(T)::type;
     constexpr int kR = decltype(R)::value, kDK = decltype(DK)::value, kDV = decltype(DV)::value;
-    hipLaunchKernelGGL((update_refresh_kernel<kR, kDK, kDV, TIN>), dim3(units), dim3(2 * kDV),
-                       lds, stream, state, sketch, basis, static_cast<const TIN*>(k_buf),
-                       static_cast<const TIN*>(v_buf), decay_buf, beta_buf, d.heads, d.window,
-                       d.rank, n);
-    return hipGetLastError();
+    auto go = [&](auto rt) {
+      hipLaunchKernelGGL((update_refresh_kernel<kR, kDK, kDV, TIN, decltype(rt)>), dim3(units),
+                         dim3(2 * kDV), lds, stream, state, sketch, basis,
+                         static_cast<const TIN*>(k_buf), static_cast<const TIN*>(v_buf),
+                         decay_buf, beta_buf, d.heads, d.window, rt, n);
+      return hipGetLastError();
+    };
+    if (rank_offsets == nullptr) return go(UniformRank{d.rank, d.heads});
+    return go(make_rank_table(rank_offsets, d.heads));
   });
 }
 

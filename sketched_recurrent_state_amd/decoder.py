@@ -21,7 +21,8 @@ from typing import Optional
 import torch
 
 from . import (Dims, IN_BF16, KDA, MAMBA2, buffer_append, full_read_decode_step,
-               recurrent_decode_step, sketch_decode_step, window_update_refresh)
+               rank_offsets, recurrent_decode_step, sketch_decode_step,
+               sketch_decode_step_ranked, window_update_refresh, window_update_refresh_ranked)
 
 
 class WindowedDecoder:
@@ -33,10 +34,12 @@ class WindowedDecoder:
             sketch kept) or "both" (both reads of the same tokens; for checks)
     fused:  append the current token inside the read kernel instead of a
             separate buffering launch
+    ranks:  optional per-head sketch ranks (H values); then basis is fp32 [sum(ranks), d_k]
+            and the sketch [N, sum(ranks), d_v]
     """
 
     def __init__(self, dims: Dims, state: torch.Tensor, basis: Optional[torch.Tensor] = None, *,
-                 read: str = "sketch", fused: bool = True):
+                 read: str = "sketch", fused: bool = True, ranks=None):
         if read not in ("sketch", "full", "both"):
             raise ValueError(read)
         if read != "full" and basis is None:
@@ -49,7 +52,9 @@ class WindowedDecoder:
         tin = torch.bfloat16 if dims.in_dtype == IN_BF16 else torch.float32
         self.state = state
         self.basis = basis
-        self.sketch = (torch.empty((N, H, r, dv), device=dev, dtype=torch.float32)
+        self.offsets = rank_offsets(ranks) if ranks is not None else None
+        rows = (H, r) if ranks is None else (int(self.offsets[H]),)
+        self.sketch = (torch.empty((N,) + rows + (dv,), device=dev, dtype=torch.float32)
                        if read != "full" else None)
         self.k_buf = torch.zeros((N, H, W, dk), device=dev, dtype=tin)
         self.v_buf = torch.zeros((N, H, W, dv), device=dev, dtype=tin)
@@ -59,18 +64,35 @@ class WindowedDecoder:
                          if dims.rule != MAMBA2 else None)
         self.tau = 0  # tokens already in the window buffer
 
+    # -- library calls, uniform or per-head ranks --------------------------------
+    def _update(self, n_tokens: int) -> None:
+        bufs = (self.k_buf, self.v_buf, self.decay_buf, self.beta_buf)
+        if n_tokens == 0:
+            bufs = (None, None, None, None)
+        if self.offsets is not None and self.sketch is not None:
+            window_update_refresh_ranked(self.d, self.offsets, self.state, self.sketch, self.basis,
+                                         *bufs, n_tokens)
+        else:
+            window_update_refresh(self.d, self.state, self.sketch,
+                                  self.basis if self.sketch is not None else None, *bufs, n_tokens)
+
+    def _sketch_read(self, q, tau, y, tok) -> None:
+        bufs = (self.k_buf, self.v_buf, self.decay_buf, self.beta_buf)
+        if self.offsets is not None:
+            sketch_decode_step_ranked(self.d, self.offsets, self.sketch, self.basis, q, *bufs, tau,
+                                      y, **tok)
+        else:
+            sketch_decode_step(self.d, self.sketch, self.basis, q, *bufs, tau, y, **tok)
+
     # -- window boundary ---------------------------------------------------------
     def refresh(self) -> None:
         """Store the sketch of the current state (refresh-only pass)."""
         if self.sketch is not None:
-            window_update_refresh(self.d, self.state, self.sketch, self.basis, None, None, None,
-                                  None, 0)
+            self._update(0)
 
     def flush(self) -> None:
         """Write the buffered tokens into the state now (a partial window) and refresh."""
-        window_update_refresh(self.d, self.state, self.sketch, self.basis if self.sketch is not None
-                              else None, self.k_buf, self.v_buf, self.decay_buf, self.beta_buf,
-                              self.tau)
+        self._update(self.tau)
         self.tau = 0
 
     # -- one decode step -----------------------------------------------------------
@@ -90,14 +112,13 @@ class WindowedDecoder:
             tok = {}
         bufs = (self.k_buf, self.v_buf, self.decay_buf, self.beta_buf)
         if self.read != "full":
-            sketch_decode_step(d, self.sketch, self.basis, q, *bufs, tau, y, **tok)
+            self._sketch_read(q, tau, y, tok)
             tok = {}  # the token is in the buffer now
         if self.read != "sketch":
             full_read_decode_step(d, self.state, q, *bufs, tau, y_full, **tok)
         self.tau = tau
         if tau == d.window:
-            window_update_refresh(d, self.state, self.sketch,
-                                  self.basis if self.sketch is not None else None, *bufs, tau)
+            self._update(tau)
             self.tau = 0
         if self.read == "both":
             return y, y_full

@@ -238,3 +238,26 @@ def test_recurrent_step_validation():
     st, msg = status_of(ssm.recurrent_decode_step, d, p[0], p[1], p[2], p[3], p[4], p[5], p[0] + 64)
     assert st == 5 and "overlaps" in msg
     assert status_of(ssm.recurrent_decode_step, dims(batch=0), *([None] * 7))[0] == 0
+
+
+def test_rank_table_validation():
+    p = addrs(8)
+    d = dims(heads=3, d_k=32)
+    # a valid table passes the table checks and stops at the NULL state
+    st, msg = status_of(ssm.window_update_refresh_ranked, d, [0, 2, 5, 9], None, *p[1:7], 1)
+    assert st == 1 and "state" in msg
+    st, msg = status_of(ssm.window_update_refresh_ranked, d, [1, 2, 5, 9], *p[:7], 1)
+    assert st == 4 and "rank_offsets[0]" in msg
+    st, msg = status_of(ssm.window_update_refresh_ranked, d, [0, 2, 2, 9], *p[:7], 1)
+    assert st == 4 and "head 1 has rank 0" in msg
+    st, msg = status_of(ssm.sketch_decode_step_ranked, d, [0, 2, 40, 41], *p[:7], 1, p[7])
+    assert st == 4 and "head 1 has rank 38" in msg
+    with pytest.raises(ValueError, match="heads \\+ 1"):
+        ssm.window_update_refresh_ranked(d, [0, 1, 2, 3, 4], *p[:7], 1)
+    big = dims(heads=300, d_k=32)
+    st, msg = status_of(ssm.window_update_refresh_ranked, big, [1] * 300, *p[:7], 1)
+    assert st == 2 and "heads" in msg
+    # sizes follow the table: a sketch that overlaps the state under the table's size is caught
+    st, msg = status_of(ssm.window_update_refresh_ranked, d, [0, 2, 5, 9], p[0], p[0] + 2 * 3 * 32 * 64 * 4 - 16,
+                        *p[2:7], 1)
+    assert st == 5 and "overlaps" in msg

@@ -213,3 +213,61 @@ def test_recurrent_step_workload_sampled(name):
     H.note(f"case recurrent {name} (sampled units, 24 steps)")
     inp = H.Inputs(cfg, workloads.sample_units(cfg, 24), cfg.steps)
     H.compare_recurrent(cfg, H.run_gpu_recurrent(cfg, inp), inp)
+
+
+def _ranked_case(cfg, ranks, steps=None):
+    """Per-head ranks: the GPU's ranked entry points against the oracle run per rank group."""
+    import oracle
+    steps = steps or cfg.steps
+    units = np.arange(cfg.units) if cfg.units <= 64 else workloads.sample_units(cfg, 32)
+    inp = H.Inputs(cfg, units, steps)
+    B = workloads.basis_ranked(cfg, ranks)
+    off = np.concatenate([[0], np.cumsum(ranks)])
+    d = H.dims_of(cfg.with_(rank=max(ranks)))
+    U, W, R = cfg.units, cfg.window, int(off[-1])
+    state = inp.S0.clone()
+    dec = WindowedDecoder(d, state, torch.from_numpy(B).cuda(), read="both", ranks=ranks)
+    dec.refresh()
+    ys, sks = [], [dec.sketch.clone()]
+    for t in range(steps):
+        y, _ = dec.step(inp.q[t], inp.k[t], inp.v[t], inp.decay[t], inp.beta[t])
+        ys.append(y.view(U, -1)[torch.as_tensor(units, device="cuda")].cpu().double().numpy())
+        if (t + 1) % W == 0:
+            sks.append(dec.sketch.clone())
+    torch.cuda.synchronize()
+    ys = np.stack(ys)
+    heads = units % cfg.heads
+    h = inp.host
+    worst = 0.0
+    for r in sorted(set(ranks)):
+        sel = np.nonzero(np.array([ranks[x] == r for x in heads]))[0]
+        if sel.size == 0:
+            continue
+        Bu = np.stack([B[off[heads[i]]:off[heads[i]] + r] for i in sel]).astype(np.float64)
+        ref = oracle.run(cfg.rule, inp.host_S0[sel], Bu, h["q"][:, sel], h["k"][:, sel],
+                         h["v"][:, sel], h["decay"][:, sel],
+                         None if h["beta"] is None else h["beta"][:, sel], W)
+        e = H.rel_rows(ys[:, sel], ref["y_sketch"])
+        worst = max(worst, float(e.max()))
+        assert e.max() <= H.Y_TOL, f"rank {r}: sketch read max rel err {e.max():.3e}"
+        for w, sk in enumerate(sks):
+            got = np.stack([sk.view(cfg.batch, R, cfg.d_v)[units[i] // cfg.heads,
+                                                          off[heads[i]]:off[heads[i]] + r]
+                            .cpu().double().numpy() for i in sel])
+            es = H.rel_rows(got.reshape(len(sel), -1)[None], ref["Sk"][w].reshape(len(sel), -1)[None])
+            assert es.max() <= H.S_TOL, f"rank {r}: sketch after window {w}: {es.max():.3e}"
+    H.note(f"ranked {cfg.name} ranks={sorted(set(ranks))}: max sketch-read err {worst:.2e}")
+
+
+@pytest.mark.parametrize("rule", ["mamba2", "gdn", "kda"])
+def test_per_head_ranks_small(rule):
+    cfg = small(rule, N=3, Hh=5, W=4, T=11)
+    H.note(f"case per-head ranks {rule}")
+    _ranked_case(cfg, [1, 8, 3, 16, 32])
+
+
+def test_per_head_ranks_average_8_workload():
+    """The GDN workload with a mean-8 rank pattern (2, 4, 8, 18 cycled over heads)."""
+    cfg = workloads.C3.with_(steps=24)
+    H.note("case per-head ranks c3 (sampled units)")
+    _ranked_case(cfg, workloads.average_rank_8(cfg.heads))

@@ -262,6 +262,22 @@ def basis(cfg: Config) -> np.ndarray:
     return out.astype(np.float32)
 
 
+def basis_ranked(cfg: Config, ranks) -> np.ndarray:
+    """Per-head ranks: head h keeps the first ranks[h] rows of its d_k-row basis
+    (the same draws as basis() with r = d_k). fp32 [sum(ranks)][d_k]."""
+    full = basis(cfg.with_(rank=cfg.d_k))
+    return np.ascontiguousarray(np.concatenate([full[h, :int(r)] for h, r in enumerate(ranks)]))
+
+
+def average_rank_8(heads: int) -> list:
+    """A per-head rank pattern with mean 8 (cycles 2, 4, 8, 18)."""
+    pattern = [2, 4, 8, 18]
+    ranks = [pattern[h % 4] for h in range(heads)]
+    if heads % 4:
+        raise ValueError("heads must be a multiple of 4 for the mean-8 pattern")
+    return ranks
+
+
 def decay_shape(cfg: Config, lead) -> tuple:
     return tuple(lead) + ((cfg.d_k,) if cfg.per_channel_decay else ())
 
