@@ -89,6 +89,9 @@ def main() -> int:
     ap.add_argument("--cpu-steps", type=int, default=16, help="oracle sample: decode steps")
     ap.add_argument("--only", choices=["sketch", "full", "update"], default=None,
                     help="profiling: run only this leg's launches")
+    ap.add_argument("--schedule", choices=["lockstep", "staggered"], default="lockstep",
+                    help="staggered: sequence n sits at window position n mod W, so every step "
+                         "updates N/W sequences (variable-length entry points, slot map)")
     ap.add_argument("--per-head-ranks", choices=["avg8"], default=None,
                     help="per-head sketch ranks (avg8: 2, 4, 8, 18 cycled over heads, mean 8)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -258,6 +261,45 @@ def main() -> int:
     elapsed = graph_s
     del g_sketch
 
+    # ---- staggered windows (serving shape): every step updates N/W sequences -----------
+    staggered = None
+    if a.schedule == "staggered":
+        N = cfg.batch
+        taus = [torch.tensor([((ph + n) % W) + 1 for n in range(N)], dtype=torch.int32, device=dev)
+                for ph in range(W)]
+        ups = [torch.tensor([n for n in range(N) if ((ph + n) % W) + 1 == W], dtype=torch.int32,
+                            device=dev) for ph in range(W)]
+        fulls = [torch.full((len(u),), W, dtype=torch.int32, device=dev) for u in ups]
+        d_ups = [ssm.Dims.make(cfg.rule, cfg.in_dtype, len(u), cfg.heads, cfg.d_k, cfg.d_v, W,
+                               cfg.rank) for u in ups]
+        tp, up, fp = [P(x) for x in taus], [P(x) for x in ups], [P(x) for x in fulls]
+
+        def run_staggered(t_lo, t_hi, sp_, upd_events=None):
+            for t in range(t_lo, t_hi):
+                q, k, v, dc, b = ptrs[t]
+                ph = t % W
+                ssm.sketch_decode_step_varlen(d, N, None, tp[ph], sk_p, bp, q, kb, vb, db, bb, yp,
+                                              k_t=k, v_t=v, decay_t=dc, beta_t=b, stream=sp_)
+                if d_ups[ph].batch:
+                    if upd_events is not None:
+                        upd_events.append((torch.cuda.Event(enable_timing=True),
+                                           torch.cuda.Event(enable_timing=True)))
+                        upd_events[-1][0].record(stream)
+                    ssm.window_update_refresh_varlen(d_ups[ph], N, up[ph], fp[ph], st_p, sk_p, bp,
+                                                     kb, vb, db, bb, stream=sp_)
+                    if upd_events is not None:
+                        upd_events[-1][1].record(stream)
+
+        run_staggered(0, a.warmup, sp)
+        stg_ev = []
+        eager_g = timed(lambda: run_staggered(a.warmup, total, sp, stg_ev))
+        graph_g, g_stg = graph_timed(lambda cs: run_staggered(a.warmup, total, cs))
+        del g_stg
+        staggered = {"steps_per_s": a.steps / graph_g, "ms_per_step": graph_g * 1e3 / a.steps,
+                     "eager_steps_per_s": a.steps / eager_g,
+                     "update_per_step_ms": float(np.mean([s_.elapsed_time(e_) for s_, e_ in stg_ev])),
+                     "sequences_updated_per_step": N / W}
+
     # ---- per-kernel time of the sketch read (events around each launch) ---------------
     def kernel_time(launch, reps):
         evs = []
@@ -420,6 +462,7 @@ def main() -> int:
         "full_read_path": full,
         "speedup_vs_full_read": (value / full["steps_per_s"]) if full else None,
         "per_token_path": per_token,
+        "staggered_windows": staggered,
         "speedup_vs_per_token": (value / per_token["steps_per_s"]) if per_token else None,
         "bytes_per_unit": {k: bm[k] for k in ("state_bytes_sketch", "state_bytes_full", "sketch_step",
                                               "full_step", "amortized_sketch", "amortized_full")},

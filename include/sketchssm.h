@@ -197,6 +197,41 @@ ssm_status ssm_sketch_decode_step_ranked(const ssm_dims* d, const int32_t* rank_
                                          float* beta_buf, int32_t tau, float* y, void* stream);
 
 /*
+ * Variable-length batches over a pool of persistent slots (serving with
+ * continuous batching: sequences join, leave and sit at different positions
+ * of their windows). A call serves d->batch rows; row n uses slot[n] (a DEVICE
+ * int32 array, or NULL for slot n) of a pool of num_slots slots:
+ *   persistent, indexed by slot: state [num_slots][H][d_k][d_v], sketch
+ *     [num_slots][H][r][d_v], k_buf/v_buf/decay_buf/beta_buf [num_slots][H][W]...
+ *   per call, indexed by row: q, k_t, v_t, decay_t, beta_t, y [batch][H][...]
+ * Per-row counts come from DEVICE int32 arrays:
+ *   ssm_window_update_refresh_varlen: n_tokens[n] in [0, W] tokens to apply
+ *     (0 = refresh only); any other value skips the row.
+ *   ssm_sketch_decode_step_varlen: tau[n] in [1, W] as in ssm_sketch_decode_step;
+ *     any other value skips the row (its y is not written).
+ * A row whose slot is outside [0, num_slots) is skipped too. Rows of one call
+ * must map to distinct slots (calls with repeated slots race); the device
+ * arrays are not read on the host. Uniform sketch rank (d->rank). The slot and
+ * count arrays need 4-byte alignment; everything else as the lockstep entry
+ * points. Source: the pages' setting of large decode batches (readsearch.ai
+ * listing, Abstract); the serving schedule itself is not on the pages.
+ */
+ssm_status ssm_window_update_refresh_varlen(const ssm_dims* d, int32_t num_slots,
+                                            const int32_t* slot, const int32_t* n_tokens,
+                                            float* state, float* sketch, const float* basis,
+                                            const void* k_buf, const void* v_buf,
+                                            const float* decay_buf, const float* beta_buf,
+                                            void* stream);
+
+ssm_status ssm_sketch_decode_step_varlen(const ssm_dims* d, int32_t num_slots,
+                                         const int32_t* slot, const int32_t* tau,
+                                         const float* sketch, const float* basis, const void* q,
+                                         const void* k_t, const void* v_t,
+                                         const float* decay_t, const float* beta_t,
+                                         void* k_buf, void* v_buf, float* decay_buf,
+                                         float* beta_buf, float* y, void* stream);
+
+/*
  * Per-token recurrent decode step (the standard decode SketchSSM is compared
  * against: readsearch.ai listing, Abstract, kernel speedups over the standard
  * vLLM baseline; agihunt.info "Confirmed", background bullet: every step reads

@@ -21,7 +21,8 @@ __all__ = [
     "Dims", "SSMError", "MAMBA2", "GDN", "KDA", "IN_BF16", "IN_F32", "RULES",
     "abi_version", "buffer_append", "window_update_refresh", "sketch_decode_step",
     "full_read_decode_step", "recurrent_decode_step", "window_update_refresh_ranked",
-    "sketch_decode_step_ranked", "rank_offsets", "LIB_PATH", "HEADER", "declared_symbols",
+    "sketch_decode_step_ranked", "rank_offsets", "window_update_refresh_varlen",
+    "sketch_decode_step_varlen", "LIB_PATH", "HEADER", "declared_symbols",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -88,6 +89,10 @@ def _load():
     lib.ssm_window_update_refresh_ranked.argtypes = [dp, ip] + [vp] * 7 + [i32, vp]
     lib.ssm_sketch_decode_step_ranked.restype = i32
     lib.ssm_sketch_decode_step_ranked.argtypes = [dp, ip] + [vp] * 11 + [i32, vp, vp]
+    lib.ssm_window_update_refresh_varlen.restype = i32
+    lib.ssm_window_update_refresh_varlen.argtypes = [dp, i32] + [vp] * 9 + [vp]
+    lib.ssm_sketch_decode_step_varlen.restype = i32
+    lib.ssm_sketch_decode_step_varlen.argtypes = [dp, i32] + [vp] * 15
     lib.ssm_recurrent_decode_step.restype = i32
     lib.ssm_recurrent_decode_step.argtypes = [dp] + [vp] * 7 + [vp]
     lib.ssm_full_read_decode_step.restype = i32
@@ -337,4 +342,65 @@ def sketch_decode_step_ranked(d: Dims, offsets, sketch, basis, q, k_buf, v_buf, 
         _addr(k_buf, "k_buf", tin, n["k_buf"]), _addr(v_buf, "v_buf", tin, n["v_buf"]),
         _addr(decay_buf, "decay_buf", f32, n["decay_buf"]),
         _addr(beta_buf, "beta_buf", f32, n["beta_buf"]), int(tau), _addr(y, "y", f32, n["y"]),
+        _stream(stream)))
+
+
+# ----------------------------------------------------------------------------
+# variable-length batches over a pool of slots
+# ----------------------------------------------------------------------------
+def _pool_numel(d: Dims, num_slots: int) -> dict:
+    n = numel(d)
+    p = numel(Dims(d.rule, d.in_dtype, num_slots, d.heads, d.d_k, d.d_v, d.window, d.rank))
+    for key in ("state", "sketch", "k_buf", "v_buf", "decay_buf", "beta_buf"):
+        n[key] = p[key]
+    n["rows"] = d.batch
+    return n
+
+
+def _i32():
+    import torch
+    return (torch.int32,)
+
+
+def window_update_refresh_varlen(d: Dims, num_slots: int, slot, n_tokens, state, sketch, basis,
+                                 k_buf, v_buf, decay_buf, beta_buf, stream=None) -> None:
+    """ssm_window_update_refresh_varlen: per-row token counts (device int32 [batch]) and an
+    optional slot map (device int32 [batch]) into a pool of num_slots persistent slots."""
+    args = (slot, n_tokens, state, sketch, basis, k_buf, v_buf, decay_buf, beta_buf)
+    if isinstance(stream, int) and _all_raw(args):
+        return _check(_lib.ssm_window_update_refresh_varlen(ctypes.byref(d), int(num_slots), *args,
+                                                            stream))
+    tin, f32 = _types(d, args)
+    i32 = None if tin is None else _i32()
+    n = _pool_numel(d, num_slots)
+    _check(_lib.ssm_window_update_refresh_varlen(
+        ctypes.byref(d), int(num_slots), _addr(slot, "slot", i32, n["rows"]),
+        _addr(n_tokens, "n_tokens", i32, n["rows"]), _addr(state, "state", f32, n["state"]),
+        _addr(sketch, "sketch", f32, n["sketch"]), _addr(basis, "basis", f32, n["basis"]),
+        _addr(k_buf, "k_buf", tin, n["k_buf"]), _addr(v_buf, "v_buf", tin, n["v_buf"]),
+        _addr(decay_buf, "decay_buf", f32, n["decay_buf"]),
+        _addr(beta_buf, "beta_buf", f32, n["beta_buf"]), _stream(stream)))
+
+
+def sketch_decode_step_varlen(d: Dims, num_slots: int, slot, tau, sketch, basis, q, k_buf, v_buf,
+                              decay_buf, beta_buf, y, *, k_t=None, v_t=None, decay_t=None,
+                              beta_t=None, stream=None) -> None:
+    """ssm_sketch_decode_step_varlen: per-row window positions tau (device int32 [batch])."""
+    args = (slot, tau, sketch, basis, q, k_t, v_t, decay_t, beta_t, k_buf, v_buf, decay_buf,
+            beta_buf, y)
+    if isinstance(stream, int) and _all_raw(args):
+        return _check(_lib.ssm_sketch_decode_step_varlen(ctypes.byref(d), int(num_slots), *args,
+                                                         stream))
+    tin, f32 = _types(d, args)
+    i32 = None if tin is None else _i32()
+    n = _pool_numel(d, num_slots)
+    _check(_lib.ssm_sketch_decode_step_varlen(
+        ctypes.byref(d), int(num_slots), _addr(slot, "slot", i32, n["rows"]),
+        _addr(tau, "tau", i32, n["rows"]), _addr(sketch, "sketch", f32, n["sketch"]),
+        _addr(basis, "basis", f32, n["basis"]), _addr(q, "q", tin, n["q"]),
+        _addr(k_t, "k_t", tin, n["k_t"]), _addr(v_t, "v_t", tin, n["v_t"]),
+        _addr(decay_t, "decay_t", f32, n["decay_t"]), _addr(beta_t, "beta_t", f32, n["beta_t"]),
+        _addr(k_buf, "k_buf", tin, n["k_buf"]), _addr(v_buf, "v_buf", tin, n["v_buf"]),
+        _addr(decay_buf, "decay_buf", f32, n["decay_buf"]),
+        _addr(beta_buf, "beta_buf", f32, n["beta_buf"]), _addr(y, "y", f32, n["y"]),
         _stream(stream)))

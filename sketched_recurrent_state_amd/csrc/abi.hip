@@ -65,12 +65,13 @@ struct Arr {
   size_t bytes;
   bool output;
   const char* name;
+  unsigned align = 16;
 };
 
 ssm_status check_arrays(const char* fn, std::initializer_list<Arr> arrs) {
   for (const Arr& a : arrs) {
-    if (a.p != nullptr && (reinterpret_cast<uintptr_t>(a.p) & 15u) != 0)
-      return fail(SSM_E_ALIGN, "%s: %s (%p) is not 16-byte aligned", fn, a.name, a.p);
+    if (a.p != nullptr && (reinterpret_cast<uintptr_t>(a.p) & (a.align - 1)) != 0)
+      return fail(SSM_E_ALIGN, "%s: %s (%p) is not %u-byte aligned", fn, a.name, a.p, a.align);
   }
   for (const Arr& a : arrs) {
     if (a.p == nullptr || a.bytes == 0) continue;
@@ -162,6 +163,34 @@ void apply_ranks(const ssm_dims& d, const int32_t* off, Sizes& z) {
   const size_t R = (size_t)off[d.heads];
   z.sketch = z.units / (size_t)d.heads * R * d.d_v * 4;
   z.basis = R * d.d_k * 4;
+}
+
+// A variable-length call: `batch` rows mapped onto a pool of num_slots persistent slots.
+ssm_status check_pool(const ssm_dims& d, int32_t num_slots, const int32_t* slot,
+                      const int32_t* counts, const char* what, const char* fn) {
+  if (num_slots < 1) return fail(SSM_E_SHAPE, "%s: num_slots %d < 1", fn, num_slots);
+  if ((long long)num_slots * d.heads >= kMaxUnits)
+    return fail(SSM_E_SHAPE, "%s: num_slots*heads = %lld >= %lld", fn,
+                (long long)num_slots * d.heads, kMaxUnits);
+  if (slot == nullptr && d.batch > num_slots)
+    return fail(SSM_E_SHAPE, "%s: %d rows but %d slots and no slot map", fn, d.batch, num_slots);
+  if (counts == nullptr) return fail(SSM_E_NULL, "%s: %s is NULL", fn, what);
+  return SSM_OK;
+}
+
+// Sizes of the persistent arrays (state, sketch, window buffer) for a pool of slots.
+Sizes pool_sizes(const ssm_dims& d, int32_t num_slots) {
+  ssm_dims p = d;
+  p.batch = num_slots;
+  const Sizes zp = sizes_of(p);
+  Sizes z = sizes_of(d);
+  z.state = zp.state;
+  z.sketch = zp.sketch;
+  z.kbuf = zp.kbuf;
+  z.vbuf = zp.vbuf;
+  z.dbuf = zp.dbuf;
+  z.bbuf = zp.bbuf;
+  return z;
 }
 
 ssm_status launched(hipError_t e, const char* fn) {
@@ -376,6 +405,74 @@ ssm_status ssm_sketch_decode_step_ranked(const ssm_dims* d, const int32_t* rank_
   return sketch_decode_impl("ssm_sketch_decode_step_ranked", d, rank_offsets, sketch, basis, q,
                             k_t, v_t, decay_t, beta_t, k_buf, v_buf, decay_buf, beta_buf, tau, y,
                             stream, true);
+}
+
+ssm_status ssm_window_update_refresh_varlen(const ssm_dims* d, int32_t num_slots,
+                                            const int32_t* slot, const int32_t* n_tokens,
+                                            float* state, float* sketch, const float* basis,
+                                            const void* k_buf, const void* v_buf,
+                                            const float* decay_buf, const float* beta_buf,
+                                            void* stream) {
+  static const char* fn = "ssm_window_update_refresh_varlen";
+  ssm_status st = check_dims(d, fn);
+  if (st != SSM_OK) return st;
+  if (d->batch == 0) return ok();
+  if ((st = check_pool(*d, num_slots, slot, n_tokens, "n_tokens", fn)) != SSM_OK) return st;
+  if (state == nullptr) return fail(SSM_E_NULL, "%s: state is NULL", fn);
+  if (sketch != nullptr && basis == nullptr)
+    return fail(SSM_E_NULL, "%s: basis is NULL but a sketch is requested", fn);
+  if ((st = check_buffers(*d, k_buf, v_buf, decay_buf, beta_buf, fn)) != SSM_OK) return st;
+  const Sizes z = pool_sizes(*d, num_slots);
+  const size_t rows = (size_t)d->batch * 4;
+  st = check_arrays(fn, {{state, z.state, true, "state"}, {sketch, z.sketch, true, "sketch"},
+                         {basis, z.basis, false, "basis"}, {k_buf, z.kbuf, false, "k_buf"},
+                         {v_buf, z.vbuf, false, "v_buf"}, {decay_buf, z.dbuf, false, "decay_buf"},
+                         {beta_buf, z.bbuf, false, "beta_buf"},
+                         {slot, rows, false, "slot", 4}, {n_tokens, rows, false, "n_tokens", 4}});
+  if (st != SSM_OK) return st;
+  const ssm::Varlen vl{slot, n_tokens, num_slots, 0, d->window};
+  (void)hipGetLastError();
+  return launched(ssm::launch_update_refresh(*d, nullptr, state, sketch, basis, k_buf, v_buf,
+                                             decay_buf, beta_buf, 0,
+                                             reinterpret_cast<hipStream_t>(stream), &vl),
+                  fn);
+}
+
+ssm_status ssm_sketch_decode_step_varlen(const ssm_dims* d, int32_t num_slots,
+                                         const int32_t* slot, const int32_t* tau,
+                                         const float* sketch, const float* basis, const void* q,
+                                         const void* k_t, const void* v_t, const float* decay_t,
+                                         const float* beta_t, void* k_buf, void* v_buf,
+                                         float* decay_buf, float* beta_buf, float* y,
+                                         void* stream) {
+  static const char* fn = "ssm_sketch_decode_step_varlen";
+  ssm_status st = check_dims(d, fn);
+  if (st != SSM_OK) return st;
+  if (d->batch == 0) return ok();
+  if ((st = check_pool(*d, num_slots, slot, tau, "tau", fn)) != SSM_OK) return st;
+  if (sketch == nullptr) return fail(SSM_E_NULL, "%s: sketch is NULL", fn);
+  if (basis == nullptr) return fail(SSM_E_NULL, "%s: basis is NULL", fn);
+  if (q == nullptr) return fail(SSM_E_NULL, "%s: q is NULL", fn);
+  if (y == nullptr) return fail(SSM_E_NULL, "%s: y is NULL", fn);
+  if ((st = check_token(*d, k_t, v_t, decay_t, beta_t, fn)) != SSM_OK) return st;
+  if ((st = check_buffers(*d, k_buf, v_buf, decay_buf, beta_buf, fn)) != SSM_OK) return st;
+  const Sizes z = pool_sizes(*d, num_slots);
+  const size_t rows = (size_t)d->batch * 4;
+  const bool fused = k_t != nullptr;
+  st = check_arrays(fn, {{sketch, z.sketch, false, "sketch"}, {basis, z.basis, false, "basis"},
+                         {q, z.qk, false, "q"}, {k_t, z.qk, false, "k_t"}, {v_t, z.v, false, "v_t"},
+                         {decay_t, z.dtok, false, "decay_t"}, {beta_t, z.btok, false, "beta_t"},
+                         {k_buf, z.kbuf, fused, "k_buf"}, {v_buf, z.vbuf, fused, "v_buf"},
+                         {decay_buf, z.dbuf, fused, "decay_buf"},
+                         {beta_buf, z.bbuf, fused, "beta_buf"}, {y, z.y, true, "y"},
+                         {slot, rows, false, "slot", 4}, {tau, rows, false, "tau", 4}});
+  if (st != SSM_OK) return st;
+  const ssm::Varlen vl{slot, tau, num_slots, 1, d->window};
+  (void)hipGetLastError();
+  return launched(ssm::launch_sketch_decode(*d, nullptr, sketch, basis, q, k_t, v_t, decay_t,
+                                            beta_t, k_buf, v_buf, decay_buf, beta_buf, 0, y,
+                                            reinterpret_cast<hipStream_t>(stream), &vl),
+                  fn);
 }
 
 }  // extern "C"

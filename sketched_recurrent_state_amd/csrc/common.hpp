@@ -300,6 +300,31 @@ struct RankTable {  // per-head ranks: off[h + 1] - off[h], off[0] = 0 (checked 
 };
 
 // ---------------------------------------------------------------------------
+// batch rows -> persistent slots and window positions. Per-step arrays (q, the
+// current token, y) are indexed by the batch row; the state, the sketch and the
+// window buffer by the row's slot.
+// ---------------------------------------------------------------------------
+struct Lockstep {  // row n is slot n; every row holds `count` tokens (tau, or n_tokens)
+  int count;
+  __device__ __forceinline__ bool row(int n, int& slot, int& cnt) const {
+    slot = n;
+    cnt = count;
+    return true;
+  }
+};
+
+struct Varlen {  // per-row slot (identity if null) and token count; rows out of range are skipped
+  const int32_t* slot;
+  const int32_t* count;
+  int num_slots, lo, hi;  // a row is served when lo <= count <= hi and 0 <= slot < num_slots
+  __device__ __forceinline__ bool row(int n, int& s, int& cnt) const {
+    s = slot ? slot[n] : n;
+    cnt = count[n];
+    return s >= 0 && s < num_slots && cnt >= lo && cnt <= hi;
+  }
+};
+
+// ---------------------------------------------------------------------------
 // window staging: the first n buffered tokens of one unit -> LDS as fp32
 // ---------------------------------------------------------------------------
 __host__ __device__ inline int pad4(int x) { return (x + 3) & ~3; }

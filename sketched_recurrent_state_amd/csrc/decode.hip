@@ -48,7 +48,7 @@ __device__ __forceinline__ void carry_back(float* u, const float* kk, const floa
 template <int DK>
 constexpr int sketch_group() { return DK >= 32 ? 32 : 16; }
 
-template <int RULE, int DK, int DV, typename TIN, int WMAX, typename RT>
+template <int RULE, int DK, int DV, typename TIN, int WMAX, typename RT, typename RM>
 __global__ void __launch_bounds__(256)
 sketch_decode_kernel(const float* __restrict__ sketch, const float* __restrict__ basis,
                      const TIN* __restrict__ q, const TIN* __restrict__ k_t,
@@ -56,7 +56,7 @@ sketch_decode_kernel(const float* __restrict__ sketch, const float* __restrict__
                      const float* __restrict__ b_t, TIN* __restrict__ kbuf,
                      TIN* __restrict__ vbuf, float* __restrict__ dbuf, float* __restrict__ bbuf,
                      float* __restrict__ y, int batch, int heads, int window, const RT rt,
-                     int tau) {
+                     const RM rm) {
   constexpr int G = sketch_group<DK>();
   static_assert(WMAX <= G, "one gate per lane");
   constexpr int UPB = 256 / G;                // sequences per workgroup
@@ -68,11 +68,13 @@ sketch_decode_kernel(const float* __restrict__ sketch, const float* __restrict__
 
   const int head = blockIdx.x % heads;
   const int rank = rt.rank(head);
-  const int seq = (blockIdx.x / heads) * UPB + threadIdx.x / G;
+  const int row = (blockIdx.x / heads) * UPB + threadIdx.x / G;  // batch row
   const int sub = threadIdx.x % G;
-  const bool active = seq < batch;            // whole G-lane groups
-  const size_t unit = (size_t)seq * heads + head;
-  const size_t slot0 = unit * window;
+  int seq = 0, tau = 0;                       // the row's persistent slot and window position
+  const bool active = row < batch && rm.row(row, seq, tau);  // whole G-lane groups
+  const size_t unit = (size_t)row * heads + head;            // per-step arrays
+  const size_t punit = (size_t)seq * heads + head;           // state, sketch, buffer
+  const size_t slot0 = punit * window;
   const bool fused = (k_t != nullptr);
 
   // ---- issue every load ----
@@ -269,7 +271,8 @@ hipError_t launch_sketch_decode(const ssm_dims& d, const int32_t* rank_offsets,
                                 const float* sketch, const float* basis, const void* q,
                                 const void* k_t, const void* v_t, const float* decay_t,
                                 const float* beta_t, void* k_buf, void* v_buf, float* decay_buf,
-                                float* beta_buf, int tau, float* y, hipStream_t stream) {
+                                float* beta_buf, int tau, float* y, hipStream_t stream,
+                                const Varlen* varlen) {
   const int max_rank = rank_offsets ? max_rank_of(rank_offsets, d.heads) : d.rank;
   return dispatch(d.rule, d.in_dtype, d.d_k, d.d_v, [&](auto R, auto DK, auto DV, auto T) {
     using TIN = typename decltype(T)::type;
@@ -277,19 +280,20 @@ hipError_t launch_sketch_decode(const ssm_dims& d, const int32_t* rank_offsets,
     constexpr unsigned UPB = 256u / sketch_group<kDK>();
     const unsigned blocks = (unsigned)d.heads * (((unsigned)d.batch + UPB - 1) / UPB);
     const size_t lds = (size_t)max_rank * kDK * sizeof(float);
-    auto go = [&](auto wmax, auto rt) {
+    auto go = [&](auto wmax, auto rt, auto rm) {
       constexpr int kW = decltype(wmax)::value;
-      hipLaunchKernelGGL((sketch_decode_kernel<kR, kDK, kDV, TIN, kW, decltype(rt)>),
-                         dim3(blocks), dim3(256), lds, stream, sketch, basis,
-                         static_cast<const TIN*>(q), static_cast<const TIN*>(k_t),
-                         static_cast<const TIN*>(v_t), decay_t, beta_t, static_cast<TIN*>(k_buf),
-                         static_cast<TIN*>(v_buf), decay_buf, beta_buf, y, d.batch, d.heads,
-                         d.window, rt, tau);
+      hipLaunchKernelGGL(
+          (sketch_decode_kernel<kR, kDK, kDV, TIN, kW, decltype(rt), decltype(rm)>),
+          dim3(blocks), dim3(256), lds, stream, sketch, basis, static_cast<const TIN*>(q),
+          static_cast<const TIN*>(k_t), static_cast<const TIN*>(v_t), decay_t, beta_t,
+          static_cast<TIN*>(k_buf), static_cast<TIN*>(v_buf), decay_buf, beta_buf, y, d.batch,
+          d.heads, d.window, rt, rm);
       return hipGetLastError();
     };
     auto with_rank = [&](auto wmax) {
-      if (rank_offsets == nullptr) return go(wmax, UniformRank{d.rank, d.heads});
-      return go(wmax, make_rank_table(rank_offsets, d.heads));
+      if (varlen != nullptr) return go(wmax, UniformRank{d.rank, d.heads}, *varlen);
+      if (rank_offsets == nullptr) return go(wmax, UniformRank{d.rank, d.heads}, Lockstep{tau});
+      return go(wmax, make_rank_table(rank_offsets, d.heads), Lockstep{tau});
     };
     if (d.window <= 4) return with_rank(std::integral_constant<int, 4>{});
     if (d.window <= 8) return with_rank(std::integral_constant<int, 8>{});

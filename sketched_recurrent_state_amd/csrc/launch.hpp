@@ -72,17 +72,19 @@ inline int max_rank_of(const int32_t* rank_offsets, int heads) {
 // Bytes of dynamic LDS the update kernel needs for n staged tokens and a basis of max_rank rows.
 size_t update_refresh_lds_bytes(const ssm_dims& d, int n_tokens, int max_rank);
 
+// varlen != nullptr: per-row slots and token counts (n_tokens is then ignored).
 hipError_t launch_update_refresh(const ssm_dims& d, const int32_t* rank_offsets, float* state,
                                  float* sketch, const float* basis, const void* k_buf,
                                  const void* v_buf, const float* decay_buf, const float* beta_buf,
-                                 int n_tokens, hipStream_t stream);
+                                 int n_tokens, hipStream_t stream,
+                                 const Varlen* varlen = nullptr);
 
 hipError_t launch_sketch_decode(const ssm_dims& d, const int32_t* rank_offsets,
                                 const float* sketch, const float* basis,
                                 const void* q, const void* k_t, const void* v_t,
                                 const float* decay_t, const float* beta_t, void* k_buf,
                                 void* v_buf, float* decay_buf, float* beta_buf, int tau, float* y,
-                                hipStream_t stream);
+                                hipStream_t stream, const Varlen* varlen = nullptr);
 
 hipError_t launch_full_read_decode(const ssm_dims& d, const float* state, const void* q,
                                    const void* k_t, const void* v_t, const float* decay_t,

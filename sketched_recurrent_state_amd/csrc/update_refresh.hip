@@ -18,12 +18,13 @@ namespace ssm {
 
 namespace {
 
-template <int RULE, int DK, int DV, typename TIN, typename RT>
+template <int RULE, int DK, int DV, typename TIN, typename RT, typename RM>
 __global__ void __launch_bounds__(2 * DV)
 update_refresh_kernel(float* __restrict__ state, float* __restrict__ sketch,
                       const float* __restrict__ basis, const TIN* __restrict__ kbuf,
                       const TIN* __restrict__ vbuf, const float* __restrict__ dbuf,
-                      const float* __restrict__ bbuf, int heads, int window, const RT rt, int n) {
+                      const float* __restrict__ bbuf, int heads, int window, const RT rt,
+                      const RM rm) {
   constexpr int RPL = DK / 8;          // rows of S per lane
   constexpr int NT = 2 * DV;           // threads per unit: d_v/32 waves
   constexpr int DSTR = (RULE == KDA) ? DK : 1;
@@ -31,8 +32,10 @@ update_refresh_kernel(float* __restrict__ state, float* __restrict__ sketch,
   extern __shared__ float4 lds4[];
   float* lds = reinterpret_cast<float*>(lds4);
 
-  const int unit = blockIdx.x;
-  const int head = unit % heads, seq = unit / heads;
+  const int head = blockIdx.x % heads;
+  int seq = 0, n = 0;  // the batch row's persistent slot and its number of buffered tokens
+  if (!rm.row(blockIdx.x / heads, seq, n)) return;  // whole workgroup: a skipped row
+  const size_t unit = (size_t)seq * heads + head;
   const int rank = rt.rank(head);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -195,23 +198,25 @@ size_t update_refresh_lds_bytes(const ssm_dims& d, int n, int max_rank) {
 hipError_t launch_update_refresh(const ssm_dims& d, const int32_t* rank_offsets, float* state,
                                  float* sketch, const float* basis, const void* k_buf,
                                  const void* v_buf, const float* decay_buf, const float* beta_buf,
-                                 int n, hipStream_t stream) {
+                                 int n, hipStream_t stream, const Varlen* varlen) {
   const unsigned units = (unsigned)d.batch * (unsigned)d.heads;
   int max_rank = 0;
   if (sketch != nullptr) max_rank = rank_offsets ? max_rank_of(rank_offsets, d.heads) : d.rank;
-  const size_t lds = update_refresh_lds_bytes(d, n, max_rank);
+  // a variable-length call can stage up to W tokens per row
+  const size_t lds = update_refresh_lds_bytes(d, varlen ? d.window : n, max_rank);
   return dispatch(d.rule, d.in_dtype, d.d_k, d.d_v, [&](auto R, auto DK, auto DV, auto T) {
     using TIN = typename decltype(T)::type;
     constexpr int kR = decltype(R)::value, kDK = decltype(DK)::value, kDV = decltype(DV)::value;
-    auto go = [&](auto rt) {
-      hipLaunchKernelGGL((update_refresh_kernel<kR, kDK, kDV, TIN, decltype(rt)>), dim3(units),
-                         dim3(2 * kDV), lds, stream, state, sketch, basis,
+    auto go = [&](auto rt, auto rm) {
+      hipLaunchKernelGGL((update_refresh_kernel<kR, kDK, kDV, TIN, decltype(rt), decltype(rm)>),
+                         dim3(units), dim3(2 * kDV), lds, stream, state, sketch, basis,
                          static_cast<const TIN*>(k_buf), static_cast<const TIN*>(v_buf),
-                         decay_buf, beta_buf, d.heads, d.window, rt, n);
+                         decay_buf, beta_buf, d.heads, d.window, rt, rm);
       return hipGetLastError();
     };
-    if (rank_offsets == nullptr) return go(UniformRank{d.rank, d.heads});
-    return go(make_rank_table(rank_offsets, d.heads));
+    if (varlen != nullptr) return go(UniformRank{d.rank, d.heads}, *varlen);
+    if (rank_offsets == nullptr) return go(UniformRank{d.rank, d.heads}, Lockstep{n});
+    return go(make_rank_table(rank_offsets, d.heads), Lockstep{n});
   });
 }
 

@@ -261,3 +261,26 @@ def test_rank_table_validation():
     st, msg = status_of(ssm.window_update_refresh_ranked, d, [0, 2, 5, 9], p[0], p[0] + 2 * 3 * 32 * 64 * 4 - 16,
                         *p[2:7], 1)
     assert st == 5 and "overlaps" in msg
+
+
+def test_varlen_validation():
+    p = addrs(16)
+    d = dims(batch=4)
+    # 4 rows, 2 slots, no slot map: rejected
+    st, msg = status_of(ssm.window_update_refresh_varlen, d, 2, None, p[0], *p[1:9])
+    assert st == 2 and "slot map" in msg
+    st, msg = status_of(ssm.window_update_refresh_varlen, d, 0, p[9], p[0], *p[1:9])
+    assert st == 2 and "num_slots" in msg
+    st, msg = status_of(ssm.sketch_decode_step_varlen, d, 8, None, None, *p[1:9])
+    assert st == 1 and "tau" in msg
+    # count arrays need 4-byte alignment only; state needs 16
+    st, msg = status_of(ssm.window_update_refresh_varlen, d, 8, p[9] + 4, p[10] + 8, p[1] + 4, *p[2:9])
+    assert st == 3 and "state" in msg
+    # persistent arrays are sized by the pool: a sketch inside an 8-slot state overlaps it
+    st, msg = status_of(ssm.window_update_refresh_varlen, d, 8, p[9], p[10], p[1],
+                        p[1] + 8 * 3 * 32 * 64 * 4 - 64, *p[3:9])
+    assert st == 5 and "state overlaps sketch" in msg
+    # y may not overlap the tau array
+    st, msg = status_of(ssm.sketch_decode_step_varlen, d, 8, p[9], p[10], p[1], p[2], p[3],
+                        p[4], p[5], p[6], p[7], p[10])
+    assert st == 5

@@ -271,3 +271,94 @@ def test_per_head_ranks_average_8_workload():
     cfg = workloads.C3.with_(steps=24)
     H.note("case per-head ranks c3 (sampled units)")
     _ranked_case(cfg, workloads.average_rank_8(cfg.heads))
+
+
+@pytest.mark.parametrize("rule", ["mamba2", "gdn", "kda"])
+def test_continuous_batching_varlen(rule):
+    """Sequences join at different steps into permuted pool slots, each at its own window
+    position; a padding row (tau = 0) is skipped and its output left untouched; update calls
+    skip rows whose window is not full (n_tokens = -1). Every sequence is checked against its
+    own oracle run over its local steps."""
+    import oracle
+    W, T = 4, 14
+    joins = [0, 1, 2, 3, 5, 6]
+    slots = [5, 0, 7, 2, 3, 6]
+    P = 8                                      # pool size
+    cfg = small(rule, d_k=64, d_v=64, W=W, r=8, N=len(joins), Hh=3, T=T)
+    H.note(f"case continuous batching {rule}")
+    Hh, dk, dv = cfg.heads, cfg.d_k, cfg.d_v
+    S0 = np.concatenate([workloads.initial_state(cfg, [n]) for n in range(len(joins))])
+    B = workloads.basis(cfg)
+    steps = [workloads.step_inputs(cfg, j) for j in range(T)]   # local step j, row n = sequence n
+    d_pool = H.dims_of(cfg.with_(batch=P))
+    dev = "cuda"
+    tin = torch.bfloat16
+
+    def td(x):
+        return None if x is None else H._to_dev(np.ascontiguousarray(x), dev)
+
+    state = torch.zeros((P, Hh, dk, dv), device=dev)
+    sketch = torch.zeros((P, Hh, cfg.rank, dv), device=dev)
+    kb = torch.zeros((P, Hh, W, dk), device=dev, dtype=tin)
+    vb = torch.zeros((P, Hh, W, dv), device=dev, dtype=tin)
+    dshape = (P, Hh, W, dk) if rule == "kda" else (P, Hh, W)
+    db = torch.zeros(dshape, device=dev)
+    bb = torch.zeros((P, Hh, W), device=dev) if rule != "mamba2" else None
+    basis = td(B)
+    got_y = {n: [] for n in range(len(joins))}
+    sentinel = 777.0
+    for t in range(T):
+        joining = [n for n in range(len(joins)) if joins[n] == t]
+        for n in joining:
+            state[slots[n]] = torch.from_numpy(S0[n]).to(dev)
+        if joining:   # refresh-only pass for the sequences that just joined
+            dj = cfg.with_(batch=len(joining))
+            ssm.window_update_refresh_varlen(
+                H.dims_of(dj), P, td(np.array([slots[n] for n in joining], np.int32)),
+                td(np.zeros(len(joining), np.int32)), state, sketch, basis, kb, vb, db, bb)
+        active = [n for n in range(len(joins)) if joins[n] <= t][::-1]   # reversed row order
+        rows = active + [None]                                          # + one padding row
+        tau = [((t - joins[n]) % W) + 1 if n is not None else 0 for n in rows]
+        slot_rows = [slots[n] if n is not None else 1 for n in rows]
+        pick = lambda x, n: x[n] if n is not None else np.zeros_like(x[0])
+        loc = lambda n: t - joins[n] if n is not None else 0
+        q = np.stack([pick(steps[loc(n)].q, n) for n in rows])
+        k = np.stack([pick(steps[loc(n)].k, n) for n in rows])
+        v = np.stack([pick(steps[loc(n)].v, n) for n in rows])
+        dc = np.stack([pick(steps[loc(n)].decay, n) for n in rows])
+        bt = (np.stack([pick(steps[loc(n)].beta, n) for n in rows]) if rule != "mamba2" else None)
+        dr = H.dims_of(cfg.with_(batch=len(rows)))
+        y = torch.full((len(rows), Hh, dv), sentinel, device=dev)
+        ssm.sketch_decode_step_varlen(dr, P, td(np.array(slot_rows, np.int32)),
+                                      td(np.array(tau, np.int32)), sketch, basis, td(q), kb, vb,
+                                      db, bb, y, k_t=td(k), v_t=td(v), decay_t=td(dc),
+                                      beta_t=td(bt))
+        yc = y.cpu().double().numpy()
+        assert (yc[-1] == sentinel).all(), "padding row was written"
+        for i, n in enumerate(active):
+            got_y[n].append(yc[i])
+        # windows that just filled: update them; the others are skipped with n_tokens = -1
+        ntok = np.array([W if tau[i] == W else -1 for i in range(len(active))], np.int32)
+        ssm.window_update_refresh_varlen(H.dims_of(cfg.with_(batch=len(active))), P,
+                                         td(np.array(slot_rows[:-1], np.int32)), td(ntok),
+                                         state, sketch, basis, kb, vb, db, bb)
+    torch.cuda.synchronize()
+    for n in range(len(joins)):
+        Tn = T - joins[n]
+        wid = lambda x, e: x.reshape((cfg.batch, Hh) + ((e,) if e else ()))[n]
+        hq = np.stack([workloads.widen(wid(steps[j].q, dk)) for j in range(Tn)])
+        hk = np.stack([workloads.widen(wid(steps[j].k, dk)) for j in range(Tn)])
+        hv = np.stack([workloads.widen(wid(steps[j].v, dv)) for j in range(Tn)])
+        hd = np.stack([wid(steps[j].decay, dk if rule == "kda" else 0) for j in range(Tn)]).astype(np.float64)
+        hb = (np.stack([wid(steps[j].beta, 0) for j in range(Tn)]).astype(np.float64)
+              if rule != "mamba2" else None)
+        ref = oracle.run(rule, S0[n].astype(np.float64), B.astype(np.float64), hq, hk, hv, hd, hb, W)
+        e = H.rel_rows(np.stack(got_y[n]), ref["y_sketch"])
+        assert e.max() <= H.Y_TOL, f"sequence {n}: sketch read {e.max():.3e}"
+        nw = Tn // W
+        gS = state[slots[n]].cpu().double().numpy()
+        assert H.rel_mats(gS[None], ref["S_win"][nw][None]).max() <= H.S_TOL, f"sequence {n}: state"
+        gK = sketch[slots[n]].cpu().double().numpy()
+        assert H.rel_mats(gK[None], ref["Sk"][nw][None]).max() <= H.S_TOL, f"sequence {n}: sketch"
+    # slot 4 and 1 were never assigned to a sequence: untouched
+    assert torch.count_nonzero(state[4]) == 0 and torch.count_nonzero(state[1]) == 0
