@@ -70,3 +70,21 @@ def test_planted_mistake_is_caught(name, old, new, tmp_path):
         except AssertionError as e:
             failures.append(f"{pin.__name__}: {e}")
     assert failures, f"planted mistake {name!r} passed every pin"
+
+
+def test_oracle_reproduces_c1_fixture(oracle_lib):
+    """Regression: the oracle still computes what tests/golden/c1_oracle.json recorded."""
+    import json
+    import os
+    from tests.golden.make_golden import c1_problem
+    fx = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "c1_oracle.json")))
+    cfg, S0, B, q, k, v, dc = c1_problem()
+    out = oracle.run(cfg.rule, S0, B, q, k, v, dc, None, cfg.window, _lib_override=oracle_lib)
+    sel = lambda y: y[[3, 15]][:, [0, 7]]
+    np.testing.assert_allclose(np.linalg.norm(out["y_exact"], axis=-1), fx["y_exact_norms"], rtol=1e-12)
+    np.testing.assert_allclose(np.linalg.norm(out["y_sketch"], axis=-1), fx["y_sketch_norms"], rtol=1e-12)
+    np.testing.assert_allclose(sel(out["y_exact"]), fx["y_exact_t3_t15_u0_u7"], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(sel(out["y_sketch"]), fx["y_sketch_t3_t15_u0_u7"], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(out["Sk"][-1][0], fx["Sk_last_u0"], rtol=1e-12, atol=1e-15)
+    fro = np.linalg.norm(out["S_win"].reshape(out["S_win"].shape[0], -1), axis=1)
+    np.testing.assert_allclose(fro, fx["S_win_frobenius"], rtol=1e-12)

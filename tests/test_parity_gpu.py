@@ -42,6 +42,9 @@ SMALL = [
     small("gdn", "f32", d_k=64, d_v=64, W=4, r=16), small("kda", "f32", d_k=128, d_v=32, W=6, r=8),
     small("mamba2", "f32", d_k=16, d_v=64, W=3, r=16),
     small("gdn", N=7, Hh=9, W=8, r=8),   # 63 units: a ragged last wave of the sketch read
+    # the largest supported shapes: LDS and registers at their maximum
+    small("kda", "f32", d_k=128, d_v=128, W=16, r=32, N=2, Hh=3, T=35),
+    small("gdn", "bf16", d_k=128, d_v=128, W=16, r=32, N=2, Hh=3, T=33),
 ]
 
 
@@ -362,3 +365,31 @@ def test_continuous_batching_varlen(rule):
         assert H.rel_mats(gK[None], ref["Sk"][nw][None]).max() <= H.S_TOL, f"sequence {n}: sketch"
     # slot 4 and 1 were never assigned to a sequence: untouched
     assert torch.count_nonzero(state[4]) == 0 and torch.count_nonzero(state[1]) == 0
+
+
+def test_checkpoint_mid_window_and_resume():
+    """A mid-window checkpoint (state, sketch, window buffer) restored into fresh memory
+    continues bitwise identically to the uninterrupted run."""
+    cfg = small("gdn", W=8, T=20)
+    H.note("case checkpoint / resume")
+    inp = H.Inputs(cfg, np.arange(cfg.units), cfg.steps)
+    d = H.dims_of(cfg)
+    a = WindowedDecoder(d, inp.S0.clone(), inp.basis, read="sketch")
+    a.refresh()
+    ya = []
+    cut = 11   # three tokens into the second window
+    b = None
+    for t in range(cfg.steps):
+        if t == cut:
+            b = WindowedDecoder(d, a.state.clone(), inp.basis, read="sketch")
+            for name in ("sketch", "k_buf", "v_buf", "decay_buf", "beta_buf"):
+                getattr(b, name).copy_(getattr(a, name))
+            b.tau = a.tau
+            yb = []
+        ya.append(a.step(inp.q[t], inp.k[t], inp.v[t], inp.decay[t], inp.beta[t]).clone())
+        if b is not None:
+            yb.append(b.step(inp.q[t], inp.k[t], inp.v[t], inp.decay[t], inp.beta[t]).clone())
+    torch.cuda.synchronize()
+    for i, y in enumerate(yb):
+        assert torch.equal(y, ya[cut + i]), f"step {cut + i}"
+    assert torch.equal(a.state, b.state) and torch.equal(a.sketch, b.sketch)
