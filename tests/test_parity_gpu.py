@@ -393,3 +393,35 @@ def test_checkpoint_mid_window_and_resume():
     for i, y in enumerate(yb):
         assert torch.equal(y, ya[cut + i]), f"step {cut + i}"
     assert torch.equal(a.state, b.state) and torch.equal(a.sketch, b.sketch)
+
+
+@pytest.mark.parametrize("rule", ["mamba2", "gdn", "kda"])
+def test_extreme_gates(rule):
+    """Exact zero gates (they clear everything before them), gates of 1, beta of 0 and 1,
+    and a large-magnitude state: the suffix-product update and the walk match the oracle."""
+    cfg = small(rule, N=3, Hh=4, W=4, T=12)
+    H.note(f"case extreme gates {rule}")
+    inp = H.Inputs(cfg, np.arange(cfg.units), cfg.steps)
+    U = cfg.units
+    rng = np.random.default_rng(7)
+    for t in range(cfg.steps):
+        dec = inp.decay[t].clone().view(U, -1)
+        pick = rng.integers(0, 4, size=U)
+        dec[torch.as_tensor(pick == 0, device="cuda")] = 0.0
+        dec[torch.as_tensor(pick == 1, device="cuda")] = 1.0
+        inp.decay[t] = dec.view_as(inp.decay[t])
+        hd = inp.host["decay"][t].reshape(U, -1)
+        hd[pick == 0] = 0.0
+        hd[pick == 1] = 1.0
+        if inp.beta[t] is not None:
+            bsel = rng.integers(0, 3, size=U)
+            b = inp.beta[t].clone().view(U)
+            b[torch.as_tensor(bsel == 0, device="cuda")] = 0.0
+            b[torch.as_tensor(bsel == 1, device="cuda")] = 1.0
+            inp.beta[t] = b.view_as(inp.beta[t])
+            hb = inp.host["beta"][t]
+            hb[bsel == 0] = 0.0
+            hb[bsel == 1] = 1.0
+    inp.S0 = inp.S0 * 1e3
+    inp.host_S0 = inp.host_S0 * 1e3
+    H.compare(cfg, H.run_gpu(cfg, inp), H.run_oracle(cfg, inp))
