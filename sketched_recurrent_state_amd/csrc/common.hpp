@@ -3,9 +3,12 @@
 // Lane layouts used by the kernels:
 //  * state tile ("tile"): one workgroup per (sequence, head) unit, one wave per
 //    32-column block of the d_k x d_v state. Lane l owns 4 adjacent columns
-//    (cg = l % 8, one 128-bit load per row) of d_k/8 contiguous rows
-//    (rg = l / 8). A reduction over d_k is a sum over the 8 lanes that share
-//    cg, i.e. over lane bits 3, 4 and 5: DPP row_ror:8 for bit 3 and the
+//    (cg = l % 8, one 128-bit load per row, so 8 lanes cover a full 128-byte
+//    line) of d_k/8 rows (rg = l / 8): contiguous rows rg*d_k/8 ... in the
+//    read kernels, interleaved rows rg, rg + 8, rg + 16, ... in the window
+//    update (its 4 waves then cover 8 whole rows, 4 KB of contiguous memory,
+//    per load instruction). A reduction over d_k is a sum over the 8 lanes that
+//    share cg, i.e. over lane bits 3, 4 and 5: DPP row_ror:8 for bit 3 and the
 //    gfx950 permlane16/permlane32 swaps for bits 4 and 5.
 //  * group: G = 16 or 32 consecutive lanes per unit, each holding d_k/G key
 //    elements and d_v/G value elements; reductions are DPP row operations plus,
@@ -350,10 +353,20 @@ __host__ __device__ inline int window_lds_floats(int n) {
   return n * DK + n * DV + pad4(n * DSTR) + ((RULE == MAMBA2) ? 0 : pad4(n));
 }
 
+// Position in LDS of d_k index i for the interleaved row layout (lane group
+// g owns rows g, g + 8, g + 16, ...): group g's d_k / 8 values are stored
+// contiguously so each lane reads them with vector loads.
+template <int DK>
+__host__ __device__ __forceinline__ int interleaved_pos(int i) {
+  return (i & 7) * (DK / 8) + (i >> 3);
+}
+
 // Cooperative copy by the NT threads of a workgroup. With a fused append the
 // newest slot (n - 1) is read from the current token and also written into
-// the buffer. The caller synchronises the workgroup before reading the LDS.
-template <int RULE, int DK, int DV, typename TIN, int NT>
+// the buffer. With PERM the d_k-indexed rows (keys, and KDA's per-row gates)
+// are stored in interleaved_pos order. The caller synchronises the workgroup
+// before reading the LDS.
+template <int RULE, int DK, int DV, typename TIN, int NT, bool PERM = false>
 __device__ __forceinline__ void stage_window(float* lds, const UnitWindow<TIN>& uw, int n,
                                              int tid) {
   constexpr int DSTR = (RULE == KDA) ? DK : 1;
@@ -371,7 +384,13 @@ __device__ __forceinline__ void stage_window(float* lds, const UnitWindow<TIN>& 
     if (cur) x.store(uw.k + e);
     float f[VIN];
     x.unpack(f);
-    Vec<float, VIN>::store(lk + e, f);
+    if constexpr (PERM) {
+      const int t0 = e - e % DK, i0 = e % DK;
+#pragma unroll
+      for (int j = 0; j < VIN; ++j) lk[t0 + interleaved_pos<DK>(i0 + j)] = f[j];
+    } else {
+      Vec<float, VIN>::store(lk + e, f);
+    }
   }
   for (int e = tid * VIN; e < n * DV; e += NT * VIN) {
     const bool cur = fused && (e / DV == last);
@@ -386,7 +405,10 @@ __device__ __forceinline__ void stage_window(float* lds, const UnitWindow<TIN>& 
     const bool cur = fused && (e / DSTR == last);
     const float x = cur ? uw.dt[e - last * DSTR] : uw.d[e];
     if (cur) uw.d[e] = x;
-    ld[e] = x;
+    if constexpr (PERM && RULE == KDA)
+      ld[e - e % DK + interleaved_pos<DK>(e % DK)] = x;
+    else
+      ld[e] = x;
   }
   if constexpr (RULE != MAMBA2) {
     for (int e = tid; e < n; e += NT) {

@@ -238,7 +238,7 @@ full_read_kernel(const float* __restrict__ state, const TIN* __restrict__ q,
   const float* lb = ld + pad4(tau * DSTR);
 
   float4 acc = f4(0.f);
-#pragma unroll 2
+#pragma unroll 1  // the walk holds cross-lane (convergent) reductions
   for (int i = tau - 1; i >= 0; --i) {
     float kk[RPL], a[EA];
     Vec<float, RPL>::load(lk + i * DK + row0, kk);

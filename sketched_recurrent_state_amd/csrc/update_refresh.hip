@@ -11,6 +11,13 @@
 // piece of S in VGPRs for the whole window: S is read from HBM once and
 // written once. The window's keys, values and gates (and the head's basis) are
 // staged in LDS as fp32 so every wave reads them without touching HBM again.
+//
+// Memory order: lane group rg owns the interleaved rows rg, rg + 8, ... so each
+// load instruction of the workgroup covers 8 whole rows of S (contiguous), and
+// consecutive units go to the same XCD (workgroups are dealt to the 8 XCDs in
+// turn; the block index is remapped so each XCD streams one contiguous run of
+// units). Together these move S about 5% faster than contiguous rows per lane
+// with the natural block order.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -32,15 +39,21 @@ update_refresh_kernel(float* __restrict__ state, float* __restrict__ sketch,
   extern __shared__ float4 lds4[];
   float* lds = reinterpret_cast<float*>(lds4);
 
-  const int head = blockIdx.x % heads;
+  // XCD x = blockIdx.x % 8 receives blocks x, x + 8, ...: give it the contiguous
+  // run of units [x * q8 + min(x, rem), ...) instead (a bijection on the grid).
+  const int G = gridDim.x, xcd = blockIdx.x & 7, q8 = G >> 3, rem = G & 7;
+  const int b = xcd * q8 + min(xcd, rem) + (blockIdx.x >> 3);
+  const int head = b % heads;
   int seq = 0, n = 0;  // the batch row's persistent slot and its number of buffered tokens
-  if (!rm.row(blockIdx.x / heads, seq, n)) return;  // whole workgroup: a skipped row
+  if (!rm.row(b / heads, seq, n)) return;  // whole workgroup: a skipped row
   const size_t unit = (size_t)seq * heads + head;
   const int rank = rt.rank(head);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int cg = lane & 7, rg = lane >> 3;
   const int col = wave * 32 + cg * 4;
+  // s[m] holds row m * 8 + rg of S; the LDS copies of keys, gates and basis
+  // keep this lane's d_k / 8 values at [row0, row0 + RPL) (interleaved_pos).
   const int row0 = rg * RPL;
 
   // 1. issue the loads of this lane's state piece (the only HBM read of S)
@@ -48,7 +61,7 @@ update_refresh_kernel(float* __restrict__ state, float* __restrict__ sketch,
   float4 s[RPL];
 #pragma unroll
   for (int m = 0; m < RPL; ++m)
-    s[m] = load_stream(Su + (size_t)(row0 + m) * DV + col);
+    s[m] = load_stream(Su + (size_t)(m * 8 + rg) * DV + col);
 
   // 2. stage the window (and the basis) in LDS as fp32
   const size_t slot0 = (size_t)unit * window;
@@ -56,7 +69,7 @@ update_refresh_kernel(float* __restrict__ state, float* __restrict__ sketch,
                      const_cast<float*>(dbuf) + slot0 * DSTR,
                      (RULE == MAMBA2) ? nullptr : const_cast<float*>(bbuf) + slot0,
                      nullptr, nullptr, nullptr, nullptr};
-  if (n > 0) stage_window<RULE, DK, DV, TIN, NT>(lds, uw, n, tid);
+  if (n > 0) stage_window<RULE, DK, DV, TIN, NT, true>(lds, uw, n, tid);
   const float* lk = lds;
   const float* lv = lk + n * DK;
   const float* ld = lv + n * DV;
@@ -64,19 +77,23 @@ update_refresh_kernel(float* __restrict__ state, float* __restrict__ sketch,
   float* lB = lds + window_lds_floats<RULE, DK, DV>(n);  // [rank][DK]
   if (sketch != nullptr) {
     const float* Bh = basis + (size_t)rt.offset(head) * DK;
-    for (int e = tid * 4; e < rank * DK; e += NT * 4)
-      *reinterpret_cast<float4*>(lB + e) = *reinterpret_cast<const float4*>(Bh + e);
+    for (int e = tid * 4; e < rank * DK; e += NT * 4) {
+      const float4 x4 = *reinterpret_cast<const float4*>(Bh + e);
+      float* row = lB + (e - e % DK);
+      const int i0 = e % DK;
+      row[interleaved_pos<DK>(i0)] = x4.x;
+      row[interleaved_pos<DK>(i0 + 1)] = x4.y;
+      row[interleaved_pos<DK>(i0 + 2)] = x4.z;
+      row[interleaved_pos<DK>(i0 + 3)] = x4.w;
+    }
   }
   __syncthreads();
 
   // 3. the window's tokens, in order: S <- M_t S + b_t k_t v_t^T on the
   //    register-resident piece; the k^T S reduction over d_k crosses the 8
-  //    lanes that share this lane's columns.
-  //    Mamba-2 and GDN decay the whole state by one scalar per token, so the
-  //    piece is kept as S = sigma * St: the decay multiplies sigma and each
-  //    token costs one FMA per element (St += k (w / sigma)^T) instead of a
-  //    multiply and an FMA. KDA decays rows by different gates and updates S
-  //    directly.
+  //    lanes that share this lane's columns. Mamba-2 and GDN carry a scaled
+  //    copy of the piece so the per-token decay costs nothing (below); KDA
+  //    decays rows by different gates and updates S directly.
   // 4. write the state back (the only HBM write of S), then
   // 5. refresh the sketch from the register-resident state: Sk[m] = S^T b_m.
   //    Eight basis rows at a time; the d_k reduction is a reduce-scatter over
@@ -85,7 +102,7 @@ update_refresh_kernel(float* __restrict__ state, float* __restrict__ sketch,
     if (n > 0) {
 #pragma unroll
       for (int m = 0; m < RPL; ++m)
-        store_stream(Su + (size_t)(row0 + m) * DV + col, s[m]);
+        store_stream(Su + (size_t)(m * 8 + rg) * DV + col, s[m]);
     }
     if (sketch == nullptr) return;
     float* Sku = sketch + ((size_t)seq * rt.total() + rt.offset(head)) * DV;
@@ -187,7 +204,7 @@ update_refresh_kernel(float* __restrict__ state, float* __restrict__ sketch,
 
 size_t update_refresh_lds_bytes(const ssm_dims& d, int n, int max_rank) {
   size_t floats = 0;
-  dispatch(d.rule, SSM_IN_F32, d.d_k, d.d_v, [&](auto R, auto DK, auto DV, auto) {
+  (void)dispatch(d.rule, SSM_IN_F32, d.d_k, d.d_v, [&](auto R, auto DK, auto DV, auto) {
     floats = (size_t)window_lds_floats<decltype(R)::value, decltype(DK)::value,
                                        decltype(DV)::value>(n);
     return hipSuccess;
