@@ -29,7 +29,8 @@
  * Memory layouts (row-major, every pointer a DEVICE pointer owned by the
  * caller; the library keeps no pointer after a call returns):
  *   state   S   fp32  [N][H][d_k][d_v]
- *   sketch  Sk  fp32  [N][H][r][d_v]     row m = S^T b_m (the output for basis vector b_m)
+ *   sketch  Sk  fp32 or bf16 (ssm_dims.sketch_dtype)  [N][H][r][d_v]
+ *                                        row m = S^T b_m (the output for basis vector b_m)
  *   basis   B   fp32  [H][r][d_k]        row m = b_m; rows orthonormal (not checked)
  *   k_buf       in    [N][H][W][d_k]     window buffer, slot i = token i+1 of the window
  *   v_buf       in    [N][H][W][d_v]
@@ -64,10 +65,14 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 1
+#define SSM_ABI_VERSION 2
 
 typedef enum { SSM_MAMBA2 = 0, SSM_GDN = 1, SSM_KDA = 2 } ssm_rule;
 typedef enum { SSM_IN_BF16 = 0, SSM_IN_F32 = 1 } ssm_in_dtype;
+/* Storage type of the sketch. The pages leave its precision open: fp32 is the
+ * default; bf16 halves the sketch bytes every decode step reads. A bf16 sketch
+ * is computed in fp32 and rounded to nearest, ties to even, when it is stored. */
+typedef enum { SSM_SKETCH_F32 = 0, SSM_SKETCH_BF16 = 1 } ssm_sketch_dtype;
 
 typedef enum {
   SSM_OK = 0,
@@ -89,6 +94,7 @@ typedef struct {
   int32_t d_v;       /* value / state columns             */
   int32_t window;    /* W buffered tokens per state write */
   int32_t rank;      /* r basis vectors (sketch rows)     */
+  int32_t sketch_dtype; /* ssm_sketch_dtype of the sketch (0: fp32) */
 } ssm_dims;
 
 /* SSM_ABI_VERSION of the library. */
@@ -128,7 +134,7 @@ ssm_status ssm_buffer_append(const ssm_dims* d,
  * Outputs: state (in/out), sketch. Inputs: basis, the buffers.
  */
 ssm_status ssm_window_update_refresh(const ssm_dims* d,
-                                     float* state, float* sketch, const float* basis,
+                                     float* state, void* sketch, const float* basis,
                                      const void* k_buf, const void* v_buf,
                                      const float* decay_buf, const float* beta_buf,
                                      int32_t n_tokens, void* stream);
@@ -150,7 +156,7 @@ ssm_status ssm_window_update_refresh(const ssm_dims* d,
  * Output: y. The sketch and the state are never written.
  */
 ssm_status ssm_sketch_decode_step(const ssm_dims* d,
-                                  const float* sketch, const float* basis, const void* q,
+                                  const void* sketch, const float* basis, const void* q,
                                   const void* k_t, const void* v_t,
                                   const float* decay_t, const float* beta_t,
                                   void* k_buf, void* v_buf, float* decay_buf, float* beta_buf,
@@ -178,19 +184,19 @@ ssm_status ssm_full_read_decode_step(const ssm_dims* d,
  * 1 <= r_h <= min(d_k, 32), rank_offsets[0] = 0, H <= 256; the array is read
  * during the call only. With R = rank_offsets[H]:
  *   basis   fp32 [R][d_k]       rows rank_offsets[h] .. +r_h are head h's basis
- *   sketch  fp32 [N][R][d_v]    rows rank_offsets[h] .. +r_h of sequence n are
+ *   sketch  [N][R][d_v] (fp32 or bf16) rows rank_offsets[h] .. +r_h of sequence n are
  *                               the outputs of head h's basis vectors
  * d->rank must still be a valid rank (the table decides the sizes). Every other
  * argument and behaviour is that of the uniform-rank entry point.
  */
 ssm_status ssm_window_update_refresh_ranked(const ssm_dims* d, const int32_t* rank_offsets,
-                                            float* state, float* sketch, const float* basis,
+                                            float* state, void* sketch, const float* basis,
                                             const void* k_buf, const void* v_buf,
                                             const float* decay_buf, const float* beta_buf,
                                             int32_t n_tokens, void* stream);
 
 ssm_status ssm_sketch_decode_step_ranked(const ssm_dims* d, const int32_t* rank_offsets,
-                                         const float* sketch, const float* basis, const void* q,
+                                         const void* sketch, const float* basis, const void* q,
                                          const void* k_t, const void* v_t,
                                          const float* decay_t, const float* beta_t,
                                          void* k_buf, void* v_buf, float* decay_buf,
@@ -218,14 +224,14 @@ ssm_status ssm_sketch_decode_step_ranked(const ssm_dims* d, const int32_t* rank_
  */
 ssm_status ssm_window_update_refresh_varlen(const ssm_dims* d, int32_t num_slots,
                                             const int32_t* slot, const int32_t* n_tokens,
-                                            float* state, float* sketch, const float* basis,
+                                            float* state, void* sketch, const float* basis,
                                             const void* k_buf, const void* v_buf,
                                             const float* decay_buf, const float* beta_buf,
                                             void* stream);
 
 ssm_status ssm_sketch_decode_step_varlen(const ssm_dims* d, int32_t num_slots,
                                          const int32_t* slot, const int32_t* tau,
-                                         const float* sketch, const float* basis, const void* q,
+                                         const void* sketch, const float* basis, const void* q,
                                          const void* k_t, const void* v_t,
                                          const float* decay_t, const float* beta_t,
                                          void* k_buf, void* v_buf, float* decay_buf,

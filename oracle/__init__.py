@@ -40,7 +40,9 @@ def _load(path: str = LIB_PATH):
     lib = ctypes.CDLL(path)
     dp = ctypes.POINTER(ctypes.c_double)
     lib.oracle_run.restype = ctypes.c_int
-    lib.oracle_run.argtypes = [ctypes.c_int] * 7 + [dp] * 14 + [ctypes.c_int]
+    lib.oracle_run.argtypes = [ctypes.c_int] * 7 + [dp] * 14 + [ctypes.c_int] * 2
+    lib.oracle_round_bf16.restype = ctypes.c_double
+    lib.oracle_round_bf16.argtypes = [ctypes.c_double]
     lib.oracle_rule_step.restype = ctypes.c_int
     lib.oracle_rule_step.argtypes = [ctypes.c_int] * 3 + [dp] * 4 + [ctypes.c_double]
     lib.oracle_transition_matrix.restype = None
@@ -100,7 +102,7 @@ def rule_step(rule: str, S, k, v, decay, beta: float = 0.0, _lib_override=None):
 
 
 def run(rule: str, S0, basis, q, k, v, decay, beta, window: int, *,
-        want_A: bool = False, want_R: bool = False, threads: int = 0,
+        want_A: bool = False, want_R: bool = False, sketch_bf16: bool = False, threads: int = 0,
         _lib_override=None) -> dict:
     """Run T decode steps for U independent units.
 
@@ -108,7 +110,8 @@ def run(rule: str, S0, basis, q, k, v, decay, beta, window: int, *,
     decay [T][U] or [T][U][dk]; beta [T][U] (None for Mamba-2).
     Returns y_exact, y_replay, y_sketch [T][U][dv]; S_win, Sk [T//W + 1][U][...]
     (window-start states and sketches) and, if asked, A [T][U][dk][dk] and
-    R [T][U][dk][dv].
+    R [T][U][dk][dv]. sketch_bf16: the stored sketch is rounded as a bf16 store
+    rounds it (to fp32, then to nearest bf16, ties to even) before it is read.
     """
     L = _lib_override or lib()
     S0, basis, q, k, v, decay = map(_f64, (S0, basis, q, k, v, decay))
@@ -130,10 +133,15 @@ def run(rule: str, S0, basis, q, k, v, decay, beta, window: int, *,
                       _ptr(S0), _ptr(basis), _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(beta),
                       _ptr(out["y_exact"]), _ptr(out["y_replay"]), _ptr(out["y_sketch"]),
                       _ptr(out["S_win"]), _ptr(out["Sk"]), _ptr(out["A"]), _ptr(out["R"]),
-                      int(threads))
+                      int(bool(sketch_bf16)), int(threads))
     if rc:
         raise RuntimeError("oracle_run failed")
     return out
+
+
+def round_bf16(x: float, _lib_override=None) -> float:
+    """x rounded as a bf16 store rounds it (to fp32, then to nearest bf16, ties to even)."""
+    return float((_lib_override or lib()).oracle_round_bf16(float(x)))
 
 
 def max_threads() -> int:

@@ -35,10 +35,18 @@
  * "R" is the additive part of the window decomposition (often written B_t);
  * it is renamed so that it does not clash with the basis B.
  *
+ * Sketch storage. The pages do not fix the sketch's precision. With
+ * sketch_bf16 set, every stored sketch element is rounded as a bf16 store
+ * would round it: first to fp32 (the precision the sketch is computed in),
+ * then to the nearest bf16 (8 significant bits), ties to the even neighbour.
+ * y_sketch then reads the rounded sketch; nothing else changes.
+ *
  * Every matrix is formed densely and multiplied with plain loops, in fp64.
  * Parity is pinned by tests/test_oracle_pins.py (closed forms, invariants and
  * brute force on tiny inputs).
  */
+#include <math.h>
+#include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -127,6 +135,27 @@ int oracle_rule_step(int rule, int dk, int dv, double* S, const double* k, const
 
 /* ------------------------------------------------------------------------- */
 /* The windowed decode run                                                   */
+/* x as a bf16 store keeps it: rounded to fp32, then to the nearest value with
+ * 8 significant bits. Of the fp32 pattern, the high 16 bits are kept; the low
+ * 16 decide: above half of the kept unit rounds up, below rounds down, exactly
+ * half rounds to the neighbour whose kept pattern is even. Infinities stay;
+ * a NaN stays a NaN. */
+double oracle_round_bf16(double x) {
+  float f = (float)x;
+  if (isnan(f)) return x;
+  uint32_t u;
+  memcpy(&u, &f, sizeof(u));
+  uint32_t kept = u >> 16, dropped = u & 0xFFFFu;
+  if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) kept += 1u;
+  u = kept << 16;
+  memcpy(&f, &u, sizeof(f));
+  return (double)f;
+}
+
+static void round_sketch(size_t n, double* Sk) {
+  for (size_t i = 0; i < n; ++i) Sk[i] = oracle_round_bf16(Sk[i]);
+}
+
 /* ------------------------------------------------------------------------- */
 /*
  * rule      0 Mamba-2, 1 GDN, 2 KDA
@@ -145,6 +174,7 @@ int oracle_rule_step(int rule, int dk, int dv, double* S, const double* k, const
  * Sk_out    [T/W + 1][U][r][dv]   the sketch B S_win stored at each window start
  * A_out     [T][U][dk][dk]        A after each token (tiny shapes only)
  * R_out     [T][U][dk][dv]        R after each token (tiny shapes only)
+ * sketch_bf16  non-zero: the stored sketch is rounded as a bf16 store rounds it
  * nthreads  OpenMP threads (<= 0: runtime default)
  * Returns 0, or 1 on allocation failure / bad arguments.
  */
@@ -154,7 +184,7 @@ int oracle_run(int rule, int U, int dk, int dv, int r, int W, int T,
                const double* decay, const double* beta,
                double* y_exact, double* y_replay, double* y_sketch,
                double* S_out, double* Sk_out, double* A_out, double* R_out,
-               int nthreads) {
+               int sketch_bf16, int nthreads) {
   if (rule < 0 || rule > 2 || U < 0 || dk < 1 || dv < 1 || r < 1 || W < 1 || T < 0) return 1;
   if (rule != ORACLE_MAMBA2 && beta == NULL) return 1;
   const int dstride = (rule == ORACLE_KDA) ? dk : 1;
@@ -187,6 +217,7 @@ int oracle_run(int rule, int U, int dk, int dv, int r, int W, int T,
       for (int i = 0; i < dk; ++i) A[i * dk + i] = 1.0;
       for (size_t i = 0; i < sz_s; ++i) R[i] = 0.0;
       matmul(r, dk, dv, Bu, Swin, Sk);
+      if (sketch_bf16) round_sketch(sz_k, Sk);
       if (S_out) memcpy(S_out + (size_t)u * sz_s, Swin, sizeof(double) * sz_s);
       if (Sk_out) memcpy(Sk_out + (size_t)u * sz_k, Sk, sizeof(double) * sz_k);
       int tau = 0, win = 0;
@@ -226,6 +257,7 @@ int oracle_run(int rule, int U, int dk, int dv, int r, int W, int T,
         if (tau == W) { /* window end: write-back point of the full state, refresh */
           memcpy(Swin, S, sizeof(double) * sz_s);
           matmul(r, dk, dv, Bu, Swin, Sk);
+          if (sketch_bf16) round_sketch(sz_k, Sk);
           for (size_t i = 0; i < sz_a; ++i) A[i] = 0.0;
           for (int i = 0; i < dk; ++i) A[i * dk + i] = 1.0;
           for (size_t i = 0; i < sz_s; ++i) R[i] = 0.0;

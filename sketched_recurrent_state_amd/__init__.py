@@ -32,6 +32,7 @@ HEADER = os.path.join(os.path.dirname(_PKG), "include", "sketchssm.h")
 MAMBA2, GDN, KDA = 0, 1, 2
 RULES = {"mamba2": MAMBA2, "gdn": GDN, "kda": KDA}
 IN_BF16, IN_F32 = 0, 1
+SKETCH_F32, SKETCH_BF16 = 0, 1
 
 STATUS = {0: "SSM_OK", 1: "SSM_E_NULL", 2: "SSM_E_SHAPE", 3: "SSM_E_ALIGN", 4: "SSM_E_RANGE",
           5: "SSM_E_ALIAS", 6: "SSM_E_LAUNCH"}
@@ -45,18 +46,22 @@ class SSMError(RuntimeError):
 
 
 class Dims(ctypes.Structure):
-    """ssm_dims: rule, in_dtype, batch, heads, d_k, d_v, window, rank."""
+    """ssm_dims: rule, in_dtype, batch, heads, d_k, d_v, window, rank, sketch_dtype."""
 
     _fields_ = [(n, ctypes.c_int32) for n in
-                ("rule", "in_dtype", "batch", "heads", "d_k", "d_v", "window", "rank")]
+                ("rule", "in_dtype", "batch", "heads", "d_k", "d_v", "window", "rank",
+                 "sketch_dtype")]
 
     @classmethod
-    def make(cls, rule, in_dtype, batch, heads, d_k, d_v, window, rank) -> "Dims":
+    def make(cls, rule, in_dtype, batch, heads, d_k, d_v, window, rank,
+             sketch_dtype="f32") -> "Dims":
         if isinstance(rule, str):
             rule = RULES[rule]
         if isinstance(in_dtype, str):
             in_dtype = {"bf16": IN_BF16, "f32": IN_F32}[in_dtype]
-        return cls(rule, in_dtype, batch, heads, d_k, d_v, window, rank)
+        if isinstance(sketch_dtype, str):
+            sketch_dtype = {"f32": SKETCH_F32, "bf16": SKETCH_BF16}[sketch_dtype]
+        return cls(rule, in_dtype, batch, heads, d_k, d_v, window, rank, sketch_dtype)
 
     def __repr__(self):
         return "Dims(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -176,6 +181,14 @@ def _f32():
     return (torch.float32,)
 
 
+def _sk_types(d: Dims, f32):
+    """Dtype set of the sketch (None when only raw addresses are passed)."""
+    if f32 is None:
+        return None
+    import torch
+    return (torch.bfloat16,) if d.sketch_dtype == SKETCH_BF16 else (torch.float32,)
+
+
 def _check(status: int):
     if status != 0:
         raise SSMError(status, _lib.ssm_last_error().decode())
@@ -220,7 +233,7 @@ def window_update_refresh(d: Dims, state, sketch, basis, k_buf, v_buf, decay_buf
     tin, f32 = _types(d, (state, sketch, basis, k_buf, v_buf, decay_buf, beta_buf))
     n = numel(d)
     _check(_lib.ssm_window_update_refresh(
-        ctypes.byref(d), _addr(state, "state", f32, n["state"]), _addr(sketch, "sketch", f32, n["sketch"]),
+        ctypes.byref(d), _addr(state, "state", f32, n["state"]), _addr(sketch, "sketch", _sk_types(d, f32), n["sketch"]),
         _addr(basis, "basis", f32, n["basis"]), _addr(k_buf, "k_buf", tin, n["k_buf"]), _addr(v_buf, "v_buf", tin, n["v_buf"]),
         _addr(decay_buf, "decay_buf", f32, n["decay_buf"]), _addr(beta_buf, "beta_buf", f32, n["beta_buf"]),
         int(n_tokens), _stream(stream)))
@@ -236,7 +249,7 @@ def sketch_decode_step(d: Dims, sketch, basis, q, k_buf, v_buf, decay_buf, beta_
     tin, f32 = _types(d, (sketch, basis, q, k_buf, v_buf, decay_buf, beta_buf, y, k_t, v_t))
     n = numel(d)
     _check(_lib.ssm_sketch_decode_step(
-        ctypes.byref(d), _addr(sketch, "sketch", f32, n["sketch"]), _addr(basis, "basis", f32, n["basis"]),
+        ctypes.byref(d), _addr(sketch, "sketch", _sk_types(d, f32), n["sketch"]), _addr(basis, "basis", f32, n["basis"]),
         _addr(q, "q", tin, n["q"]), _addr(k_t, "k_t", tin, n["k_t"]), _addr(v_t, "v_t", tin, n["v_t"]),
         _addr(decay_t, "decay_t", f32, n["decay_t"]), _addr(beta_t, "beta_t", f32, n["beta_t"]),
         _addr(k_buf, "k_buf", tin, n["k_buf"]), _addr(v_buf, "v_buf", tin, n["v_buf"]),
@@ -316,7 +329,7 @@ def window_update_refresh_ranked(d: Dims, offsets, state, sketch, basis, k_buf, 
     n = _ranked_numel(d, off)
     _check(_lib.ssm_window_update_refresh_ranked(
         ctypes.byref(d), off, _addr(state, "state", f32, n["state"]),
-        _addr(sketch, "sketch", f32, n["sketch"]), _addr(basis, "basis", f32, n["basis"]),
+        _addr(sketch, "sketch", _sk_types(d, f32), n["sketch"]), _addr(basis, "basis", f32, n["basis"]),
         _addr(k_buf, "k_buf", tin, n["k_buf"]), _addr(v_buf, "v_buf", tin, n["v_buf"]),
         _addr(decay_buf, "decay_buf", f32, n["decay_buf"]),
         _addr(beta_buf, "beta_buf", f32, n["beta_buf"]), int(n_tokens), _stream(stream)))
@@ -335,7 +348,7 @@ def sketch_decode_step_ranked(d: Dims, offsets, sketch, basis, q, k_buf, v_buf, 
     tin, f32 = _types(d, (sketch, basis, q, k_buf, v_buf, decay_buf, beta_buf, y, k_t, v_t))
     n = _ranked_numel(d, off)
     _check(_lib.ssm_sketch_decode_step_ranked(
-        ctypes.byref(d), off, _addr(sketch, "sketch", f32, n["sketch"]),
+        ctypes.byref(d), off, _addr(sketch, "sketch", _sk_types(d, f32), n["sketch"]),
         _addr(basis, "basis", f32, n["basis"]), _addr(q, "q", tin, n["q"]),
         _addr(k_t, "k_t", tin, n["k_t"]), _addr(v_t, "v_t", tin, n["v_t"]),
         _addr(decay_t, "decay_t", f32, n["decay_t"]), _addr(beta_t, "beta_t", f32, n["beta_t"]),
@@ -376,7 +389,7 @@ def window_update_refresh_varlen(d: Dims, num_slots: int, slot, n_tokens, state,
     _check(_lib.ssm_window_update_refresh_varlen(
         ctypes.byref(d), int(num_slots), _addr(slot, "slot", i32, n["rows"]),
         _addr(n_tokens, "n_tokens", i32, n["rows"]), _addr(state, "state", f32, n["state"]),
-        _addr(sketch, "sketch", f32, n["sketch"]), _addr(basis, "basis", f32, n["basis"]),
+        _addr(sketch, "sketch", _sk_types(d, f32), n["sketch"]), _addr(basis, "basis", f32, n["basis"]),
         _addr(k_buf, "k_buf", tin, n["k_buf"]), _addr(v_buf, "v_buf", tin, n["v_buf"]),
         _addr(decay_buf, "decay_buf", f32, n["decay_buf"]),
         _addr(beta_buf, "beta_buf", f32, n["beta_buf"]), _stream(stream)))
@@ -396,7 +409,7 @@ def sketch_decode_step_varlen(d: Dims, num_slots: int, slot, tau, sketch, basis,
     n = _pool_numel(d, num_slots)
     _check(_lib.ssm_sketch_decode_step_varlen(
         ctypes.byref(d), int(num_slots), _addr(slot, "slot", i32, n["rows"]),
-        _addr(tau, "tau", i32, n["rows"]), _addr(sketch, "sketch", f32, n["sketch"]),
+        _addr(tau, "tau", i32, n["rows"]), _addr(sketch, "sketch", _sk_types(d, f32), n["sketch"]),
         _addr(basis, "basis", f32, n["basis"]), _addr(q, "q", tin, n["q"]),
         _addr(k_t, "k_t", tin, n["k_t"]), _addr(v_t, "v_t", tin, n["v_t"]),
         _addr(decay_t, "decay_t", f32, n["decay_t"]), _addr(beta_t, "beta_t", f32, n["beta_t"]),

@@ -20,7 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsketchssm.so")
-SOURCES = ["abi.hip", "update_refresh.hip", "decode.hip", "append.hip", "recurrent.hip"]
+SOURCES = ["abi.hip", "update_refresh.hip", "decode.hip", "sketch_decode_mamba2.hip",
+           "sketch_decode_gdn.hip", "sketch_decode_kda.hip", "append.hip", "recurrent.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
@@ -48,7 +49,8 @@ def _compile(src: str, save_temps: bool) -> str:
     return obj
 
 
-def build(jobs: int = 4, save_temps: bool = False, verbose: bool = True) -> str:
+def build(jobs: int = 0, save_temps: bool = False, verbose: bool = True) -> str:
+    jobs = jobs or min(8, os.cpu_count() or 1)
     os.makedirs(BUILD, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         objs = list(ex.map(lambda s: _compile(s, save_temps), SOURCES))
@@ -65,7 +67,7 @@ def build(jobs: int = 4, save_temps: bool = False, verbose: bool = True) -> str:
 
 def main() -> None:
     ap = argparse.ArgumentParser()
-    ap.add_argument("-j", "--jobs", type=int, default=4)
+    ap.add_argument("-j", "--jobs", type=int, default=min(8, os.cpu_count() or 1))
     ap.add_argument("--save-temps", action="store_true")
     a = ap.parse_args()
     build(a.jobs, a.save_temps)

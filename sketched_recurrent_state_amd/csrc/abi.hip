@@ -43,6 +43,9 @@ ssm_status check_dims(const ssm_dims* d, const char* fn) {
     return fail(SSM_E_RANGE, "%s: rule %d is not 0 (Mamba-2), 1 (GDN) or 2 (KDA)", fn, d->rule);
   if (d->in_dtype != SSM_IN_BF16 && d->in_dtype != SSM_IN_F32)
     return fail(SSM_E_RANGE, "%s: in_dtype %d is not 0 (bf16) or 1 (fp32)", fn, d->in_dtype);
+  if (d->sketch_dtype != SSM_SKETCH_F32 && d->sketch_dtype != SSM_SKETCH_BF16)
+    return fail(SSM_E_RANGE, "%s: sketch_dtype %d is not 0 (fp32) or 1 (bf16)", fn,
+                d->sketch_dtype);
   if (d->batch < 0) return fail(SSM_E_SHAPE, "%s: batch %d < 0", fn, d->batch);
   if (d->heads < 1) return fail(SSM_E_SHAPE, "%s: heads %d < 1", fn, d->heads);
   if (!in_set(d->d_k, {16, 32, 64, 128}))
@@ -88,17 +91,18 @@ ssm_status check_arrays(const char* fn, std::initializer_list<Arr> arrs) {
 }
 
 struct Sizes {
-  size_t units, elem, state, sketch, basis, kbuf, vbuf, dbuf, bbuf, qk, v, dtok, btok, y;
+  size_t units, elem, sk_elem, state, sketch, basis, kbuf, vbuf, dbuf, bbuf, qk, v, dtok, btok, y;
 };
 
 Sizes sizes_of(const ssm_dims& d) {
   Sizes z;
   z.units = (size_t)d.batch * (size_t)d.heads;
   z.elem = d.in_dtype == SSM_IN_BF16 ? 2 : 4;
+  z.sk_elem = d.sketch_dtype == SSM_SKETCH_BF16 ? 2 : 4;
   const size_t dstr = d.rule == SSM_KDA ? (size_t)d.d_k : 1;
   const size_t W = (size_t)d.window;
   z.state = z.units * d.d_k * d.d_v * 4;
-  z.sketch = z.units * d.rank * d.d_v * 4;
+  z.sketch = z.units * d.rank * d.d_v * z.sk_elem;
   z.basis = (size_t)d.heads * d.rank * d.d_k * 4;
   z.kbuf = z.units * W * d.d_k * z.elem;
   z.vbuf = z.units * W * d.d_v * z.elem;
@@ -161,7 +165,7 @@ ssm_status check_rank_offsets(const ssm_dims& d, const int32_t* off, const char*
 void apply_ranks(const ssm_dims& d, const int32_t* off, Sizes& z) {
   if (off == nullptr) return;
   const size_t R = (size_t)off[d.heads];
-  z.sketch = z.units / (size_t)d.heads * R * d.d_v * 4;
+  z.sketch = z.units / (size_t)d.heads * R * d.d_v * z.sk_elem;
   z.basis = R * d.d_k * 4;
 }
 
@@ -246,7 +250,7 @@ ssm_status ssm_buffer_append(const ssm_dims* d, const void* k_t, const void* v_t
 }
 
 static ssm_status update_refresh_impl(const char* fn, const ssm_dims* d, const int32_t* rank_offsets,
-                               float* state, float* sketch, const float* basis, const void* k_buf,
+                               float* state, void* sketch, const float* basis, const void* k_buf,
                                const void* v_buf, const float* decay_buf, const float* beta_buf,
                                int32_t n_tokens, void* stream, bool ranked) {
   ssm_status st = check_dims(d, fn);
@@ -280,7 +284,7 @@ static ssm_status update_refresh_impl(const char* fn, const ssm_dims* d, const i
 }
 
 static ssm_status sketch_decode_impl(const char* fn, const ssm_dims* d, const int32_t* rank_offsets,
-                              const float* sketch, const float* basis, const void* q,
+                              const void* sketch, const float* basis, const void* q,
                               const void* k_t, const void* v_t, const float* decay_t,
                               const float* beta_t, void* k_buf, void* v_buf, float* decay_buf,
                               float* beta_buf, int32_t tau, float* y, void* stream, bool ranked) {
@@ -369,7 +373,7 @@ ssm_status ssm_recurrent_decode_step(const ssm_dims* d, float* state, const void
                   fn);
 }
 
-ssm_status ssm_window_update_refresh(const ssm_dims* d, float* state, float* sketch,
+ssm_status ssm_window_update_refresh(const ssm_dims* d, float* state, void* sketch,
                                      const float* basis, const void* k_buf, const void* v_buf,
                                      const float* decay_buf, const float* beta_buf,
                                      int32_t n_tokens, void* stream) {
@@ -378,7 +382,7 @@ ssm_status ssm_window_update_refresh(const ssm_dims* d, float* state, float* ske
 }
 
 ssm_status ssm_window_update_refresh_ranked(const ssm_dims* d, const int32_t* rank_offsets,
-                                            float* state, float* sketch, const float* basis,
+                                            float* state, void* sketch, const float* basis,
                                             const void* k_buf, const void* v_buf,
                                             const float* decay_buf, const float* beta_buf,
                                             int32_t n_tokens, void* stream) {
@@ -386,7 +390,7 @@ ssm_status ssm_window_update_refresh_ranked(const ssm_dims* d, const int32_t* ra
                              basis, k_buf, v_buf, decay_buf, beta_buf, n_tokens, stream, true);
 }
 
-ssm_status ssm_sketch_decode_step(const ssm_dims* d, const float* sketch, const float* basis,
+ssm_status ssm_sketch_decode_step(const ssm_dims* d, const void* sketch, const float* basis,
                                   const void* q, const void* k_t, const void* v_t,
                                   const float* decay_t, const float* beta_t, void* k_buf,
                                   void* v_buf, float* decay_buf, float* beta_buf, int32_t tau,
@@ -397,7 +401,7 @@ ssm_status ssm_sketch_decode_step(const ssm_dims* d, const float* sketch, const 
 }
 
 ssm_status ssm_sketch_decode_step_ranked(const ssm_dims* d, const int32_t* rank_offsets,
-                                         const float* sketch, const float* basis, const void* q,
+                                         const void* sketch, const float* basis, const void* q,
                                          const void* k_t, const void* v_t, const float* decay_t,
                                          const float* beta_t, void* k_buf, void* v_buf,
                                          float* decay_buf, float* beta_buf, int32_t tau, float* y,
@@ -409,7 +413,7 @@ ssm_status ssm_sketch_decode_step_ranked(const ssm_dims* d, const int32_t* rank_
 
 ssm_status ssm_window_update_refresh_varlen(const ssm_dims* d, int32_t num_slots,
                                             const int32_t* slot, const int32_t* n_tokens,
-                                            float* state, float* sketch, const float* basis,
+                                            float* state, void* sketch, const float* basis,
                                             const void* k_buf, const void* v_buf,
                                             const float* decay_buf, const float* beta_buf,
                                             void* stream) {
@@ -440,7 +444,7 @@ ssm_status ssm_window_update_refresh_varlen(const ssm_dims* d, int32_t num_slots
 
 ssm_status ssm_sketch_decode_step_varlen(const ssm_dims* d, int32_t num_slots,
                                          const int32_t* slot, const int32_t* tau,
-                                         const float* sketch, const float* basis, const void* q,
+                                         const void* sketch, const float* basis, const void* q,
                                          const void* k_t, const void* v_t, const float* decay_t,
                                          const float* beta_t, void* k_buf, void* v_buf,
                                          float* decay_buf, float* beta_buf, float* y,

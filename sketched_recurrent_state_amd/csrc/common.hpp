@@ -30,6 +30,23 @@ typedef uint16_t bf16_t;  // bf16 bit pattern
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// fp32 -> bf16 bits, rounded to nearest with ties to even: adding 0x7FFF plus
+// the lowest kept bit carries into the kept bits exactly when the dropped half
+// is above one half, or equal to it with an odd kept part. Overflow rounds to
+// infinity; a NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// Four floats stored at p as fp32 (16 bytes) or bf16 (8 bytes).
+__device__ __forceinline__ void store4(float* p, float4 x) { *reinterpret_cast<float4*>(p) = x; }
+__device__ __forceinline__ void store4(uint16_t* p, float4 x) {
+  *reinterpret_cast<uint2*>(p) = make_uint2(bf16_rne(x.x) | (bf16_rne(x.y) << 16),
+                                            bf16_rne(x.z) | (bf16_rne(x.w) << 16));
+}
+
 template <typename T, int E>
 struct Vec;
 

@@ -24,6 +24,32 @@ struct type_tag {
   using type = T;
 };
 
+// Calls f(d_k, d_v, type_tag<input type>) with compile-time constants for every
+// supported combination; returns hipErrorInvalidValue for anything else.
+template <typename F>
+hipError_t dispatch_shape(int in_dtype, int dk, int dv, F&& f) {
+  auto with_dv = [&](auto DK, auto T) -> hipError_t {
+    switch (dv) {
+      case 32: return f(DK, std::integral_constant<int, 32>{}, T);
+      case 64: return f(DK, std::integral_constant<int, 64>{}, T);
+      case 128: return f(DK, std::integral_constant<int, 128>{}, T);
+    }
+    return hipErrorInvalidValue;
+  };
+  auto with_dk = [&](auto T) -> hipError_t {
+    switch (dk) {
+      case 16: return with_dv(std::integral_constant<int, 16>{}, T);
+      case 32: return with_dv(std::integral_constant<int, 32>{}, T);
+      case 64: return with_dv(std::integral_constant<int, 64>{}, T);
+      case 128: return with_dv(std::integral_constant<int, 128>{}, T);
+    }
+    return hipErrorInvalidValue;
+  };
+  if (in_dtype == SSM_IN_BF16) return with_dk(type_tag<uint16_t>{});
+  if (in_dtype == SSM_IN_F32) return with_dk(type_tag<float>{});
+  return hipErrorInvalidValue;
+}
+
 // Calls f(rule, d_k, d_v, type_tag<input type>) with compile-time constants for
 // every supported combination; returns hipErrorInvalidValue for anything else.
 template <typename F>
@@ -58,6 +84,13 @@ hipError_t dispatch(int rule, int in_dtype, int dk, int dv, F&& f) {
   return hipErrorInvalidValue;
 }
 
+// Calls f(type_tag<sketch element type>) for d.sketch_dtype (fp32 or bf16 bits).
+template <typename F>
+hipError_t with_sketch_type(const ssm_dims& d, F&& f) {
+  if (d.sketch_dtype == SSM_SKETCH_BF16) return f(type_tag<uint16_t>{});
+  return f(type_tag<float>{});
+}
+
 // Per-head ranks: rank_offsets is a host array of heads + 1 prefix offsets (checked by the
 // caller), or nullptr for the uniform rank d.rank.
 inline int max_rank_of(const int32_t* rank_offsets, int heads) {
@@ -74,13 +107,13 @@ size_t update_refresh_lds_bytes(const ssm_dims& d, int n_tokens, int max_rank);
 
 // varlen != nullptr: per-row slots and token counts (n_tokens is then ignored).
 hipError_t launch_update_refresh(const ssm_dims& d, const int32_t* rank_offsets, float* state,
-                                 float* sketch, const float* basis, const void* k_buf,
+                                 void* sketch, const float* basis, const void* k_buf,
                                  const void* v_buf, const float* decay_buf, const float* beta_buf,
                                  int n_tokens, hipStream_t stream,
                                  const Varlen* varlen = nullptr);
 
 hipError_t launch_sketch_decode(const ssm_dims& d, const int32_t* rank_offsets,
-                                const float* sketch, const float* basis,
+                                const void* sketch, const float* basis,
                                 const void* q, const void* k_t, const void* v_t,
                                 const float* decay_t, const float* beta_t, void* k_buf,
                                 void* v_buf, float* decay_buf, float* beta_buf, int tau, float* y,

@@ -25,9 +25,9 @@ namespace ssm {
 
 namespace {
 
-template <int RULE, int DK, int DV, typename TIN, typename RT, typename RM>
+template <int RULE, int DK, int DV, typename TIN, typename TSK, typename RT, typename RM>
 __global__ void __launch_bounds__(2 * DV)
-update_refresh_kernel(float* __restrict__ state, float* __restrict__ sketch,
+update_refresh_kernel(float* __restrict__ state, TSK* __restrict__ sketch,
                       const float* __restrict__ basis, const TIN* __restrict__ kbuf,
                       const TIN* __restrict__ vbuf, const float* __restrict__ dbuf,
                       const float* __restrict__ bbuf, int heads, int window, const RT rt,
@@ -105,7 +105,7 @@ update_refresh_kernel(float* __restrict__ state, float* __restrict__ sketch,
         store_stream(Su + (size_t)(m * 8 + rg) * DV + col, s[m]);
     }
     if (sketch == nullptr) return;
-    float* Sku = sketch + ((size_t)seq * rt.total() + rt.offset(head)) * DV;
+    TSK* Sku = sketch + ((size_t)seq * rt.total() + rt.offset(head)) * DV;
     const bool b3 = (lane >> 3) & 1;
     for (int m0 = 0; m0 < rank; m0 += 8) {
       float4 P[8];
@@ -139,7 +139,7 @@ update_refresh_kernel(float* __restrict__ state, float* __restrict__ sketch,
       res.z = halve8(P[0].z, P[1].z, b3);
       res.w = halve8(P[0].w, P[1].w, b3);
       const int m = m0 + rg;
-      if (m < rank) *reinterpret_cast<float4*>(Sku + (size_t)m * DV + col) = res;
+      if (m < rank) store4(Sku + (size_t)m * DV + col, res);  // fp32, or bf16 rounded to nearest
     }
   };
 
@@ -213,7 +213,7 @@ size_t update_refresh_lds_bytes(const ssm_dims& d, int n, int max_rank) {
 }
 
 hipError_t launch_update_refresh(const ssm_dims& d, const int32_t* rank_offsets, float* state,
-                                 float* sketch, const float* basis, const void* k_buf,
+                                 void* sketch, const float* basis, const void* k_buf,
                                  const void* v_buf, const float* decay_buf, const float* beta_buf,
                                  int n, hipStream_t stream, const Varlen* varlen) {
   const unsigned units = (unsigned)d.batch * (unsigned)d.heads;
@@ -224,16 +224,20 @@ hipError_t launch_update_refresh(const ssm_dims& d, const int32_t* rank_offsets,
   return dispatch(d.rule, d.in_dtype, d.d_k, d.d_v, [&](auto R, auto DK, auto DV, auto T) {
     using TIN = typename decltype(T)::type;
     constexpr int kR = decltype(R)::value, kDK = decltype(DK)::value, kDV = decltype(DV)::value;
-    auto go = [&](auto rt, auto rm) {
-      hipLaunchKernelGGL((update_refresh_kernel<kR, kDK, kDV, TIN, decltype(rt), decltype(rm)>),
-                         dim3(units), dim3(2 * kDV), lds, stream, state, sketch, basis,
-                         static_cast<const TIN*>(k_buf), static_cast<const TIN*>(v_buf),
-                         decay_buf, beta_buf, d.heads, d.window, rt, rm);
-      return hipGetLastError();
-    };
-    if (varlen != nullptr) return go(UniformRank{d.rank, d.heads}, *varlen);
-    if (rank_offsets == nullptr) return go(UniformRank{d.rank, d.heads}, Lockstep{n});
-    return go(make_rank_table(rank_offsets, d.heads), Lockstep{n});
+    return with_sketch_type(d, [&](auto SK) {
+      using TSK = typename decltype(SK)::type;
+      auto go = [&](auto rt, auto rm) {
+        hipLaunchKernelGGL(
+            (update_refresh_kernel<kR, kDK, kDV, TIN, TSK, decltype(rt), decltype(rm)>),
+            dim3(units), dim3(2 * kDV), lds, stream, state, static_cast<TSK*>(sketch), basis,
+            static_cast<const TIN*>(k_buf), static_cast<const TIN*>(v_buf), decay_buf, beta_buf,
+            d.heads, d.window, rt, rm);
+        return hipGetLastError();
+      };
+      if (varlen != nullptr) return go(UniformRank{d.rank, d.heads}, *varlen);
+      if (rank_offsets == nullptr) return go(UniformRank{d.rank, d.heads}, Lockstep{n});
+      return go(make_rank_table(rank_offsets, d.heads), Lockstep{n});
+    });
   });
 }
 

@@ -20,7 +20,7 @@ from typing import Optional
 
 import torch
 
-from . import (Dims, IN_BF16, KDA, MAMBA2, buffer_append, full_read_decode_step,
+from . import (Dims, IN_BF16, KDA, MAMBA2, SKETCH_BF16, buffer_append, full_read_decode_step,
                rank_offsets, recurrent_decode_step, sketch_decode_step,
                sketch_decode_step_ranked, window_update_refresh, window_update_refresh_ranked)
 
@@ -36,6 +36,7 @@ class WindowedDecoder:
             separate buffering launch
     ranks:  optional per-head sketch ranks (H values); then basis is fp32 [sum(ranks), d_k]
             and the sketch [N, sum(ranks), d_v]
+    The sketch is kept in dims.sketch_dtype (fp32, or bf16 rounded to nearest).
     """
 
     def __init__(self, dims: Dims, state: torch.Tensor, basis: Optional[torch.Tensor] = None, *,
@@ -54,7 +55,8 @@ class WindowedDecoder:
         self.basis = basis
         self.offsets = rank_offsets(ranks) if ranks is not None else None
         rows = (H, r) if ranks is None else (int(self.offsets[H]),)
-        self.sketch = (torch.empty((N,) + rows + (dv,), device=dev, dtype=torch.float32)
+        sk_dtype = torch.bfloat16 if dims.sketch_dtype == SKETCH_BF16 else torch.float32
+        self.sketch = (torch.empty((N,) + rows + (dv,), device=dev, dtype=sk_dtype)
                        if read != "full" else None)
         self.k_buf = torch.zeros((N, H, W, dk), device=dev, dtype=tin)
         self.v_buf = torch.zeros((N, H, W, dv), device=dev, dtype=tin)

@@ -311,4 +311,73 @@ def pin_scalar_hand_case(L):
     close(out["S_win"].ravel(), [2.0, 4.0], 1e-15, "scalar S_win")
 
 
+# ----------------------------------------------------------------------------
+# bf16 sketch storage (an option: the pages leave the sketch's precision open)
+# ----------------------------------------------------------------------------
+def pin_bf16_rounding_cases(L):
+    """Round to nearest bf16, ties to even, after rounding to fp32: values worked by hand.
+
+    bf16 keeps 8 significant bits, so near 1 the spacing is 2^-7 and 1 + 2^-8 is
+    exactly half way between 1 (pattern 0x3F80, even) and 1 + 2^-7 (0x3F81, odd).
+    """
+    f = lambda x: oracle.round_bf16(x, _lib_override=L)
+    e = 2.0 ** -8
+    cases = [
+        (1.0, 1.0),
+        (1 + e, 1.0),                     # tie, the even neighbour is 1
+        (1 + 3 * e, 1 + 4 * e),           # tie between 0x3F81 (odd) and 0x3F82 (even)
+        (1 + e + 2.0 ** -20, 1 + 2 * e),  # above half
+        (1 + e - 2.0 ** -20, 1.0),        # below half
+        (-(1 + 3 * e), -(1 + 4 * e)),     # sign symmetric
+        (1 + e + 2.0 ** -30, 1.0),        # fp32 first: the 2^-30 is lost, then a tie
+        ((2 - e) * 2.0 ** 127, np.inf),   # half way above the largest bf16: to infinity
+        (3.0, 3.0), (0.0, 0.0),
+    ]
+    for x, want in cases:
+        got = f(x)
+        assert got == want, f"round_bf16({x!r}) = {got!r}, want {want!r}"
+    assert np.copysign(1.0, f(-0.0)) == -1.0, "the sign of zero is kept"
+    assert np.isnan(f(float("nan")))
+
+
+def pin_bf16_rounding_matches_torch(L):
+    """The rounding equals torch's fp32 -> bfloat16 conversion (round to nearest even) on
+    random fp32 values and on values built to sit exactly on ties."""
+    import torch
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal(4000) * np.exp(rng.uniform(-20, 20, 4000))).astype(np.float32)
+    ties = (np.float32(1.0) + np.arange(1, 200, dtype=np.float32) * np.float32(2.0 ** -8))
+    x = np.concatenate([x, ties, -ties]).astype(np.float64)
+    want = torch.from_numpy(x).to(torch.float32).to(torch.bfloat16).to(torch.float64).numpy()
+    got = np.array([oracle.round_bf16(v, _lib_override=L) for v in x])
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, f"{bad.size} values differ, e.g. {x[bad[0]]!r}: {got[bad[0]]!r} vs {want[bad[0]]!r}"
+
+
+def pin_bf16_sketch_enters_only_the_sketch_read(L):
+    """With a bf16 sketch every stored sketch (each window) is the fp32 sketch rounded
+    (checked against torch's conversion); the exact reads do not change; and y_sketch
+    moves by exactly (Sk_bf16 - Sk_f32)^T c with c = B A^T q from the same run."""
+    import torch
+    for rule in RULES:
+        p = problem(rule, U=2, dk=6, dv=5, r=3, W=3, T=7, seed=5)
+        a = run(L, p, want_A=True)
+        b = run(L, p, want_A=True, sketch_bf16=True)
+        want = torch.from_numpy(a["Sk"]).to(torch.float32).to(torch.bfloat16).to(torch.float64)
+        assert np.array_equal(b["Sk"], want.numpy()), f"{rule}: stored sketch not rounded"
+        assert not np.array_equal(a["Sk"], b["Sk"]), f"{rule}: rounding changed nothing"
+        for key in ("y_exact", "y_replay", "S_win"):
+            assert np.array_equal(a[key], b[key]), f"{rule}: {key} changed"
+        T, U = p["q"].shape[:2]
+        W = p["window"]
+        for t in range(T):
+            win = t // W
+            for u in range(U):
+                qt = a["A"][t, u].T @ p["q"][t, u]
+                c = p["basis"][u] @ qt
+                dy = (b["Sk"][win, u] - a["Sk"][win, u]).T @ c
+                close(b["y_sketch"][t, u] - a["y_sketch"][t, u], dy, 1e-12,
+                      f"{rule} t={t} u={u} y_sketch shift")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert ssm.abi_version() == 1
+    assert ssm.abi_version() == 2
     lib = ssm.library()
     for code in range(7):
         assert lib.ssm_status_string(code).decode()
@@ -65,6 +65,7 @@ def test_null_dims():
     ("rule", 3, 4), ("rule", -1, 4), ("in_dtype", 2, 4),
     ("batch", -1, 2), ("heads", 0, 2), ("d_k", 48, 2), ("d_k", 256, 2), ("d_v", 16, 2),
     ("d_v", 256, 2), ("window", 0, 2), ("window", 17, 2), ("rank", 0, 2), ("rank", 33, 2),
+    ("sketch_dtype", 2, 4), ("sketch_dtype", -1, 4),
 ])
 def test_bad_dims(field, value, code):
     d = dims()
@@ -187,6 +188,23 @@ def test_aliasing():
     d = dims(rule="mamba2")
     st, msg = status_of(ssm.full_read_decode_step, d, p[0], p[1], p[1], p[1], p[1], None, 1, p[1])
     assert st == 5  # but y may not overlap them
+
+
+def test_bf16_sketch_is_sized_in_bf16():
+    # dims(): 6 units x rank 4 x d_v 64 -> the sketch is 6144 bytes in fp32, 3072 in bf16.
+    # The basis sits 3072 bytes after the sketch and k_buf overlaps the sketch's first half,
+    # so the first overlap found names the basis for an fp32 sketch and k_buf for a bf16 one.
+    # Either way validation fails before anything is launched.
+    s = A + (8 << 28)
+    state, basis, kbuf = A, s + 3072, s + 3056
+    vbuf, dbuf, bbuf = A + (9 << 28), A + (10 << 28), A + (11 << 28)
+    st, msg = status_of(ssm.window_update_refresh, dims(), state, s, basis, kbuf, vbuf, dbuf,
+                        bbuf, 2)
+    assert st == 5 and "sketch overlaps basis" in msg, msg
+    d = ssm.Dims.make("gdn", "bf16", 2, 3, 32, 64, 4, 4, sketch_dtype="bf16")
+    assert d.sketch_dtype == ssm.SKETCH_BF16
+    st, msg = status_of(ssm.window_update_refresh, d, state, s, basis, kbuf, vbuf, dbuf, bbuf, 2)
+    assert st == 5 and "sketch overlaps k_buf" in msg, msg
 
 
 def test_last_error_is_thread_local_and_cleared():

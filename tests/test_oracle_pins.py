@@ -45,6 +45,13 @@ MUTANTS = [
      "matmul(r, dk, dv, Bu, Swin, Sk);\n          memcpy(Swin, S, sizeof(double) * sz_s);"),
     ("exact_read_before_update", "if (y_exact) transpose_times(dk, dv, S, qv, y_exact + tu * dv);",
      "if (y_exact) transpose_times(dk, dv, Swin, qv, y_exact + tu * dv);"),
+    ("bf16_ties_away_from_zero", "if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) kept += 1u;",
+     "if (dropped >= 0x8000u) kept += 1u;"),
+    ("bf16_truncates", "if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) kept += 1u;",
+     "(void)dropped;"),
+    ("bf16_window_refresh_not_rounded",
+     "matmul(r, dk, dv, Bu, Swin, Sk);\n          if (sketch_bf16) round_sketch(sz_k, Sk);",
+     "matmul(r, dk, dv, Bu, Swin, Sk);"),
 ]
 
 

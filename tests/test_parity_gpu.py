@@ -438,3 +438,23 @@ def test_extreme_gates(rule):
     inp.S0 = inp.S0 * 1e3
     inp.host_S0 = inp.host_S0 * 1e3
     H.compare(cfg, H.run_gpu(cfg, inp), H.run_oracle(cfg, inp))
+
+
+# bf16 sketch storage: the sketch is rounded to bf16 when the refresh stores it;
+# the oracle rounds its sketch the same way. Rules, input types, odd shapes,
+# per-head ranks do not change the path, so one of each shape family is enough.
+BF16_SKETCH = [
+    small("gdn"), small("kda", W=4, r=8), small("mamba2", d_k=128, d_v=64),
+    small("gdn", "f32", d_k=64, d_v=32, W=5, r=3), small("kda", d_k=16, d_v=128, W=1, r=16),
+    small("gdn", "bf16", d_k=128, d_v=128, W=16, r=32, N=2, Hh=3, T=33),
+]
+
+
+@pytest.mark.parametrize("cfg", BF16_SKETCH, ids=lambda c: c.name)
+def test_bf16_sketch(cfg):
+    H.note(f"case bf16 sketch {cfg.name}")
+    inp = H.Inputs(cfg, np.arange(cfg.units), cfg.steps)
+    got = H.run_gpu(cfg, inp, sketch_dtype="bf16")
+    ref = H.run_oracle(cfg, inp, sketch_bf16=True)
+    H.compare(cfg, got, ref, sketch_bf16=True)
+    assert got["sketch"].dtype == torch.bfloat16
