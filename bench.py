@@ -48,8 +48,8 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def bytes_model(cfg) -> dict:
-    """Algorithmic HBM bytes per unit (sequence, head)."""
+def bytes_model(cfg, sk_bytes: int = 4) -> dict:
+    """Algorithmic HBM bytes per unit (sequence, head); sk_bytes per sketch element."""
     s_in = 2 if cfg.in_dtype == "bf16" else 4
     g = {"mamba2": 4, "gdn": 8, "kda": 4 * cfg.d_k + 4}[cfg.rule]
     tok = (cfg.d_k + cfg.d_v) * s_in + g
@@ -58,13 +58,13 @@ def bytes_model(cfg) -> dict:
     # per decode step: q + the current token (appended: read once, written once)
     #   + the older buffered tokens + y; plus the sketch or the full state
     step_common = dk * s_in + tok + (tau_mean - 1) * tok + tok + 4 * dv
-    sketch_step = 4 * r * dv + step_common
+    sketch_step = sk_bytes * r * dv + step_common
     full_step = 4 * dk * dv + step_common
-    update = 8 * dk * dv + 4 * r * dv + W * tok          # read S, write S, write Sk, read buffer
+    update = 8 * dk * dv + sk_bytes * r * dv + W * tok   # read S, write S, write Sk, read buffer
     update_no_refresh = 8 * dk * dv + W * tok
     return dict(tok=tok, sketch_step=sketch_step, full_step=full_step, update=update,
                 update_no_refresh=update_no_refresh,
-                state_bytes_sketch=4 * r * dv, state_bytes_full=4 * dk * dv,
+                state_bytes_sketch=sk_bytes * r * dv, state_bytes_full=4 * dk * dv,
                 amortized_sketch=sketch_step + update / W,
                 amortized_full=full_step + update_no_refresh / W)
 
@@ -94,6 +94,8 @@ def main() -> int:
                          "updates N/W sequences (variable-length entry points, slot map)")
     ap.add_argument("--per-head-ranks", choices=["avg8"], default=None,
                     help="per-head sketch ranks (avg8: 2, 4, 8, 18 cycled over heads, mean 8)")
+    ap.add_argument("--sketch-dtype", choices=["f32", "bf16"], default="f32",
+                    help="storage type of the sketch (the headline workload keeps fp32)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="profiling: copy MIB MiB with a plain device copy kernel, then exit")
     a = ap.parse_args()
@@ -128,7 +130,8 @@ def main() -> int:
         print(f"--steps and --warmup must be multiples of the window W={W}", file=sys.stderr)
         return 2
     total = a.warmup + a.steps
-    d = ssm.Dims.make(cfg.rule, cfg.in_dtype, cfg.batch, cfg.heads, cfg.d_k, cfg.d_v, W, cfg.rank)
+    d = ssm.Dims.make(cfg.rule, cfg.in_dtype, cfg.batch, cfg.heads, cfg.d_k, cfg.d_v, W, cfg.rank,
+                      a.sketch_dtype)
     U = cfg.units
 
     # ---- inputs, resident in HBM before timing ---------------------------------------
@@ -151,7 +154,7 @@ def main() -> int:
         basis = to_dev(workloads.basis_ranked(cfg, ranks))
         offsets = ssm.rank_offsets(ranks)
         d_r = ssm.Dims.make(cfg.rule, cfg.in_dtype, cfg.batch, cfg.heads, cfg.d_k, cfg.d_v, W,
-                            max(ranks))
+                            max(ranks), a.sketch_dtype)
     else:
         basis = to_dev(workloads.basis(cfg))
     inputs = [(to_dev(s.q), to_dev(s.k), to_dev(s.v), to_dev(s.decay), to_dev(s.beta))
@@ -239,12 +242,13 @@ def main() -> int:
         return timed(g.replay), g
 
     sp = stream.cuda_stream
-    bm = bytes_model(cfg)
+    bm = bytes_model(cfg, 2 if a.sketch_dtype == "bf16" else 4)
 
     # ---- the sketch path, eager launches (update kernel timed by HIP events) ---------
     state = S0_dev.clone()
     sk_rows = cfg.heads * cfg.rank if ranks is None else sum(ranks)
-    sketch = torch.empty((cfg.batch, sk_rows, cfg.d_v), device=dev)
+    sk_dtype = torch.bfloat16 if a.sketch_dtype == "bf16" else torch.float32
+    sketch = torch.empty((cfg.batch, sk_rows, cfg.d_v), device=dev, dtype=sk_dtype)
     st_p, sk_p = P(state), P(sketch)
     update_refresh(st_p, sk_p, bp, None, None, None, None, 0, stream=sp)
     run_sketch(st_p, sk_p, 0, a.warmup, sp, only=a.only)
@@ -271,7 +275,7 @@ def main() -> int:
                             device=dev) for ph in range(W)]
         fulls = [torch.full((len(u),), W, dtype=torch.int32, device=dev) for u in ups]
         d_ups = [ssm.Dims.make(cfg.rule, cfg.in_dtype, len(u), cfg.heads, cfg.d_k, cfg.d_v, W,
-                               cfg.rank) for u in ups]
+                               cfg.rank, a.sketch_dtype) for u in ups]
         tp, up, fp = [P(x) for x in taus], [P(x) for x in ups], [P(x) for x in fulls]
 
         def run_staggered(t_lo, t_hi, sp_, upd_events=None):
@@ -403,7 +407,11 @@ def main() -> int:
                 if sep and key in ("config", "kernel_source_hash", "bytes_per_launch"):
                     tr[key] = val
         # counters taken on another kernel version do not describe this one
-        if tr.get("kernel_source_hash") == kernel_source_hash() and tr.get("config") == cfg.name:
+        # ... nor does a run on another workload (the counters are for the lockstep,
+        # uniform-rank, fp32-sketch decode of that config)
+        same_workload = (tr.get("config") == cfg.name and a.schedule == "lockstep"
+                         and ranks is None and a.sketch_dtype == "f32")
+        if tr.get("kernel_source_hash") == kernel_source_hash() and same_workload:
             traffic = float(tr["bytes_per_launch"])
 
     # ---- CPU baseline: the oracle on a bounded sample --------------------------------
@@ -447,7 +455,8 @@ def main() -> int:
         "config": {"workload": cfg.description, "rule": cfg.rule, "batch": cfg.batch,
                    "heads": cfg.heads, "d_k": cfg.d_k, "d_v": cfg.d_v, "window": W,
                    "rank": cfg.rank if ranks is None else f"per head {sorted(set(ranks))}, mean "
-                   f"{sum(ranks) / len(ranks):g}", "inputs": cfg.in_dtype, "state": "f32"},
+                   f"{sum(ranks) / len(ranks):g}", "inputs": cfg.in_dtype, "state": "f32",
+                   "sketch": a.sketch_dtype},
         "roofline": {"bound": "hbm", "kernel": "update_refresh_kernel", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "bytes_per_launch": upd_bytes,
