@@ -30,21 +30,20 @@ typedef uint16_t bf16_t;  // bf16 bit pattern
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// fp32 -> bf16 bits, rounded to nearest with ties to even: adding 0x7FFF plus
-// the lowest kept bit carries into the kept bits exactly when the dropped half
-// is above one half, or equal to it with an odd kept part. Overflow rounds to
-// infinity; a NaN stays a (quiet) NaN.
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+// Two floats -> packed bf16 bits (a in the low half), rounded to nearest with
+// ties to even: one gfx950 v_cvt_pk_bf16_f32 under the default rounding mode.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2_t v;
+  v.x = (__bf16)a;
+  v.y = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Four floats stored at p as fp32 (16 bytes) or bf16 (8 bytes).
 __device__ __forceinline__ void store4(float* p, float4 x) { *reinterpret_cast<float4*>(p) = x; }
 __device__ __forceinline__ void store4(uint16_t* p, float4 x) {
-  *reinterpret_cast<uint2*>(p) = make_uint2(bf16_rne(x.x) | (bf16_rne(x.y) << 16),
-                                            bf16_rne(x.z) | (bf16_rne(x.w) << 16));
+  *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(x.x, x.y), pack_bf16x2(x.z, x.w));
 }
 
 template <typename T, int E>
