@@ -238,6 +238,42 @@ ssm_status ssm_sketch_decode_step_varlen(const ssm_dims* d, int32_t num_slots,
                                          float* beta_buf, float* y, void* stream);
 
 /*
+ * Least-squares coefficients: the other reading of the pages' "low-rank
+ * state-weighted query approximation" (readsearch.ai listing of arXiv
+ * 2609.33051, Abstract). Instead of c = B q~, a step takes the c that minimises
+ * || S_win^T q~ - Sk^T c || (the smallest such c when the sketch rows are
+ * linearly dependent), so its output Sk^T c + R^T q is the orthogonal
+ * projection of the exact window-start read on the span of the sketch rows.
+ * It is never further from the exact read than the projection read, and it is
+ * exact whenever S_win^T q~ lies in that span (e.g. a state of rank <= r whose
+ * row space the sketch captures).
+ *
+ * ssm_window_update_refresh_ls: the window update as ssm_window_update_refresh,
+ * then, from the updated state S and Sk = B S,
+ *   sketch_q  fp32 [N][H][r][d_v]  rows orthonormal and spanning the rows of Sk
+ *                                  (Gram-Schmidt; a row whose residual is below
+ *                                  1e-5 of the largest Sk row norm is stored as zero)
+ *   read_map  fp32 [N][H][r][d_k]  Y = sketch_q S^T
+ * ssm_sketch_decode_step_ls: the step as ssm_sketch_decode_step, with
+ * y = sketch_q^T (read_map q~) + R^T q. The basis is not read.
+ * Requires sketch_dtype = SSM_SKETCH_F32 (else SSM_E_RANGE); uniform rank; all
+ * sequences at the same window position. Outputs of the update: state,
+ * sketch_q, read_map; of the step: y (and the buffers when the token is fused).
+ * Per step the read moves r*(d_v + d_k)*4 bytes of sketch_q and read_map per
+ * unit instead of r*d_v*4 of Sk.
+ */
+ssm_status ssm_window_update_refresh_ls(const ssm_dims* d, float* state, float* sketch_q,
+                                        float* read_map, const float* basis, const void* k_buf,
+                                        const void* v_buf, const float* decay_buf,
+                                        const float* beta_buf, int32_t n_tokens, void* stream);
+ssm_status ssm_sketch_decode_step_ls(const ssm_dims* d, const float* sketch_q,
+                                     const float* read_map, const void* q, const void* k_t,
+                                     const void* v_t, const float* decay_t,
+                                     const float* beta_t, void* k_buf, void* v_buf,
+                                     float* decay_buf, float* beta_buf, int32_t tau, float* y,
+                                     void* stream);
+
+/*
  * Per-token recurrent decode step (the standard decode SketchSSM is compared
  * against: readsearch.ai listing, Abstract, kernel speedups over the standard
  * vLLM baseline; agihunt.info "Confirmed", background bullet: every step reads

@@ -40,7 +40,7 @@ def _load(path: str = LIB_PATH):
     lib = ctypes.CDLL(path)
     dp = ctypes.POINTER(ctypes.c_double)
     lib.oracle_run.restype = ctypes.c_int
-    lib.oracle_run.argtypes = [ctypes.c_int] * 7 + [dp] * 14 + [ctypes.c_int] * 2
+    lib.oracle_run.argtypes = [ctypes.c_int] * 7 + [dp] * 15 + [ctypes.c_int] * 2
     lib.oracle_round_bf16.restype = ctypes.c_double
     lib.oracle_round_bf16.argtypes = [ctypes.c_double]
     lib.oracle_rule_step.restype = ctypes.c_int
@@ -102,8 +102,8 @@ def rule_step(rule: str, S, k, v, decay, beta: float = 0.0, _lib_override=None):
 
 
 def run(rule: str, S0, basis, q, k, v, decay, beta, window: int, *,
-        want_A: bool = False, want_R: bool = False, sketch_bf16: bool = False, threads: int = 0,
-        _lib_override=None) -> dict:
+        want_A: bool = False, want_R: bool = False, want_ls: bool = False,
+        sketch_bf16: bool = False, threads: int = 0, _lib_override=None) -> dict:
     """Run T decode steps for U independent units.
 
     Shapes: S0 [U][dk][dv]; basis [U][r][dk]; q, k [T][U][dk]; v [T][U][dv];
@@ -112,6 +112,8 @@ def run(rule: str, S0, basis, q, k, v, decay, beta, window: int, *,
     (window-start states and sketches) and, if asked, A [T][U][dk][dk] and
     R [T][U][dk][dv]. sketch_bf16: the stored sketch is rounded as a bf16 store
     rounds it (to fp32, then to nearest bf16, ties to even) before it is read.
+    want_ls: also y_ls [T][U][dv], the sketch read with least-squares coefficients
+    (see ls_read) and q~ [T][U][dk].
     """
     L = _lib_override or lib()
     S0, basis, q, k, v, decay = map(_f64, (S0, basis, q, k, v, decay))
@@ -128,15 +130,43 @@ def run(rule: str, S0, basis, q, k, v, decay, beta, window: int, *,
         "Sk": np.zeros((nwin + 1, U, r, dv)),
         "A": np.zeros((T, U, dk, dk)) if want_A else None,
         "R": np.zeros((T, U, dk, dv)) if want_R else None,
+        "qt": np.zeros((T, U, dk)) if want_ls else None,
     }
     rc = L.oracle_run(RULE_IDS[rule], U, dk, dv, r, window, T,
                       _ptr(S0), _ptr(basis), _ptr(q), _ptr(k), _ptr(v), _ptr(decay), _ptr(beta),
                       _ptr(out["y_exact"]), _ptr(out["y_replay"]), _ptr(out["y_sketch"]),
                       _ptr(out["S_win"]), _ptr(out["Sk"]), _ptr(out["A"]), _ptr(out["R"]),
-                      int(bool(sketch_bf16)), int(threads))
+                      _ptr(out["qt"]), int(bool(sketch_bf16)), int(threads))
     if rc:
         raise RuntimeError("oracle_run failed")
+    if want_ls:
+        out["y_ls"] = ls_read(out, window)
     return out
+
+
+# Rank decisions of the least-squares read: a singular value of the sketch counts
+# as zero below this fraction of the largest one.
+LS_RCOND = 1e-5
+
+
+def ls_read(out: dict, window: int) -> np.ndarray:
+    """The sketch read with least-squares coefficients (a reading of the pages'
+    "state-weighted query approximation", readsearch.ai listing of arXiv 2609.33051,
+    Abstract): at step t of a window, c minimises || S_win^T q~ - Sk^T c || (the
+    smallest such c when Sk is rank-deficient) and y = Sk^T c + R^T q, where
+    R^T q = y_replay - S_win^T q~. Sk^T c is the orthogonal projection of the exact
+    window-start read S_win^T q~ onto the span of the sketch rows.
+    """
+    T, U, dv = out["y_replay"].shape
+    y = np.empty((T, U, dv))
+    for t in range(T):
+        win = t // window
+        for u in range(U):
+            Sw, Sk, qt = out["S_win"][win, u], out["Sk"][win, u], out["qt"][t, u]
+            exact = Sw.T @ qt                                  # S_win^T q~, [dv]
+            c = np.linalg.lstsq(Sk.T, exact, rcond=LS_RCOND)[0]
+            y[t, u] = Sk.T @ c + (out["y_replay"][t, u] - exact)
+    return y
 
 
 def round_bf16(x: float, _lib_override=None) -> float:

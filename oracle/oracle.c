@@ -174,6 +174,7 @@ static void round_sketch(size_t n, double* Sk) {
  * Sk_out    [T/W + 1][U][r][dv]   the sketch B S_win stored at each window start
  * A_out     [T][U][dk][dk]        A after each token (tiny shapes only)
  * R_out     [T][U][dk][dv]        R after each token (tiny shapes only)
+ * qt_out    [T][U][dk]            q~ = A^T q of each step (the carried-back query)
  * sketch_bf16  non-zero: the stored sketch is rounded as a bf16 store rounds it
  * nthreads  OpenMP threads (<= 0: runtime default)
  * Returns 0, or 1 on allocation failure / bad arguments.
@@ -184,7 +185,7 @@ int oracle_run(int rule, int U, int dk, int dv, int r, int W, int T,
                const double* decay, const double* beta,
                double* y_exact, double* y_replay, double* y_sketch,
                double* S_out, double* Sk_out, double* A_out, double* R_out,
-               int sketch_bf16, int nthreads) {
+               double* qt_out, int sketch_bf16, int nthreads) {
   if (rule < 0 || rule > 2 || U < 0 || dk < 1 || dv < 1 || r < 1 || W < 1 || T < 0) return 1;
   if (rule != ORACLE_MAMBA2 && beta == NULL) return 1;
   const int dstride = (rule == ORACLE_KDA) ? dk : 1;
@@ -240,6 +241,7 @@ int oracle_run(int rule, int U, int dk, int dv, int r, int W, int T,
         if (y_exact) transpose_times(dk, dv, S, qv, y_exact + tu * dv);
         /* q~ = A^T q ; c = B q~ ; intra = R^T q */
         transpose_times(dk, dk, A, qv, qt);
+        if (qt_out) memcpy(qt_out + tu * dk, qt, sizeof(double) * dk);
         for (int m = 0; m < r; ++m) {
           double acc = 0.0;
           for (int i = 0; i < dk; ++i) acc += Bu[(size_t)m * dk + i] * qt[i];

@@ -102,6 +102,10 @@ def _load():
     lib.ssm_recurrent_decode_step.argtypes = [dp] + [vp] * 7 + [vp]
     lib.ssm_full_read_decode_step.restype = i32
     lib.ssm_full_read_decode_step.argtypes = [dp] + [vp] * 10 + [i32, vp, vp]
+    lib.ssm_window_update_refresh_ls.restype = i32
+    lib.ssm_window_update_refresh_ls.argtypes = [dp] + [vp] * 8 + [i32, vp]
+    lib.ssm_sketch_decode_step_ls.restype = i32
+    lib.ssm_sketch_decode_step_ls.argtypes = [dp] + [vp] * 11 + [i32, vp, vp]
     return lib
 
 
@@ -136,6 +140,7 @@ def numel(d: Dims) -> dict:
     dstr = d.d_k if d.rule == KDA else 1
     return {
         "state": U * d.d_k * d.d_v, "sketch": U * d.rank * d.d_v, "basis": d.heads * d.rank * d.d_k,
+        "read_map": U * d.rank * d.d_k,
         "k_buf": U * d.window * d.d_k, "v_buf": U * d.window * d.d_v,
         "decay_buf": U * d.window * dstr, "beta_buf": U * d.window,
         "q": U * d.d_k, "k_t": U * d.d_k, "v_t": U * d.d_v, "decay_t": U * dstr, "beta_t": U,
@@ -416,4 +421,45 @@ def sketch_decode_step_varlen(d: Dims, num_slots: int, slot, tau, sketch, basis,
         _addr(k_buf, "k_buf", tin, n["k_buf"]), _addr(v_buf, "v_buf", tin, n["v_buf"]),
         _addr(decay_buf, "decay_buf", f32, n["decay_buf"]),
         _addr(beta_buf, "beta_buf", f32, n["beta_buf"]), _addr(y, "y", f32, n["y"]),
+        _stream(stream)))
+
+
+def window_update_refresh_ls(d: Dims, state, sketch_q, read_map, basis, k_buf, v_buf, decay_buf,
+                             beta_buf, n_tokens: int, stream=None) -> None:
+    """ssm_window_update_refresh_ls: the window update, then the least-squares sketch
+    (orthonormal sketch rows sketch_q [N][H][r][d_v] and read_map [N][H][r][d_k])."""
+    args = (state, sketch_q, read_map, basis, k_buf, v_buf, decay_buf, beta_buf)
+    if isinstance(stream, int) and _all_raw(args):
+        return _check(_lib.ssm_window_update_refresh_ls(ctypes.byref(d), *args, n_tokens, stream))
+    tin, f32 = _types(d, args)
+    n = numel(d)
+    _check(_lib.ssm_window_update_refresh_ls(
+        ctypes.byref(d), _addr(state, "state", f32, n["state"]),
+        _addr(sketch_q, "sketch_q", f32, n["sketch"]),
+        _addr(read_map, "read_map", f32, n["read_map"]), _addr(basis, "basis", f32, n["basis"]),
+        _addr(k_buf, "k_buf", tin, n["k_buf"]), _addr(v_buf, "v_buf", tin, n["v_buf"]),
+        _addr(decay_buf, "decay_buf", f32, n["decay_buf"]),
+        _addr(beta_buf, "beta_buf", f32, n["beta_buf"]), int(n_tokens), _stream(stream)))
+
+
+def sketch_decode_step_ls(d: Dims, sketch_q, read_map, q, k_buf, v_buf, decay_buf, beta_buf,
+                          tau: int, y, *, k_t=None, v_t=None, decay_t=None, beta_t=None,
+                          stream=None) -> None:
+    """ssm_sketch_decode_step_ls: y = sketch_q^T (read_map q~) + R^T q."""
+    args = (sketch_q, read_map, q, k_buf, v_buf, decay_buf, beta_buf, y, k_t, v_t, decay_t,
+            beta_t)
+    if isinstance(stream, int) and _all_raw(args):
+        return _check(_lib.ssm_sketch_decode_step_ls(ctypes.byref(d), sketch_q, read_map, q, k_t,
+                                                     v_t, decay_t, beta_t, k_buf, v_buf,
+                                                     decay_buf, beta_buf, tau, y, stream))
+    tin, f32 = _types(d, args)
+    n = numel(d)
+    _check(_lib.ssm_sketch_decode_step_ls(
+        ctypes.byref(d), _addr(sketch_q, "sketch_q", f32, n["sketch"]),
+        _addr(read_map, "read_map", f32, n["read_map"]), _addr(q, "q", tin, n["q"]),
+        _addr(k_t, "k_t", tin, n["k_t"]), _addr(v_t, "v_t", tin, n["v_t"]),
+        _addr(decay_t, "decay_t", f32, n["decay_t"]), _addr(beta_t, "beta_t", f32, n["beta_t"]),
+        _addr(k_buf, "k_buf", tin, n["k_buf"]), _addr(v_buf, "v_buf", tin, n["v_buf"]),
+        _addr(decay_buf, "decay_buf", f32, n["decay_buf"]),
+        _addr(beta_buf, "beta_buf", f32, n["beta_buf"]), int(tau), _addr(y, "y", f32, n["y"]),
         _stream(stream)))

@@ -252,7 +252,8 @@ ssm_status ssm_buffer_append(const ssm_dims* d, const void* k_t, const void* v_t
 static ssm_status update_refresh_impl(const char* fn, const ssm_dims* d, const int32_t* rank_offsets,
                                float* state, void* sketch, const float* basis, const void* k_buf,
                                const void* v_buf, const float* decay_buf, const float* beta_buf,
-                               int32_t n_tokens, void* stream, bool ranked) {
+                               int32_t n_tokens, void* stream, bool ranked,
+                               float* read_map = nullptr, bool ls = false) {
   ssm_status st = check_dims(d, fn);
   if (st != SSM_OK) return st;
   if (ranked && (st = check_rank_offsets(*d, rank_offsets, fn)) != SSM_OK) return st;
@@ -260,6 +261,12 @@ static ssm_status update_refresh_impl(const char* fn, const ssm_dims* d, const i
     return fail(SSM_E_RANGE, "%s: n_tokens %d not in [0, %d]", fn, n_tokens, d->window);
   if (d->batch == 0) return ok();
   if (state == nullptr) return fail(SSM_E_NULL, "%s: state is NULL", fn);
+  if (ls) {
+    if (d->sketch_dtype != SSM_SKETCH_F32)
+      return fail(SSM_E_RANGE, "%s: least-squares coefficients need an fp32 sketch", fn);
+    if (sketch == nullptr) return fail(SSM_E_NULL, "%s: sketch_q is NULL", fn);
+    if (read_map == nullptr) return fail(SSM_E_NULL, "%s: read_map is NULL", fn);
+  }
   if (sketch != nullptr && basis == nullptr)
     return fail(SSM_E_NULL, "%s: basis is NULL but a sketch is requested", fn);
   if (n_tokens > 0) {
@@ -269,7 +276,9 @@ static ssm_status update_refresh_impl(const char* fn, const ssm_dims* d, const i
   Sizes z = sizes_of(*d);
   apply_ranks(*d, rank_offsets, z);
   const bool tok = n_tokens > 0;
-  st = check_arrays(fn, {{state, z.state, true, "state"}, {sketch, z.sketch, true, "sketch"},
+  const size_t map_bytes = z.units * d->rank * d->d_k * 4;
+  st = check_arrays(fn, {{state, z.state, true, "state"}, {sketch, z.sketch, true, ls ? "sketch_q" : "sketch"},
+                         {read_map, map_bytes, true, "read_map"},
                          {basis, z.basis, false, "basis"},
                          {tok ? k_buf : nullptr, z.kbuf, false, "k_buf"},
                          {tok ? v_buf : nullptr, z.vbuf, false, "v_buf"},
@@ -279,7 +288,8 @@ static ssm_status update_refresh_impl(const char* fn, const ssm_dims* d, const i
   (void)hipGetLastError();
   return launched(ssm::launch_update_refresh(*d, rank_offsets, state, sketch, basis, k_buf, v_buf, decay_buf,
                                              beta_buf, n_tokens,
-                                             reinterpret_cast<hipStream_t>(stream)),
+                                             reinterpret_cast<hipStream_t>(stream), nullptr,
+                                             read_map),
                   fn);
 }
 
@@ -287,23 +297,28 @@ static ssm_status sketch_decode_impl(const char* fn, const ssm_dims* d, const in
                               const void* sketch, const float* basis, const void* q,
                               const void* k_t, const void* v_t, const float* decay_t,
                               const float* beta_t, void* k_buf, void* v_buf, float* decay_buf,
-                              float* beta_buf, int32_t tau, float* y, void* stream, bool ranked) {
+                              float* beta_buf, int32_t tau, float* y, void* stream, bool ranked,
+                              bool ls = false) {
   ssm_status st = check_dims(d, fn);
   if (st != SSM_OK) return st;
   if (ranked && (st = check_rank_offsets(*d, rank_offsets, fn)) != SSM_OK) return st;
   if (tau < 1 || tau > d->window)
     return fail(SSM_E_RANGE, "%s: tau %d not in [1, %d]", fn, tau, d->window);
   if (d->batch == 0) return ok();
-  if (sketch == nullptr) return fail(SSM_E_NULL, "%s: sketch is NULL", fn);
-  if (basis == nullptr) return fail(SSM_E_NULL, "%s: basis is NULL", fn);
+  if (ls && d->sketch_dtype != SSM_SKETCH_F32)
+    return fail(SSM_E_RANGE, "%s: least-squares coefficients need an fp32 sketch", fn);
+  if (sketch == nullptr) return fail(SSM_E_NULL, "%s: %s is NULL", fn, ls ? "sketch_q" : "sketch");
+  if (basis == nullptr) return fail(SSM_E_NULL, "%s: %s is NULL", fn, ls ? "read_map" : "basis");
   if (q == nullptr) return fail(SSM_E_NULL, "%s: q is NULL", fn);
   if (y == nullptr) return fail(SSM_E_NULL, "%s: y is NULL", fn);
   if ((st = check_token(*d, k_t, v_t, decay_t, beta_t, fn)) != SSM_OK) return st;
   if ((st = check_buffers(*d, k_buf, v_buf, decay_buf, beta_buf, fn)) != SSM_OK) return st;
   Sizes z = sizes_of(*d);
   apply_ranks(*d, rank_offsets, z);
+  if (ls) z.basis = z.units * d->rank * d->d_k * 4;  // the per-unit read map
   const bool fused = k_t != nullptr;
-  st = check_arrays(fn, {{sketch, z.sketch, false, "sketch"}, {basis, z.basis, false, "basis"},
+  st = check_arrays(fn, {{sketch, z.sketch, false, ls ? "sketch_q" : "sketch"},
+                         {basis, z.basis, false, ls ? "read_map" : "basis"},
                          {q, z.qk, false, "q"}, {k_t, z.qk, false, "k_t"}, {v_t, z.v, false, "v_t"},
                          {decay_t, z.dtok, false, "decay_t"}, {beta_t, z.btok, false, "beta_t"},
                          {k_buf, z.kbuf, fused, "k_buf"}, {v_buf, z.vbuf, fused, "v_buf"},
@@ -313,7 +328,7 @@ static ssm_status sketch_decode_impl(const char* fn, const ssm_dims* d, const in
   (void)hipGetLastError();
   return launched(ssm::launch_sketch_decode(*d, rank_offsets, sketch, basis, q, k_t, v_t, decay_t, beta_t,
                                             k_buf, v_buf, decay_buf, beta_buf, tau, y,
-                                            reinterpret_cast<hipStream_t>(stream)),
+                                            reinterpret_cast<hipStream_t>(stream), nullptr, ls),
                   fn);
 }
 
@@ -409,6 +424,26 @@ ssm_status ssm_sketch_decode_step_ranked(const ssm_dims* d, const int32_t* rank_
   return sketch_decode_impl("ssm_sketch_decode_step_ranked", d, rank_offsets, sketch, basis, q,
                             k_t, v_t, decay_t, beta_t, k_buf, v_buf, decay_buf, beta_buf, tau, y,
                             stream, true);
+}
+
+ssm_status ssm_window_update_refresh_ls(const ssm_dims* d, float* state, float* sketch_q,
+                                        float* read_map, const float* basis, const void* k_buf,
+                                        const void* v_buf, const float* decay_buf,
+                                        const float* beta_buf, int32_t n_tokens, void* stream) {
+  return update_refresh_impl("ssm_window_update_refresh_ls", d, nullptr, state, sketch_q, basis,
+                             k_buf, v_buf, decay_buf, beta_buf, n_tokens, stream, false, read_map,
+                             true);
+}
+
+ssm_status ssm_sketch_decode_step_ls(const ssm_dims* d, const float* sketch_q,
+                                     const float* read_map, const void* q, const void* k_t,
+                                     const void* v_t, const float* decay_t,
+                                     const float* beta_t, void* k_buf, void* v_buf,
+                                     float* decay_buf, float* beta_buf, int32_t tau, float* y,
+                                     void* stream) {
+  return sketch_decode_impl("ssm_sketch_decode_step_ls", d, nullptr, sketch_q, read_map, q, k_t,
+                            v_t, decay_t, beta_t, k_buf, v_buf, decay_buf, beta_buf, tau, y,
+                            stream, false, true);
 }
 
 ssm_status ssm_window_update_refresh_varlen(const ssm_dims* d, int32_t num_slots,

@@ -13,7 +13,7 @@ hipError_t launch_sketch_decode_rule(const ssm_dims& d, const int32_t* rank_offs
                                      const void* k_t, const void* v_t, const float* decay_t,
                                      const float* beta_t, void* k_buf, void* v_buf,
                                      float* decay_buf, float* beta_buf, int tau, float* y,
-                                     hipStream_t stream, const Varlen* varlen);
+                                     hipStream_t stream, const Varlen* varlen, bool per_unit_map);
 
 namespace {
 
@@ -103,20 +103,20 @@ hipError_t launch_sketch_decode(const ssm_dims& d, const int32_t* rank_offsets,
                                 const void* k_t, const void* v_t, const float* decay_t,
                                 const float* beta_t, void* k_buf, void* v_buf, float* decay_buf,
                                 float* beta_buf, int tau, float* y, hipStream_t stream,
-                                const Varlen* varlen) {
+                                const Varlen* varlen, bool per_unit_map) {
   switch (d.rule) {
     case SSM_MAMBA2:
       return launch_sketch_decode_rule<MAMBA2>(d, rank_offsets, sketch, basis, q, k_t, v_t,
                                                decay_t, beta_t, k_buf, v_buf, decay_buf,
-                                               beta_buf, tau, y, stream, varlen);
+                                               beta_buf, tau, y, stream, varlen, per_unit_map);
     case SSM_GDN:
       return launch_sketch_decode_rule<GDN>(d, rank_offsets, sketch, basis, q, k_t, v_t, decay_t,
                                             beta_t, k_buf, v_buf, decay_buf, beta_buf, tau, y,
-                                            stream, varlen);
+                                            stream, varlen, per_unit_map);
     case SSM_KDA:
       return launch_sketch_decode_rule<KDA>(d, rank_offsets, sketch, basis, q, k_t, v_t, decay_t,
                                             beta_t, k_buf, v_buf, decay_buf, beta_buf, tau, y,
-                                            stream, varlen);
+                                            stream, varlen, per_unit_map);
   }
   return hipErrorInvalidValue;
 }

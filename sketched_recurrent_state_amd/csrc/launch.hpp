@@ -102,22 +102,27 @@ inline int max_rank_of(const int32_t* rank_offsets, int heads) {
   return m;
 }
 
-// Bytes of dynamic LDS the update kernel needs for n staged tokens and a basis of max_rank rows.
-size_t update_refresh_lds_bytes(const ssm_dims& d, int n_tokens, int max_rank);
+// Bytes of dynamic LDS the update kernel needs for n staged tokens and a basis of max_rank rows
+// (ls: plus the least-squares refresh's work space).
+size_t update_refresh_lds_bytes(const ssm_dims& d, int n_tokens, int max_rank, bool ls);
 
 // varlen != nullptr: per-row slots and token counts (n_tokens is then ignored).
+// read_map != nullptr: the least-squares refresh (fp32 sketch, uniform rank, no varlen).
 hipError_t launch_update_refresh(const ssm_dims& d, const int32_t* rank_offsets, float* state,
                                  void* sketch, const float* basis, const void* k_buf,
                                  const void* v_buf, const float* decay_buf, const float* beta_buf,
                                  int n_tokens, hipStream_t stream,
-                                 const Varlen* varlen = nullptr);
+                                 const Varlen* varlen = nullptr, float* read_map = nullptr);
 
+// per_unit_map: `basis` is a per-unit read map [N][H][r][d_k] (least-squares
+// coefficients) instead of the per-head basis.
 hipError_t launch_sketch_decode(const ssm_dims& d, const int32_t* rank_offsets,
                                 const void* sketch, const float* basis,
                                 const void* q, const void* k_t, const void* v_t,
                                 const float* decay_t, const float* beta_t, void* k_buf,
                                 void* v_buf, float* decay_buf, float* beta_buf, int tau, float* y,
-                                hipStream_t stream, const Varlen* varlen = nullptr);
+                                hipStream_t stream, const Varlen* varlen = nullptr,
+                                bool per_unit_map = false);
 
 hipError_t launch_full_read_decode(const ssm_dims& d, const float* state, const void* q,
                                    const void* k_t, const void* v_t, const float* decay_t,

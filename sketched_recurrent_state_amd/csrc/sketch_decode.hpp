@@ -27,7 +27,11 @@ namespace {
 template <int DK>
 constexpr int sketch_group() { return DK >= 32 ? 32 : 16; }
 
-template <int RULE, int DK, int DV, typename TIN, typename TSK, int WMAX, typename RT, typename RM>
+// MAP: `basis` is a per-unit read map [N][H][r][d_k] (least-squares coefficients,
+// row m giving c_m = row . q~), read from memory like the sketch rows, instead of
+// the head's basis in LDS.
+template <int RULE, int DK, int DV, typename TIN, typename TSK, int WMAX, bool MAP, typename RT,
+          typename RM>
 __global__ void __launch_bounds__(256)
 sketch_decode_kernel(const TSK* __restrict__ sketch, const float* __restrict__ basis,
                      const TIN* __restrict__ q, const TIN* __restrict__ k_t,
@@ -62,6 +66,8 @@ sketch_decode_kernel(const TSK* __restrict__ sketch, const float* __restrict__ b
   float ak[(RULE == KDA) ? WMAX : 1][EK];     // KDA: per-channel gates of each token
   float a_lane = 1.f, b_lane = 1.f;           // scalar gates of token `sub`
   float sk[RCH][EV];
+  float ym[MAP ? RCH : 1][EK];                // MAP: the first read-map rows
+  const float* Yu = basis + (MAP ? punit * (size_t)rank * DK + sub * EK : 0);
   const TSK* Sku = sketch + ((size_t)seq * rt.total() + rt.offset(head)) * DV + sub * EV;
   if (active) {
     qr.load(q + unit * DK + sub * EK);
@@ -84,8 +90,13 @@ sketch_decode_kernel(const TSK* __restrict__ sketch, const float* __restrict__ b
 #pragma unroll
     for (int m = 0; m < RCH; ++m)
       if (m < rank) Vec<TSK, EV>::load(Sku + (size_t)m * DV, sk[m]);
+    if constexpr (MAP) {
+#pragma unroll
+      for (int m = 0; m < RCH; ++m)
+        if (m < rank) Vec<float, EK>::load(Yu + (size_t)m * DK, ym[m]);
+    }
   }
-  {
+  if constexpr (!MAP) {
     const float* Bh = basis + (size_t)rt.offset(head) * DK;
     for (int e = threadIdx.x * 4; e < rank * DK; e += 256 * 4)
       *reinterpret_cast<float4*>(lB + e) = *reinterpret_cast<const float4*>(Bh + e);
@@ -138,21 +149,30 @@ sketch_decode_kernel(const TSK* __restrict__ sketch, const float* __restrict__ b
       }
     }
   }
-  __syncthreads();  // the basis is in LDS
+  if constexpr (!MAP) __syncthreads();  // the basis is in LDS
   if (!active) return;
 
   // ---- c_m = b_m . q~ ; y = intra + sum_m c_m Sk[m] ----
   for (int m0 = 0; m0 < rank; m0 += RCH) {
     if (m0 > 0) {
 #pragma unroll
-      for (int m = 0; m < RCH; ++m)
-        if (m0 + m < rank) Vec<TSK, EV>::load(Sku + (size_t)(m0 + m) * DV, sk[m]);
+      for (int m = 0; m < RCH; ++m) {
+        if (m0 + m < rank) {
+          Vec<TSK, EV>::load(Sku + (size_t)(m0 + m) * DV, sk[m]);
+          if constexpr (MAP) Vec<float, EK>::load(Yu + (size_t)(m0 + m) * DK, ym[m]);
+        }
+      }
     }
 #pragma unroll
     for (int m = 0; m < RCH; ++m) {
       if (m0 + m < rank) {
         float bm[EK];
-        Vec<float, EK>::load(lB + (m0 + m) * DK + sub * EK, bm);
+        if constexpr (MAP) {
+#pragma unroll
+          for (int e = 0; e < EK; ++e) bm[e] = ym[m][e];
+        } else {
+          Vec<float, EK>::load(lB + (m0 + m) * DK + sub * EK, bm);
+        }
         float c = 0.f;
 #pragma unroll
         for (int e = 0; e < EK; ++e) c = fmaf(bm[e], u[e], c);
@@ -173,7 +193,7 @@ hipError_t launch_sketch_decode_rule(const ssm_dims& d, const int32_t* rank_offs
                                 const void* k_t, const void* v_t, const float* decay_t,
                                 const float* beta_t, void* k_buf, void* v_buf, float* decay_buf,
                                 float* beta_buf, int tau, float* y, hipStream_t stream,
-                                const Varlen* varlen) {
+                                const Varlen* varlen, bool per_unit_map) {
   const int max_rank = rank_offsets ? max_rank_of(rank_offsets, d.heads) : d.rank;
   return dispatch_shape(d.in_dtype, d.d_k, d.d_v, [&](auto DK, auto DV, auto T) {
     using TIN = typename decltype(T)::type;
@@ -181,12 +201,28 @@ hipError_t launch_sketch_decode_rule(const ssm_dims& d, const int32_t* rank_offs
     constexpr unsigned UPB = 256u / sketch_group<kDK>();
     const unsigned blocks = (unsigned)d.heads * (((unsigned)d.batch + UPB - 1) / UPB);
     const size_t lds = (size_t)max_rank * kDK * sizeof(float);
+    if (per_unit_map) {  // least squares: fp32 sketch, uniform rank, lockstep (checked)
+      auto go_map = [&](auto wmax) {
+        constexpr int kW = decltype(wmax)::value;
+        hipLaunchKernelGGL(
+            (sketch_decode_kernel<kR, kDK, kDV, TIN, float, kW, true, UniformRank, Lockstep>),
+            dim3(blocks), dim3(256), 0, stream, static_cast<const float*>(sketch), basis,
+            static_cast<const TIN*>(q), static_cast<const TIN*>(k_t),
+            static_cast<const TIN*>(v_t), decay_t, beta_t, static_cast<TIN*>(k_buf),
+            static_cast<TIN*>(v_buf), decay_buf, beta_buf, y, d.batch, d.heads, d.window,
+            UniformRank{d.rank, d.heads}, Lockstep{tau});
+        return hipGetLastError();
+      };
+      if (d.window <= 4) return go_map(std::integral_constant<int, 4>{});
+      if (d.window <= 8) return go_map(std::integral_constant<int, 8>{});
+      return go_map(std::integral_constant<int, 16>{});
+    }
     return with_sketch_type(d, [&](auto SK) {
       using TSK = typename decltype(SK)::type;
       auto go = [&](auto wmax, auto rt, auto rm) {
         constexpr int kW = decltype(wmax)::value;
         hipLaunchKernelGGL(
-            (sketch_decode_kernel<kR, kDK, kDV, TIN, TSK, kW, decltype(rt), decltype(rm)>),
+            (sketch_decode_kernel<kR, kDK, kDV, TIN, TSK, kW, false, decltype(rt), decltype(rm)>),
             dim3(blocks), dim3(256), lds, stream, static_cast<const TSK*>(sketch), basis,
             static_cast<const TIN*>(q), static_cast<const TIN*>(k_t),
             static_cast<const TIN*>(v_t), decay_t, beta_t, static_cast<TIN*>(k_buf),

@@ -6,6 +6,6 @@ namespace ssm {
 template hipError_t launch_sketch_decode_rule<GDN>(
     const ssm_dims&, const int32_t*, const void*, const float*, const void*, const void*,
     const void*, const float*, const float*, void*, void*, float*, float*, int, float*,
-    hipStream_t, const Varlen*);
+    hipStream_t, const Varlen*, bool);
 
 }  // namespace ssm

@@ -25,9 +25,18 @@ namespace ssm {
 
 namespace {
 
-template <int RULE, int DK, int DV, typename TIN, typename TSK, typename RT, typename RM>
+// Rank decisions of the least-squares refresh: a sketch row whose part orthogonal
+// to the rows before it is below this fraction of the largest row norm adds nothing.
+constexpr float kLsRelTol = 1e-5f;
+
+// LS = false: stores Sk = B S (row m = S^T b_m). LS = true (least-squares
+// coefficients): stores instead Q, orthonormal rows spanning the rows of Sk, in
+// `sketch`, and the read map Y = Q S^T [r][d_k] in `rmap`; a read then gives
+// Q^T (Y q~), the projection of S^T q~ on the span of the sketch rows.
+template <int RULE, int DK, int DV, typename TIN, typename TSK, bool LS, typename RT, typename RM>
 __global__ void __launch_bounds__(2 * DV)
 update_refresh_kernel(float* __restrict__ state, TSK* __restrict__ sketch,
+                      float* __restrict__ rmap,
                       const float* __restrict__ basis, const TIN* __restrict__ kbuf,
                       const TIN* __restrict__ vbuf, const float* __restrict__ dbuf,
                       const float* __restrict__ bbuf, int heads, int window, const RT rt,
@@ -98,6 +107,83 @@ update_refresh_kernel(float* __restrict__ state, TSK* __restrict__ sketch,
   // 5. refresh the sketch from the register-resident state: Sk[m] = S^T b_m.
   //    Eight basis rows at a time; the d_k reduction is a reduce-scatter over
   //    the 8 row groups, after which lane group rg holds basis row m0 + rg.
+  // Least-squares refresh, after the rows of Sk are in LDS (lQ):
+  //   a. wave 0 makes them orthonormal: classical Gram-Schmidt, two passes per row
+  //      (the second removes what rounding left of the first); a row whose residual
+  //      is below kLsRelTol of the largest row norm is set to zero;
+  //   b. every wave forms Y = Q S^T over its 32 columns: per row of S a dot product
+  //      of 4 columns, summed over the 8 lanes of the row group (lane bits 0..2);
+  //   c. the waves' partial Y are added in a fixed order and stored with Q.
+  float* lQ = lB + rank * DK;  // [rank][DV] (LS only)
+  float* lP = lQ + rank * DV;  // [DV / 32][rank][DK] per-wave partial Y (LS only)
+  auto ls_epilogue = [&](float* Qu) {
+    __syncthreads();
+    if (wave == 0) {
+      constexpr int EPL = (DV + 63) / 64;  // row elements per lane
+      auto wsum = [](float x) { return group_allreduce<64>(x); };
+      float maxn2 = 0.f;
+      for (int m = 0; m < rank; ++m) {
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+          if (lane + 64 * e < DV) a = fmaf(lQ[m * DV + lane + 64 * e], lQ[m * DV + lane + 64 * e], a);
+        maxn2 = fmaxf(maxn2, wsum(a));
+      }
+      const float thr2 = kLsRelTol * kLsRelTol * maxn2;
+      for (int m = 0; m < rank; ++m) {
+        float x[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) x[e] = lane + 64 * e < DV ? lQ[m * DV + lane + 64 * e] : 0.f;
+        for (int pass = 0; pass < 2; ++pass) {
+          for (int p = 0; p < m; ++p) {  // rows p < m are final: subtract x's part along each
+            float a = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPL; ++e)
+              if (lane + 64 * e < DV) a = fmaf(x[e], lQ[p * DV + lane + 64 * e], a);
+            const float dp = wsum(a);
+#pragma unroll
+            for (int e = 0; e < EPL; ++e)
+              if (lane + 64 * e < DV) x[e] = fmaf(-dp, lQ[p * DV + lane + 64 * e], x[e]);
+          }
+        }
+        float a = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) a = fmaf(x[e], x[e], a);
+        const float n2 = wsum(a);
+        const float scale = n2 > thr2 ? 1.f / sqrtf(n2) : 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e)
+          if (lane + 64 * e < DV) lQ[m * DV + lane + 64 * e] = x[e] * scale;
+      }
+    }
+    __syncthreads();
+    for (int m = 0; m < rank; ++m) {
+      const float4 qm = *reinterpret_cast<const float4*>(lQ + m * DV + col);
+#pragma unroll
+      for (int mm = 0; mm < RPL; ++mm) {
+        float a = qm.x * s[mm].x;
+        a = fmaf(qm.y, s[mm].y, a);
+        a = fmaf(qm.z, s[mm].z, a);
+        a = fmaf(qm.w, s[mm].w, a);
+        a += dpp<DPP_QUAD_1032>(a);  // lane bit 0
+        a += dpp<DPP_QUAD_2301>(a);  // lane bit 1
+        a += __shfl_xor(a, 4);       // lane bit 2
+        // every lane of the row group now holds the 32-column sum for row mm * 8 + rg;
+        // lane cg stores the rows with mm % 8 == cg
+        if ((mm & 7) == cg) lP[(wave * rank + m) * DK + mm * 8 + rg] = a;
+      }
+    }
+    __syncthreads();
+    float* Yu = rmap + unit * (size_t)rank * DK;
+    for (int e = tid; e < rank * DK; e += NT) {
+      float y = 0.f;
+#pragma unroll
+      for (int w = 0; w < DV / 32; ++w) y += lP[w * rank * DK + e];
+      Yu[e] = y;
+    }
+    for (int e = tid; e < rank * DV; e += NT) Qu[e] = lQ[e];
+  };
+
   auto finish = [&]() {
     if (n > 0) {
 #pragma unroll
@@ -139,8 +225,13 @@ update_refresh_kernel(float* __restrict__ state, TSK* __restrict__ sketch,
       res.z = halve8(P[0].z, P[1].z, b3);
       res.w = halve8(P[0].w, P[1].w, b3);
       const int m = m0 + rg;
-      if (m < rank) store4(Sku + (size_t)m * DV + col, res);  // fp32, or bf16 rounded to nearest
+      if constexpr (LS) {
+        if (m < rank) *reinterpret_cast<float4*>(lQ + m * DV + col) = res;
+      } else {
+        if (m < rank) store4(Sku + (size_t)m * DV + col, res);  // fp32, or bf16 rounded to nearest
+      }
     }
+    if constexpr (LS) ls_epilogue(Sku);
   };
 
   if constexpr (RULE == KDA) {
@@ -202,36 +293,46 @@ update_refresh_kernel(float* __restrict__ state, TSK* __restrict__ sketch,
 
 }  // namespace
 
-size_t update_refresh_lds_bytes(const ssm_dims& d, int n, int max_rank) {
+size_t update_refresh_lds_bytes(const ssm_dims& d, int n, int max_rank, bool ls) {
   size_t floats = 0;
   (void)dispatch(d.rule, SSM_IN_F32, d.d_k, d.d_v, [&](auto R, auto DK, auto DV, auto) {
     floats = (size_t)window_lds_floats<decltype(R)::value, decltype(DK)::value,
                                        decltype(DV)::value>(n);
     return hipSuccess;
   });
-  return (floats + (size_t)max_rank * d.d_k) * sizeof(float);
+  // least squares: the sketch rows [r][d_v] and the waves' partial read maps [d_v/32][r][d_k]
+  const size_t ls_floats = ls ? (size_t)max_rank * d.d_v + (size_t)(d.d_v / 32) * max_rank * d.d_k : 0;
+  return (floats + (size_t)max_rank * d.d_k + ls_floats) * sizeof(float);
 }
 
 hipError_t launch_update_refresh(const ssm_dims& d, const int32_t* rank_offsets, float* state,
                                  void* sketch, const float* basis, const void* k_buf,
                                  const void* v_buf, const float* decay_buf, const float* beta_buf,
-                                 int n, hipStream_t stream, const Varlen* varlen) {
+                                 int n, hipStream_t stream, const Varlen* varlen, float* read_map) {
   const unsigned units = (unsigned)d.batch * (unsigned)d.heads;
   int max_rank = 0;
   if (sketch != nullptr) max_rank = rank_offsets ? max_rank_of(rank_offsets, d.heads) : d.rank;
   // a variable-length call can stage up to W tokens per row
-  const size_t lds = update_refresh_lds_bytes(d, varlen ? d.window : n, max_rank);
+  const size_t lds = update_refresh_lds_bytes(d, varlen ? d.window : n, max_rank, read_map != nullptr);
   return dispatch(d.rule, d.in_dtype, d.d_k, d.d_v, [&](auto R, auto DK, auto DV, auto T) {
     using TIN = typename decltype(T)::type;
     constexpr int kR = decltype(R)::value, kDK = decltype(DK)::value, kDV = decltype(DV)::value;
+    if (read_map != nullptr) {  // least squares: fp32 sketch, uniform rank, lockstep (checked)
+      hipLaunchKernelGGL(
+          (update_refresh_kernel<kR, kDK, kDV, TIN, float, true, UniformRank, Lockstep>),
+          dim3(units), dim3(2 * kDV), lds, stream, state, static_cast<float*>(sketch), read_map,
+          basis, static_cast<const TIN*>(k_buf), static_cast<const TIN*>(v_buf), decay_buf,
+          beta_buf, d.heads, d.window, UniformRank{d.rank, d.heads}, Lockstep{n});
+      return hipGetLastError();
+    }
     return with_sketch_type(d, [&](auto SK) {
       using TSK = typename decltype(SK)::type;
       auto go = [&](auto rt, auto rm) {
         hipLaunchKernelGGL(
-            (update_refresh_kernel<kR, kDK, kDV, TIN, TSK, decltype(rt), decltype(rm)>),
-            dim3(units), dim3(2 * kDV), lds, stream, state, static_cast<TSK*>(sketch), basis,
-            static_cast<const TIN*>(k_buf), static_cast<const TIN*>(v_buf), decay_buf, beta_buf,
-            d.heads, d.window, rt, rm);
+            (update_refresh_kernel<kR, kDK, kDV, TIN, TSK, false, decltype(rt), decltype(rm)>),
+            dim3(units), dim3(2 * kDV), lds, stream, state, static_cast<TSK*>(sketch), nullptr,
+            basis, static_cast<const TIN*>(k_buf), static_cast<const TIN*>(v_buf), decay_buf,
+            beta_buf, d.heads, d.window, rt, rm);
         return hipGetLastError();
       };
       if (varlen != nullptr) return go(UniformRank{d.rank, d.heads}, *varlen);

@@ -21,8 +21,9 @@ from typing import Optional
 import torch
 
 from . import (Dims, IN_BF16, KDA, MAMBA2, SKETCH_BF16, buffer_append, full_read_decode_step,
-               rank_offsets, recurrent_decode_step, sketch_decode_step,
-               sketch_decode_step_ranked, window_update_refresh, window_update_refresh_ranked)
+               rank_offsets, recurrent_decode_step, sketch_decode_step, sketch_decode_step_ls,
+               sketch_decode_step_ranked, window_update_refresh, window_update_refresh_ls,
+               window_update_refresh_ranked)
 
 
 class WindowedDecoder:
@@ -36,13 +37,22 @@ class WindowedDecoder:
             separate buffering launch
     ranks:  optional per-head sketch ranks (H values); then basis is fp32 [sum(ranks), d_k]
             and the sketch [N, sum(ranks), d_v]
+    coefficients: "projection" (c = B q~) or "least_squares" (c minimising the error of the
+            window-start read; then `sketch` holds orthonormal sketch rows and `read_map`
+            [N, H, r, d_k] the per-unit map q~ -> c; uniform rank and fp32 sketch only)
     The sketch is kept in dims.sketch_dtype (fp32, or bf16 rounded to nearest).
     """
 
     def __init__(self, dims: Dims, state: torch.Tensor, basis: Optional[torch.Tensor] = None, *,
-                 read: str = "sketch", fused: bool = True, ranks=None):
+                 read: str = "sketch", fused: bool = True, ranks=None,
+                 coefficients: str = "projection"):
         if read not in ("sketch", "full", "both"):
             raise ValueError(read)
+        if coefficients not in ("projection", "least_squares"):
+            raise ValueError(coefficients)
+        self.ls = coefficients == "least_squares"
+        if self.ls and ranks is not None:
+            raise ValueError("least-squares coefficients use a uniform rank")
         if read != "full" and basis is None:
             raise ValueError("a sketch read needs a basis")
         self.d = dims
@@ -58,6 +68,8 @@ class WindowedDecoder:
         sk_dtype = torch.bfloat16 if dims.sketch_dtype == SKETCH_BF16 else torch.float32
         self.sketch = (torch.empty((N,) + rows + (dv,), device=dev, dtype=sk_dtype)
                        if read != "full" else None)
+        self.read_map = (torch.empty((N, H, r, dk), device=dev, dtype=torch.float32)
+                         if self.ls and read != "full" else None)
         self.k_buf = torch.zeros((N, H, W, dk), device=dev, dtype=tin)
         self.v_buf = torch.zeros((N, H, W, dv), device=dev, dtype=tin)
         dshape = (N, H, W, dk) if dims.rule == KDA else (N, H, W)
@@ -71,7 +83,10 @@ class WindowedDecoder:
         bufs = (self.k_buf, self.v_buf, self.decay_buf, self.beta_buf)
         if n_tokens == 0:
             bufs = (None, None, None, None)
-        if self.offsets is not None and self.sketch is not None:
+        if self.read_map is not None:
+            window_update_refresh_ls(self.d, self.state, self.sketch, self.read_map, self.basis,
+                                     *bufs, n_tokens)
+        elif self.offsets is not None and self.sketch is not None:
             window_update_refresh_ranked(self.d, self.offsets, self.state, self.sketch, self.basis,
                                          *bufs, n_tokens)
         else:
@@ -80,7 +95,9 @@ class WindowedDecoder:
 
     def _sketch_read(self, q, tau, y, tok) -> None:
         bufs = (self.k_buf, self.v_buf, self.decay_buf, self.beta_buf)
-        if self.offsets is not None:
+        if self.read_map is not None:
+            sketch_decode_step_ls(self.d, self.sketch, self.read_map, q, *bufs, tau, y, **tok)
+        elif self.offsets is not None:
             sketch_decode_step_ranked(self.d, self.offsets, self.sketch, self.basis, q, *bufs, tau,
                                       y, **tok)
         else:

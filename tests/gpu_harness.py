@@ -86,13 +86,14 @@ class Inputs:
 
 
 def run_gpu(cfg: workloads.Config, inp: Inputs, *, fused: bool = True, check_state_frozen=True,
-            sketch_dtype: str = "f32"):
+            sketch_dtype: str = "f32", coefficients: str = "projection"):
     """Decode all steps with both reads; returns sampled outputs and window snapshots."""
     d = dims_of(cfg, sketch_dtype)
     U, W = cfg.units, cfg.window
     idx = torch.as_tensor(inp.units, device=inp.S0.device)
     state = inp.S0.clone()
-    dec = WindowedDecoder(d, state, inp.basis, read="both", fused=fused)
+    dec = WindowedDecoder(d, state, inp.basis, read="both", fused=fused,
+                          coefficients=coefficients)
     dec.refresh()
     ys, yf = [], []
     S_snap = [state.view(U, -1)[idx].cpu().numpy()]
@@ -121,13 +122,15 @@ def run_gpu(cfg: workloads.Config, inp: Inputs, *, fused: bool = True, check_sta
     return dict(y_sketch=np.stack(ys).astype(np.float64), y_full=np.stack(yf).astype(np.float64),
                 S=np.stack(S_snap).reshape(-1, n, cfg.d_k, cfg.d_v).astype(np.float64),
                 Sk=np.stack(Sk_snap).reshape(-1, n, cfg.rank, cfg.d_v).astype(np.float64),
-                final_state=state, sketch=dec.sketch)
+                final_state=state, sketch=dec.sketch, read_map=dec.read_map)
 
 
-def run_oracle(cfg: workloads.Config, inp: Inputs, threads: int = 0, sketch_bf16: bool = False):
+def run_oracle(cfg: workloads.Config, inp: Inputs, threads: int = 0, sketch_bf16: bool = False,
+               want_ls: bool = False):
     h = inp.host
     return oracle.run(cfg.rule, inp.host_S0, inp.host_basis, h["q"], h["k"], h["v"], h["decay"],
-                      h["beta"], cfg.window, threads=threads, sketch_bf16=sketch_bf16)
+                      h["beta"], cfg.window, threads=threads, sketch_bf16=sketch_bf16,
+                      want_ls=want_ls)
 
 
 def bf16_ulp(x: np.ndarray) -> np.ndarray:

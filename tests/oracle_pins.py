@@ -380,4 +380,53 @@ def pin_bf16_sketch_enters_only_the_sketch_read(L):
                       f"{rule} t={t} u={u} y_sketch shift")
 
 
+# ----------------------------------------------------------------------------
+# least-squares coefficients (the alternative reading of "state-weighted")
+# ----------------------------------------------------------------------------
+def pin_ls_exact_for_rank_one_state(L):
+    """A rank-1 window-start state S = u w^T has outputs along w only, and the sketch
+    rows B S = (B u) w^T span w: the least-squares read is exact in that window, while
+    the projection read c = B q~ is not (q~ is not in the span of B)."""
+    for rule in RULES:
+        p = problem(rule, U=2, dk=6, dv=5, r=2, W=4, T=4, seed=7)
+        rng = np.random.default_rng(3)
+        for u in range(2):
+            p["S0"][u] = np.outer(rng.standard_normal(6), rng.standard_normal(5))
+        out = run(L, p, want_ls=True)
+        close(out["y_ls"], out["y_replay"], 1e-9, f"{rule} rank-1 LS read")
+        err = np.abs(out["y_sketch"] - out["y_replay"]).max()
+        assert err > 1e-3, f"{rule}: the projection read is unexpectedly exact ({err:.2e})"
+
+
+def pin_ls_full_rank_is_exact(L):
+    """r = d_k: the sketch rows span the state's row space, so the read is exact."""
+    for rule in RULES:
+        p = problem(rule, U=2, dk=5, dv=6, r=5, W=3, T=7, seed=8)
+        out = run(L, p, want_ls=True)
+        close(out["y_ls"], out["y_replay"], 1e-9, f"{rule} full-rank LS read")
+
+
+def pin_ls_never_worse_than_projection(L):
+    """Least squares minimises the read error over all c, so per step its error against
+    the exact read is at most that of c = B q~."""
+    for rule in RULES:
+        p = problem(rule, U=3, dk=6, dv=5, r=2, W=3, T=7, seed=9)
+        out = run(L, p, want_ls=True)
+        e_ls = np.linalg.norm(out["y_ls"] - out["y_replay"], axis=-1)
+        e_pr = np.linalg.norm(out["y_sketch"] - out["y_replay"], axis=-1)
+        assert np.all(e_ls <= e_pr + 1e-12), f"{rule}: LS error above the projection's"
+        assert np.any(e_ls < e_pr - 1e-6), f"{rule}: LS never better than the projection"
+
+
+def pin_ls_zero_state(L):
+    """S_win = 0: the sketch is zero, every c gives Sk^T c = 0 and the read is the
+    window term R^T q alone (the rank-deficient case takes the smallest c)."""
+    for rule in RULES:
+        p = problem(rule, U=2, dk=4, dv=3, r=2, W=3, T=3, seed=10)
+        p["S0"][:] = 0.0
+        out = run(L, p, want_ls=True)
+        close(out["y_ls"], out["y_replay"], 1e-12, f"{rule} zero state")
+        close(out["y_ls"], out["y_sketch"], 1e-12, f"{rule} zero state vs projection")
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

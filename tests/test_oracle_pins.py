@@ -49,6 +49,8 @@ MUTANTS = [
      "if (dropped >= 0x8000u) kept += 1u;"),
     ("bf16_truncates", "if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) kept += 1u;",
      "(void)dropped;"),
+    ("carried_query_not_recorded", "if (qt_out) memcpy(qt_out + tu * dk, qt, sizeof(double) * dk);",
+     "if (qt_out) memcpy(qt_out + tu * dk, qv, sizeof(double) * dk);"),
     ("bf16_window_refresh_not_rounded",
      "matmul(r, dk, dv, Bu, Swin, Sk);\n          if (sketch_bf16) round_sketch(sz_k, Sk);",
      "matmul(r, dk, dv, Bu, Swin, Sk);"),

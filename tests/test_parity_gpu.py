@@ -458,3 +458,57 @@ def test_bf16_sketch(cfg):
     ref = H.run_oracle(cfg, inp, sketch_bf16=True)
     H.compare(cfg, got, ref, sketch_bf16=True)
     assert got["sketch"].dtype == torch.bfloat16
+
+
+# Least-squares coefficients: the read is the projection of the exact window-start
+# read on the span of the sketch rows; the refresh stores orthonormal sketch rows Q
+# and the per-unit read map Y = Q S^T.
+LS_CASES = [
+    small("gdn"), small("mamba2", d_k=128, d_v=64), small("kda", W=4, r=8),
+    small("gdn", "f32", d_k=64, d_v=32, W=5, r=3),
+    small("kda", d_k=16, d_v=128, W=1, r=16),   # r = d_k: the read is exact
+    small("gdn", "bf16", d_k=128, d_v=128, W=16, r=32, N=2, Hh=3, T=33),
+]
+
+
+@pytest.mark.parametrize("cfg", LS_CASES, ids=lambda c: c.name)
+def test_least_squares_coefficients(cfg):
+    H.note(f"case least squares {cfg.name}")
+    inp = H.Inputs(cfg, np.arange(cfg.units), cfg.steps)
+    got = H.run_gpu(cfg, inp, coefficients="least_squares")
+    ref = H.run_oracle(cfg, inp, want_ls=True)
+    nw = got["S"].shape[0]
+    e_y = H.rel_rows(got["y_sketch"], ref["y_ls"])
+    e_x = H.rel_rows(got["y_full"], ref["y_exact"])
+    e_S = H.rel_mats(got["S"], ref["S_win"][:nw])
+    # the stored rows are orthonormal and span the oracle's sketch rows
+    Q = got["Sk"]
+    gram = np.einsum("wuij,wukj->wuik", Q, Q)
+    e_orth = np.abs(gram - np.eye(cfg.rank)).max()
+    Sk = ref["Sk"][:nw]
+    resid = Sk - np.einsum("wuij,wujk->wuik", np.einsum("wuij,wukj->wuik", Sk, Q), Q)
+    e_span = float((np.linalg.norm(resid.reshape(nw, cfg.units, -1), axis=-1)
+                    / np.linalg.norm(Sk.reshape(nw, cfg.units, -1), axis=-1)).max())
+    approx_ls = H.rel_rows(ref["y_ls"], ref["y_exact"]).mean()
+    approx_pr = H.rel_rows(ref["y_sketch"], ref["y_exact"]).mean()
+    H.note(f"least squares {cfg.name}: y {e_y.max():.2e} exact {e_x.max():.2e} S {e_S.max():.2e} "
+           f"orth {e_orth:.2e} span {e_span:.2e} approx err {approx_ls:.3f} (projection {approx_pr:.3f})")
+    assert e_y.max() <= H.Y_TOL, f"least-squares read: {e_y.max():.3e}"
+    assert e_x.max() <= H.Y_TOL and e_S.max() <= H.S_TOL
+    assert e_orth <= 1e-5, f"sketch rows not orthonormal: {e_orth:.2e}"
+    assert e_span <= H.S_TOL, f"sketch rows do not span the sketch: {e_span:.2e}"
+    if cfg.rank == cfg.d_k:
+        assert H.rel_rows(got["y_sketch"], ref["y_exact"]).max() <= H.Y_TOL
+
+
+def test_least_squares_zero_state():
+    """A zero state has a zero sketch: every row is dropped and the read is the window
+    term alone, equal to the exact read within the first window."""
+    cfg = small("gdn", N=2, Hh=3, W=4, T=4)
+    inp = H.Inputs(cfg, np.arange(cfg.units), cfg.steps)
+    inp.S0.zero_()
+    inp.host_S0[:] = 0.0
+    got = H.run_gpu(cfg, inp, coefficients="least_squares")
+    assert np.all(got["Sk"][0] == 0.0)
+    e = H.rel_rows(got["y_sketch"], got["y_full"])
+    assert e.max() <= H.Y_TOL, f"{e.max():.2e}"
