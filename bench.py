@@ -48,8 +48,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def bytes_model(cfg, sk_bytes: int = 4) -> dict:
-    """Algorithmic HBM bytes per unit (sequence, head); sk_bytes per sketch element."""
+def bytes_model(cfg, sk_bytes: int = 4, ls: bool = False) -> dict:
+    """Algorithmic HBM bytes per unit (sequence, head); sk_bytes per sketch element;
+    ls: least-squares coefficients (the per-unit read map [r][d_k] fp32 is written by
+    the update and read every step)."""
     s_in = 2 if cfg.in_dtype == "bf16" else 4
     g = {"mamba2": 4, "gdn": 8, "kda": 4 * cfg.d_k + 4}[cfg.rule]
     tok = (cfg.d_k + cfg.d_v) * s_in + g
@@ -58,9 +60,10 @@ def bytes_model(cfg, sk_bytes: int = 4) -> dict:
     # per decode step: q + the current token (appended: read once, written once)
     #   + the older buffered tokens + y; plus the sketch or the full state
     step_common = dk * s_in + tok + (tau_mean - 1) * tok + tok + 4 * dv
-    sketch_step = sk_bytes * r * dv + step_common
+    rmap = 4 * r * dk if ls else 0
+    sketch_step = sk_bytes * r * dv + rmap + step_common
     full_step = 4 * dk * dv + step_common
-    update = 8 * dk * dv + sk_bytes * r * dv + W * tok   # read S, write S, write Sk, read buffer
+    update = 8 * dk * dv + sk_bytes * r * dv + rmap + W * tok  # S in and out, Sk (+map), buffer
     update_no_refresh = 8 * dk * dv + W * tok
     return dict(tok=tok, sketch_step=sketch_step, full_step=full_step, update=update,
                 update_no_refresh=update_no_refresh,
@@ -96,6 +99,8 @@ def main() -> int:
                     help="per-head sketch ranks (avg8: 2, 4, 8, 18 cycled over heads, mean 8)")
     ap.add_argument("--sketch-dtype", choices=["f32", "bf16"], default="f32",
                     help="storage type of the sketch (the headline workload keeps fp32)")
+    ap.add_argument("--coefficients", choices=["projection", "least_squares"],
+                    default="projection", help="sketch-read coefficients (headline: projection)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="profiling: copy MIB MiB with a plain device copy kernel, then exit")
     a = ap.parse_args()
@@ -176,7 +181,22 @@ def main() -> int:
     kb, vb, db, bb = (P(x) for x in bufs)
     yp, bp = P(y), P(basis)
 
-    if ranks is None:
+    ls = a.coefficients == "least_squares"
+    if ls and (ranks is not None or a.schedule != "lockstep" or a.sketch_dtype != "f32"):
+        print("least-squares coefficients run with uniform ranks, lockstep and an fp32 sketch",
+              file=sys.stderr)
+        return 2
+    rmaps = {}  # sketch address -> its read map (least squares)
+
+    def _addr(x):
+        return x if isinstance(x, int) else x.data_ptr()
+
+    if ls:
+        sketch_step = lambda sk, b, *x, **kw: ssm.sketch_decode_step_ls(
+            d, sk, rmaps[_addr(sk)], *x, **kw)
+        update_refresh = lambda st, sk, b, *x, **kw: ssm.window_update_refresh_ls(
+            d, st, sk, rmaps[_addr(sk)], b, *x, **kw)
+    elif ranks is None:
         sketch_step = lambda *x, **kw: ssm.sketch_decode_step(d, *x, **kw)
         update_refresh = lambda *x, **kw: ssm.window_update_refresh(d, *x, **kw)
     else:
@@ -242,13 +262,16 @@ def main() -> int:
         return timed(g.replay), g
 
     sp = stream.cuda_stream
-    bm = bytes_model(cfg, 2 if a.sketch_dtype == "bf16" else 4)
+    bm = bytes_model(cfg, 2 if a.sketch_dtype == "bf16" else 4, ls)
 
     # ---- the sketch path, eager launches (update kernel timed by HIP events) ---------
     state = S0_dev.clone()
     sk_rows = cfg.heads * cfg.rank if ranks is None else sum(ranks)
     sk_dtype = torch.bfloat16 if a.sketch_dtype == "bf16" else torch.float32
     sketch = torch.empty((cfg.batch, sk_rows, cfg.d_v), device=dev, dtype=sk_dtype)
+    if ls:
+        rm_main = torch.empty((cfg.batch, cfg.heads, cfg.rank, cfg.d_k), device=dev)
+        rmaps[sketch.data_ptr()] = rm_main.data_ptr()
     st_p, sk_p = P(state), P(sketch)
     update_refresh(st_p, sk_p, bp, None, None, None, None, 0, stream=sp)
     run_sketch(st_p, sk_p, 0, a.warmup, sp, only=a.only)
@@ -366,6 +389,9 @@ def main() -> int:
     # ---- approximation error of the sketch read vs the exact read (untimed) -----------
     st_a = S0_dev.clone()
     sk_a = torch.empty_like(sketch)
+    if ls:
+        rm_a = torch.empty((cfg.batch, cfg.heads, cfg.rank, cfg.d_k), device=dev)
+        rmaps[sk_a.data_ptr()] = rm_a.data_ptr()
     update_refresh(st_a, sk_a, basis, None, None, None, None, 0, stream=stream)
     errs = []
     y_f = torch.empty_like(y)
@@ -410,7 +436,7 @@ def main() -> int:
         # ... nor does a run on another workload (the counters are for the lockstep,
         # uniform-rank, fp32-sketch decode of that config)
         same_workload = (tr.get("config") == cfg.name and a.schedule == "lockstep"
-                         and ranks is None and a.sketch_dtype == "f32")
+                         and ranks is None and a.sketch_dtype == "f32" and not ls)
         if tr.get("kernel_source_hash") == kernel_source_hash() and same_workload:
             traffic = float(tr["bytes_per_launch"])
 
@@ -456,7 +482,7 @@ def main() -> int:
                    "heads": cfg.heads, "d_k": cfg.d_k, "d_v": cfg.d_v, "window": W,
                    "rank": cfg.rank if ranks is None else f"per head {sorted(set(ranks))}, mean "
                    f"{sum(ranks) / len(ranks):g}", "inputs": cfg.in_dtype, "state": "f32",
-                   "sketch": a.sketch_dtype},
+                   "sketch": a.sketch_dtype, "coefficients": a.coefficients},
         "roofline": {"bound": "hbm", "kernel": "update_refresh_kernel", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "bytes_per_launch": upd_bytes,
