@@ -512,3 +512,51 @@ def test_least_squares_zero_state():
     assert np.all(got["Sk"][0] == 0.0)
     e = H.rel_rows(got["y_sketch"], got["y_full"])
     assert e.max() <= H.Y_TOL, f"{e.max():.2e}"
+
+
+@pytest.mark.parametrize("rule", ["gdn", "kda"])
+def test_graph_replay_matches_eager(rule):
+    """One window of decode steps (fused appends, sketch reads, the update with the refresh)
+    captured in a HIP graph gives, on every replay, exactly the eager outputs, state and
+    sketch. Between replays the state is restored and the sketch refreshed eagerly."""
+    cfg = small(rule, N=8, Hh=4, W=4, T=4)
+    H.note(f"case graph replay {rule}")
+    inp = H.Inputs(cfg, np.arange(cfg.units), cfg.steps)
+    d = H.dims_of(cfg)
+    W = cfg.window
+
+    def fresh():
+        state = inp.S0.clone()
+        dec = WindowedDecoder(d, state, inp.basis, read="sketch")
+        dec.refresh()
+        return state, dec
+
+    ys = [torch.empty((cfg.batch, cfg.heads, cfg.d_v), device="cuda") for _ in range(W)]
+    state_e, dec_e = fresh()
+    for t in range(W):
+        dec_e.step(inp.q[t], inp.k[t], inp.v[t], inp.decay[t], inp.beta[t], y=ys[t])
+    torch.cuda.synchronize()
+    want_y = [y.clone() for y in ys]
+    want_S, want_Sk = state_e.clone(), dec_e.sketch.clone()
+
+    state_g, dec_g = fresh()
+    gy = [torch.empty_like(y) for y in ys]
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for t in range(W):
+            dec_g.step(inp.q[t], inp.k[t], inp.v[t], inp.decay[t], inp.beta[t], y=gy[t])
+    torch.cuda.synchronize()
+    for rep in range(3):
+        state_g.copy_(inp.S0)
+        dec_g.tau = 0
+        dec_g.refresh()
+        torch.cuda.synchronize()
+        for y in gy:
+            y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for t in range(W):
+            assert torch.equal(gy[t], want_y[t]), f"replay {rep}: step {t} output differs"
+        assert torch.equal(state_g, want_S), f"replay {rep}: state differs"
+        assert torch.equal(dec_g.sketch, want_Sk), f"replay {rep}: sketch differs"
