@@ -377,63 +377,111 @@ __host__ __device__ __forceinline__ int interleaved_pos(int i) {
   return (i & 7) * (DK / 8) + (i >> 3);
 }
 
-// Cooperative copy by the NT threads of a workgroup. With a fused append the
-// newest slot (n - 1) is read from the current token and also written into
-// the buffer. With PERM the d_k-indexed rows (keys, and KDA's per-row gates)
-// are stored in interleaved_pos order. The caller synchronises the workgroup
+// Cooperative copy by the NT threads of a workgroup, in two phases so that a
+// caller can issue other loads in between: issue() starts every thread's first
+// chunk of each array (keys, values, gates, beta), so the whole window costs one
+// memory round trip; commit() writes those chunks to LDS and copies any further
+// ones (windows longer than one chunk per thread) directly. Loads are clamped
+// into the window, so every lane issues the same instructions (the wait counts
+// stay exact); only lanes in range store. With a fused append the newest slot
+// (n - 1) is read from the current token and also written into the buffer. With
+// PERM the d_k-indexed rows (keys, and KDA's per-row gates) are stored in
+// interleaved_pos order. Requires n >= 1; the caller synchronises the workgroup
 // before reading the LDS.
 template <int RULE, int DK, int DV, typename TIN, int NT, bool PERM = false>
-__device__ __forceinline__ void stage_window(float* lds, const UnitWindow<TIN>& uw, int n,
-                                             int tid) {
-  constexpr int DSTR = (RULE == KDA) ? DK : 1;
-  constexpr int VIN = 16 / sizeof(TIN);
-  float* lk = lds;
-  float* lv = lk + n * DK;
-  float* ld = lv + n * DV;
-  float* lb = ld + pad4(n * DSTR);
-  const bool fused = uw.kt != nullptr;
-  const int last = n - 1;
-  for (int e = tid * VIN; e < n * DK; e += NT * VIN) {
-    const bool cur = fused && (e / DK == last);
-    Packed<TIN, VIN> x;
-    x.load(cur ? uw.kt + (e - last * DK) : uw.k + e);
-    if (cur) x.store(uw.k + e);
-    float f[VIN];
-    x.unpack(f);
-    if constexpr (PERM) {
-      const int t0 = e - e % DK, i0 = e % DK;
+struct WindowStage {
+  static constexpr int DSTR = (RULE == KDA) ? DK : 1;
+  static constexpr int VIN = 16 / sizeof(TIN);       // input elements per chunk
+  static constexpr int VG = (RULE == KDA) ? 4 : 1;   // gate elements per chunk
+  Packed<TIN, VIN> k0, v0;
+  float g0[VG];
+  float b0 = 0.f;
+
+  // source of the chunk at element e of a [n][len] array: the buffer, or the
+  // current token for the newest slot of a fused append
+  template <typename T>
+  static __device__ __forceinline__ const T* src(const T* buf, const T* cur, int e, int len,
+                                                 int last, bool fused) {
+    return (fused && e / len == last) ? cur + (e - last * len) : buf + e;
+  }
+
+  __device__ __forceinline__ void issue(const UnitWindow<TIN>& uw, int n, int tid) {
+    const bool fused = uw.kt != nullptr;
+    const int last = n - 1;
+    k0.load(src<TIN>(uw.k, uw.kt, min(tid * VIN, n * DK - VIN), DK, last, fused));
+    v0.load(src<TIN>(uw.v, uw.vt, min(tid * VIN, n * DV - VIN), DV, last, fused));
+    Vec<float, VG>::load(src<float>(uw.d, uw.dt, min(tid * VG, n * DSTR - VG), DSTR, last, fused),
+                         g0);
+    if constexpr (RULE != MAMBA2) b0 = *src<float>(uw.b, uw.bt, min(tid, last), 1, last, fused);
+  }
+
+  __device__ __forceinline__ void commit(float* lds, const UnitWindow<TIN>& uw, int n,
+                                         int tid) const {
+    float* lk = lds;
+    float* lv = lk + n * DK;
+    float* ld = lv + n * DV;
+    float* lb = ld + pad4(n * DSTR);
+    const bool fused = uw.kt != nullptr;
+    const int last = n - 1;
+    auto put_k = [&](const Packed<TIN, VIN>& x, int e) {
+      if (fused && e / DK == last) x.store(uw.k + e);
+      float f[VIN];
+      x.unpack(f);
+      if constexpr (PERM) {
+        const int t0 = e - e % DK, i0 = e % DK;
 #pragma unroll
-      for (int j = 0; j < VIN; ++j) lk[t0 + interleaved_pos<DK>(i0 + j)] = f[j];
-    } else {
-      Vec<float, VIN>::store(lk + e, f);
-    }
-  }
-  for (int e = tid * VIN; e < n * DV; e += NT * VIN) {
-    const bool cur = fused && (e / DV == last);
-    Packed<TIN, VIN> x;
-    x.load(cur ? uw.vt + (e - last * DV) : uw.v + e);
-    if (cur) x.store(uw.v + e);
-    float f[VIN];
-    x.unpack(f);
-    Vec<float, VIN>::store(lv + e, f);
-  }
-  for (int e = tid; e < n * DSTR; e += NT) {
-    const bool cur = fused && (e / DSTR == last);
-    const float x = cur ? uw.dt[e - last * DSTR] : uw.d[e];
-    if (cur) uw.d[e] = x;
-    if constexpr (PERM && RULE == KDA)
-      ld[e - e % DK + interleaved_pos<DK>(e % DK)] = x;
-    else
-      ld[e] = x;
-  }
-  if constexpr (RULE != MAMBA2) {
-    for (int e = tid; e < n; e += NT) {
-      const bool cur = fused && (e == last);
-      const float x = cur ? uw.bt[0] : uw.b[e];
-      if (cur) uw.b[e] = x;
+        for (int j = 0; j < VIN; ++j) lk[t0 + interleaved_pos<DK>(i0 + j)] = f[j];
+      } else {
+        Vec<float, VIN>::store(lk + e, f);
+      }
+    };
+    auto put_v = [&](const Packed<TIN, VIN>& x, int e) {
+      if (fused && e / DV == last) x.store(uw.v + e);
+      float f[VIN];
+      x.unpack(f);
+      Vec<float, VIN>::store(lv + e, f);
+    };
+    auto put_g = [&](const float* g, int e) {
+      if (fused && e / DSTR == last) Vec<float, VG>::store(uw.d + e, g);
+      if constexpr (PERM && RULE == KDA) {
+        const int t0 = e - e % DK, i0 = e % DK;
+#pragma unroll
+        for (int j = 0; j < VG; ++j) ld[t0 + interleaved_pos<DK>(i0 + j)] = g[j];
+      } else {
+        Vec<float, VG>::store(ld + e, g);
+      }
+    };
+    auto put_b = [&](float x, int e) {
+      if (fused && e == last) uw.b[e] = x;
       lb[e] = x;
+    };
+    // the chunks issue() fetched
+    if (tid * VIN < n * DK) put_k(k0, tid * VIN);
+    if (tid * VIN < n * DV) put_v(v0, tid * VIN);
+    if (tid * VG < n * DSTR) put_g(g0, tid * VG);
+    if constexpr (RULE != MAMBA2) {
+      if (tid < n) put_b(b0, tid);
+    }
+    // the rest, for windows longer than one chunk per thread
+    for (int e = (tid + NT) * VIN; e < n * DK; e += NT * VIN) {
+      Packed<TIN, VIN> x;
+      x.load(src<TIN>(uw.k, uw.kt, e, DK, last, fused));
+      put_k(x, e);
+    }
+    for (int e = (tid + NT) * VIN; e < n * DV; e += NT * VIN) {
+      Packed<TIN, VIN> x;
+      x.load(src<TIN>(uw.v, uw.vt, e, DV, last, fused));
+      put_v(x, e);
+    }
+    for (int e = (tid + NT) * VG; e < n * DSTR; e += NT * VG) {
+      float g[VG];
+      Vec<float, VG>::load(src<float>(uw.d, uw.dt, e, DSTR, last, fused), g);
+      put_g(g, e);
+    }
+    if constexpr (RULE != MAMBA2) {
+      for (int e = tid + NT; e < n; e += NT) put_b(*src<float>(uw.b, uw.bt, e, 1, last, fused), e);
     }
   }
-}
+};
 
 }  // namespace ssm

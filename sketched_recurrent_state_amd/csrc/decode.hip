@@ -19,9 +19,10 @@ namespace {
 
 // ---------------------------------------------------------------------------
 // exact read of the window-start state: the state tile layout, one workgroup
-// per unit. The state loads are issued first; the window is staged in LDS
-// meanwhile and every wave walks it on its own (no synchronisation after the
-// staging barrier).
+// per unit. The query and the window are fetched first (the walk needs them
+// first, and small reads issued behind a 64 KB state stream wait for all of
+// it); the state loads follow and land while every wave walks the buffer on
+// its own (no synchronisation after the staging barrier).
 // ---------------------------------------------------------------------------
 template <int RULE, int DK, int DV, typename TIN>
 __global__ void __launch_bounds__(2 * DV)
@@ -47,11 +48,6 @@ full_read_kernel(const float* __restrict__ state, const TIN* __restrict__ q,
   const size_t slot0 = (size_t)unit * window;
   const bool fused = (k_t != nullptr);
 
-  const float* Su = state + (size_t)unit * (DK * DV);
-  float4 s[RPL];
-#pragma unroll
-  for (int m = 0; m < RPL; ++m)
-    s[m] = load_stream(Su + (size_t)(row0 + m) * DV + col);
   float u[RPL];
   Vec<TIN, RPL>::load(q + (size_t)unit * DK + row0, u);
 
@@ -61,7 +57,14 @@ full_read_kernel(const float* __restrict__ state, const TIN* __restrict__ q,
                      fused ? v_t + (size_t)unit * DV : nullptr,
                      fused ? d_t + (size_t)unit * DSTR : nullptr,
                      (fused && RULE != MAMBA2) ? b_t + unit : nullptr};
-  stage_window<RULE, DK, DV, TIN, NT>(lds, uw, tau, tid);
+  WindowStage<RULE, DK, DV, TIN, NT> stage;
+  stage.issue(uw, tau, tid);
+  const float* Su = state + (size_t)unit * (DK * DV);
+  float4 s[RPL];
+#pragma unroll
+  for (int m = 0; m < RPL; ++m)
+    s[m] = load_stream(Su + (size_t)(row0 + m) * DV + col);
+  stage.commit(lds, uw, tau, tid);
   __syncthreads();
   const float* lk = lds;
   const float* lv = lk + tau * DK;

@@ -28,15 +28,19 @@ recurrent_step_kernel(float* __restrict__ state, const TIN* __restrict__ q,
   const int col = wave * 32 + cg * 4;
   const int row0 = rg * RPL;
 
-  float* Su = state + (size_t)unit * (DK * DV);
-  float4 s[RPL];
-#pragma unroll
-  for (int m = 0; m < RPL; ++m) s[m] = load_stream(Su + (size_t)(row0 + m) * DV + col);
+  // the token's small inputs first: issued behind the 64 KB state stream they
+  // would wait for all of it
   float kr[RPL], qr[RPL], vv[4];
   Vec<TIN, RPL>::load(k_t + (size_t)unit * DK + row0, kr);
   Vec<TIN, RPL>::load(q + (size_t)unit * DK + row0, qr);
   Vec<TIN, 4>::load(v_t + (size_t)unit * DV + col, vv);
   const float4 v4 = make_float4(vv[0], vv[1], vv[2], vv[3]);
+  float ar[(RULE == KDA) ? RPL : 1];  // KDA's per-row gates
+  if constexpr (RULE == KDA) Vec<float, RPL>::load(d_t + (size_t)unit * DK + row0, ar);
+  float* Su = state + (size_t)unit * (DK * DV);
+  float4 s[RPL];
+#pragma unroll
+  for (int m = 0; m < RPL; ++m) s[m] = load_stream(Su + (size_t)(row0 + m) * DV + col);
 
   // S <- M S + b k v^T
   if constexpr (RULE == MAMBA2) {
@@ -53,8 +57,6 @@ recurrent_step_kernel(float* __restrict__ state, const TIN* __restrict__ q,
 #pragma unroll
     for (int m = 0; m < RPL; ++m) s[m] = fma4(kr[m], w, scale4(a, s[m]));
   } else {
-    float ar[RPL];
-    Vec<float, RPL>::load(d_t + (size_t)unit * DK + row0, ar);
     const float b = b_t[unit];
     float4 p = f4(0.f);
 #pragma unroll

@@ -65,46 +65,57 @@ update_refresh_kernel(float* __restrict__ state, TSK* __restrict__ sketch,
   // keep this lane's d_k / 8 values at [row0, row0 + RPL) (interleaved_pos).
   const int row0 = rg * RPL;
 
-  // 1. issue the loads of this lane's state piece (the only HBM read of S)
-  float* Su = state + (size_t)unit * (DK * DV);
-  float4 s[RPL];
-#pragma unroll
-  for (int m = 0; m < RPL; ++m)
-    s[m] = load_stream(Su + (size_t)(m * 8 + rg) * DV + col);
-
-  // 2. stage the window (and the basis) in LDS as fp32
+  // 1. issue the staging reads: the window's tokens and the head's basis (each
+  //    thread's first chunk of every array, one memory round trip in all)
   const size_t slot0 = (size_t)unit * window;
   UnitWindow<TIN> uw{const_cast<TIN*>(kbuf) + slot0 * DK, const_cast<TIN*>(vbuf) + slot0 * DV,
                      const_cast<float*>(dbuf) + slot0 * DSTR,
                      (RULE == MAMBA2) ? nullptr : const_cast<float*>(bbuf) + slot0,
                      nullptr, nullptr, nullptr, nullptr};
-  if (n > 0) stage_window<RULE, DK, DV, TIN, NT, true>(lds, uw, n, tid);
+  WindowStage<RULE, DK, DV, TIN, NT, true> stage;
+  if (n > 0) stage.issue(uw, n, tid);
+  const float* Bh = basis + (size_t)rt.offset(head) * DK;
+  float4 b4 = f4(0.f);
+  if (sketch != nullptr) b4 = *reinterpret_cast<const float4*>(Bh + min(tid * 4, rank * DK - 4));
+  // 2. then the loads of this lane's state piece (the only HBM read of S). In
+  //    this order the small staging reads are served first; issued behind the
+  //    unit's 64 KB stream they would wait for it, and for every other
+  //    workgroup's: then all workgroups start computing at once and HBM idles
+  //    meanwhile (about 10% of the kernel's time at 128 x 128).
+  float* Su = state + (size_t)unit * (DK * DV);
+  float4 s[RPL];
+#pragma unroll
+  for (int m = 0; m < RPL; ++m)
+    s[m] = load_stream(Su + (size_t)(m * 8 + rg) * DV + col);
+  // 3. the staged data to LDS as fp32 while the state is in flight
+  if (n > 0) stage.commit(lds, uw, n, tid);
   const float* lk = lds;
   const float* lv = lk + n * DK;
   const float* ld = lv + n * DV;
   const float* lb = ld + pad4(n * DSTR);
   float* lB = lds + window_lds_floats<RULE, DK, DV>(n);  // [rank][DK]
   if (sketch != nullptr) {
-    const float* Bh = basis + (size_t)rt.offset(head) * DK;
-    for (int e = tid * 4; e < rank * DK; e += NT * 4) {
-      const float4 x4 = *reinterpret_cast<const float4*>(Bh + e);
+    auto put = [&](float4 x4, int e) {
       float* row = lB + (e - e % DK);
       const int i0 = e % DK;
       row[interleaved_pos<DK>(i0)] = x4.x;
       row[interleaved_pos<DK>(i0 + 1)] = x4.y;
       row[interleaved_pos<DK>(i0 + 2)] = x4.z;
       row[interleaved_pos<DK>(i0 + 3)] = x4.w;
-    }
+    };
+    if (tid * 4 < rank * DK) put(b4, tid * 4);
+    for (int e = (tid + NT) * 4; e < rank * DK; e += NT * 4)
+      put(*reinterpret_cast<const float4*>(Bh + e), e);
   }
   __syncthreads();
 
-  // 3. the window's tokens, in order: S <- M_t S + b_t k_t v_t^T on the
+  // 4. the window's tokens, in order: S <- M_t S + b_t k_t v_t^T on the
   //    register-resident piece; the k^T S reduction over d_k crosses the 8
   //    lanes that share this lane's columns. Mamba-2 and GDN carry a scaled
   //    copy of the piece so the per-token decay costs nothing (below); KDA
   //    decays rows by different gates and updates S directly.
-  // 4. write the state back (the only HBM write of S), then
-  // 5. refresh the sketch from the register-resident state: Sk[m] = S^T b_m.
+  // 5. write the state back (the only HBM write of S), then
+  // 6. refresh the sketch from the register-resident state: Sk[m] = S^T b_m.
   //    Eight basis rows at a time; the d_k reduction is a reduce-scatter over
   //    the 8 row groups, after which lane group rg holds basis row m0 + rg.
   // Least-squares refresh, after the rows of Sk are in LDS (lQ):
