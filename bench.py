@@ -80,6 +80,18 @@ def metric_name(cfg) -> str:
             f"state, B={cfg.batch}, H={cfg.heads}, W={cfg.window}, r={cfg.rank}")
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (Linux), for the CPU-baseline record."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -88,6 +100,8 @@ def main() -> int:
     ap.add_argument("--config", default="c3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compare", action="store_true", help="skip the full-read comparison pass")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache (Infinity Cache flushed) kernel timings")
     ap.add_argument("--cpu-units", type=int, default=512, help="oracle sample: units")
     ap.add_argument("--cpu-steps", type=int, default=16, help="oracle sample: decode steps")
     ap.add_argument("--only", choices=["sketch", "full", "update"], default=None,
@@ -422,6 +436,53 @@ def main() -> int:
     copy_gbs = 2 * n_copy * 4 / (copy_ms * 1e-3) / 1e9
     del src, dst
 
+    # ---- cold-cache kernel times: the 256 MB Infinity Cache flushed before each launch ----
+    # A 512 MiB read between launches, outside the events, replaces the cached lines with
+    # clean ones. (A write would leave them dirty, and the timed kernel would pay for their
+    # write-back.) Without a flush, part of the sketch step's working set, and of the state
+    # the previous update wrote, is served from that cache.
+    cold = None
+    if not a.no_cold:
+        flush = torch.ones((512 << 20) // 4, device=dev)
+        flush_sum = torch.empty((), device=dev)
+        st_c, sk_c = S0_dev.clone(), torch.empty_like(sketch)
+        if ls:
+            rm_c = torch.empty((cfg.batch, cfg.heads, cfg.rank, cfg.d_k), device=dev)
+            rmaps[sk_c.data_ptr()] = rm_c.data_ptr()
+        update_refresh(st_c, sk_c, basis, None, None, None, None, 0, stream=stream)
+
+        def cold_time(launch, reps=5):
+            evs = []
+            launch()
+            for i in range(reps):
+                torch.sum(flush, dim=0, out=flush_sum)
+                s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                s_.record(stream)
+                launch()
+                e_.record(stream)
+                evs.append((s_, e_))
+            torch.cuda.synchronize()
+            return float(np.mean([s_.elapsed_time(e_) for s_, e_ in evs]))
+
+        stc_p, skc_p = P(st_c), P(sk_c)
+        c_upd = cold_time(lambda: update_refresh(stc_p, skc_p, bp, kb, vb, db, bb, W, stream=sp))
+        c_sk = cold_time(lambda: sketch_step(skc_p, bp, q0, kb, vb, db, bb, tau_mid, yp, stream=sp))
+        c_full = cold_time(lambda: ssm.full_read_decode_step(d, stc_p, q0, kb, vb, db, bb,
+                                                             tau_mid, yp, stream=sp))
+        # bytes of one read at window position tau_mid, the token already buffered (no append):
+        # q + tau_mid buffered tokens + y, plus the sketch (and read map) or the full state
+        s_in = 2 if cfg.in_dtype == "bf16" else 4
+        common = cfg.d_k * s_in + tau_mid * bm["tok"] + 4 * cfg.d_v
+        sk_b = U * (bm["state_bytes_sketch"] + (4 * cfg.rank * cfg.d_k if ls else 0) + common)
+        full_b = U * (bm["state_bytes_full"] + common)
+        cold = {"flush_bytes": flush.numel() * 4, "tau": tau_mid,
+                "update_refresh_ms": c_upd, "update_refresh_gbs": bm["update"] * U / (c_upd * 1e-3) / 1e9,
+                "sketch_decode_ms": c_sk, "sketch_decode_gbs": sk_b / (c_sk * 1e-3) / 1e9,
+                "full_read_decode_ms": c_full, "full_read_decode_gbs": full_b / (c_full * 1e-3) / 1e9}
+        for key in ("update_refresh", "sketch_decode", "full_read_decode"):
+            cold[key + "_frac"] = cold[key + "_gbs"] / HBM_PEAK_GBS
+        del flush, flush_sum, st_c, sk_c
+
     # ---- roofline of the dominant kernel (update + refresh) ---------------------------
     upd_avg_ms = float(np.mean(upd_ms))
     upd_bytes = bm["update"] * U
@@ -462,9 +523,19 @@ def main() -> int:
         oracle.run(cfg.rule, S0s, Bs, q, k, v, dc, be, W, threads=threads)
         cpu_s = time.perf_counter() - c0
         steps_per_s = Ts / (cpu_s * U / len(units))
+        # one thread on the first 64 sampled units: the per-core rate
+        n1 = min(64, len(units))
+        c0 = time.perf_counter()
+        oracle.run(cfg.rule, S0s[:n1], Bs[:n1], q[:, :n1], k[:, :n1], v[:, :n1], dc[:, :n1],
+                   be[:, :n1] if be is not None else None, W, threads=1)
+        one_s = time.perf_counter() - c0
         cpu = {"value": steps_per_s, "unit": "decode steps/s", "cores": threads, "kind": "oracle",
                "sample": f"{len(units)} of {U} (sequence, head) units x {Ts} steps, fp64, "
-                         f"{cpu_s:.2f} s wall on {threads} threads; rate scaled to all {U} units"}
+                         f"{cpu_s:.2f} s wall on {threads} threads; rate scaled to all {U} units",
+               "cpu_model": cpu_model(),
+               "one_thread": {"value": Ts / (one_s * U / n1), "unit": "decode steps/s",
+                              "sample": f"{n1} units x {Ts} steps on 1 thread, {one_s:.2f} s; "
+                                        f"rate scaled to all {U} units"}}
 
     value = a.steps / elapsed
     out = {
@@ -506,6 +577,7 @@ def main() -> int:
         "state_bytes_ratio": bm["state_bytes_full"] / bm["state_bytes_sketch"],
         "read_path_bytes_ratio": bm["full_step"] / bm["sketch_step"],
         "approx_error": approx,
+        "cold_cache": cold,
         "copy_probe_gbs": copy_gbs,
         "update_refresh_frac_of_copy": achieved / copy_gbs,
         "input_gen_s": gen_s,
