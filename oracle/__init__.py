@@ -10,6 +10,10 @@ control"): the full state is written once per window, a sketch B S_win is
 stored at each window start, and each decode step combines the sketch with
 query coefficients c = B q~ plus the exact within-window term. See the header
 of ``oracle.c`` for the exact definitions and the readings taken.
+
+Two parts are plain numpy here rather than C: the least-squares read
+(``ls_read``) and the offline basis fit (``fit_basis``: top eigenvectors of the
+uncentred second moment of sampled queries).
 """
 from __future__ import annotations
 
@@ -167,6 +171,38 @@ def ls_read(out: dict, window: int) -> np.ndarray:
             c = np.linalg.lstsq(Sk.T, exact, rcond=LS_RCOND)[0]
             y[t, u] = Sk.T @ c + (out["y_replay"][t, u] - exact)
     return y
+
+
+def fit_basis(samples, rank: int):
+    """The offline basis fit of the C2 workload, as a plain definition (the pages fix the
+    basis vectors offline, readsearch.ai listing of arXiv 2609.33051, Abstract; the
+    query-basis idea, agihunt.info summary, "Mechanism details"; the recipe, top-r PCA
+    directions of sampled queries made orthonormal, is read from the workload's
+    description). Per head h, with X = samples[h] ([S][d_k]):
+
+      M = X^T X / S   (the uncentred second moment of the samples),
+      rows m = 0 .. rank-1: unit eigenvectors of M for its rank largest eigenvalues,
+      in decreasing order of eigenvalue, each signed so that its entry of largest
+      magnitude (the first such entry on a tie) is positive.
+
+    Returns (basis [H][rank][d_k], eigenvalues [H][d_k] in decreasing order), fp64.
+    The rows are unique (up to the sign rule) only where the eigenvalue gaps around
+    them are non-zero; callers compare subspaces where they are not.
+    """
+    X = _f64(samples)
+    H, S, dk = X.shape
+    out = np.empty((H, rank, dk))
+    lam = np.empty((H, dk))
+    for h in range(H):
+        M = X[h].T @ X[h] / S
+        w, V = np.linalg.eigh(M)                 # ascending eigenvalues, orthonormal columns
+        order = np.argsort(-w, kind="stable")
+        lam[h] = w[order]
+        for m in range(rank):
+            v = V[:, order[m]]
+            big = int(np.argmax(np.abs(v)))
+            out[h, m] = v if v[big] > 0 else -v
+    return out, lam
 
 
 def round_bf16(x: float, _lib_override=None) -> float:

@@ -429,4 +429,98 @@ def pin_ls_zero_state(L):
         close(out["y_ls"], out["y_sketch"], 1e-12, f"{rule} zero state vs projection")
 
 
+# ----------------------------------------------------------------------------
+# the offline basis fit (oracle.fit_basis, numpy): top-r eigenvectors of the
+# uncentred second moment of sampled queries. Each pin takes the fit function so
+# that test_oracle_pins.py can run the same pins on copies with planted mistakes.
+# ----------------------------------------------------------------------------
+def _sign_rule(rows):
+    """Rows signed so that the entry of largest magnitude (first on a tie) is positive."""
+    out = np.array(rows, dtype=np.float64)
+    for m in range(out.shape[0]):
+        if out[m, int(np.argmax(np.abs(out[m])))] < 0:
+            out[m] = -out[m]
+    return out
+
+
+def pin_fit_closed_form(L, fit=oracle.fit_basis):
+    """Samples X = sqrt(S) Z diag(sig) U^T with Z^T Z = I have second moment
+    X^T X / S = U diag(sig^2) U^T: the fit must return the columns of U ordered by
+    decreasing sig (signed by the rule) and the eigenvalues sig^2."""
+    rng = np.random.default_rng(11)
+    H, S, dk, r = 2, 40, 6, 4
+    X = np.empty((H, S, dk))
+    want_rows, want_lam = [], []
+    for h in range(H):
+        Z, _ = np.linalg.qr(rng.standard_normal((S, dk)))
+        U, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+        sig = rng.permutation(np.array([3.0, 2.5, 2.0, 1.5, 1.0, 0.5]))
+        X[h] = np.sqrt(S) * Z @ np.diag(sig) @ U.T
+        order = np.argsort(-sig)
+        want_rows.append(_sign_rule(U[:, order[:r]].T))
+        want_lam.append(sig[order] ** 2)
+    rows, lam = fit(X, r)
+    close(rows, np.stack(want_rows), 1e-10, "closed-form basis rows")
+    close(lam, np.stack(want_lam), 1e-10, "closed-form eigenvalues")
+
+
+def pin_fit_brute_force_plane(L, fit=oracle.fit_basis):
+    """d_k = 2: the leading direction maximises the mean squared projection
+    (1/S) sum_s (q_s . u)^2 over unit u. Brute force over 400,001 angles."""
+    rng = np.random.default_rng(12)
+    X = rng.standard_normal((1, 9, 2)) * np.array([1.0, 0.4]) + np.array([0.3, -0.2])
+    theta = np.linspace(0.0, np.pi, 400001)
+    u = np.stack([np.cos(theta), np.sin(theta)], axis=1)            # [angles][2]
+    quot = np.mean((X[0] @ u.T) ** 2, axis=0)
+    best = u[int(np.argmax(quot))]
+    rows, lam = fit(X, 2)
+    assert abs(abs(rows[0, 0] @ best) - 1.0) < 1e-9, "leading direction off the brute-force maximum"
+    assert abs(lam[0, 0] - quot.max()) < 1e-9 * quot.max(), "largest eigenvalue is not the maximum"
+    assert abs(lam[0, 1] - quot.min()) < 1e-9 * quot.max(), "smallest eigenvalue is not the minimum"
+
+
+def pin_fit_samples_in_a_subspace(L, fit=oracle.fit_basis):
+    """Samples spanning a k-dimensional subspace: the top k rows span exactly it and
+    the remaining eigenvalues are zero."""
+    rng = np.random.default_rng(13)
+    dk, k, S = 7, 3, 20
+    P, _ = np.linalg.qr(rng.standard_normal((dk, k)))               # orthonormal columns
+    X = (rng.standard_normal((S, k)) @ P.T)[None]
+    rows, lam = fit(X, 5)
+    proj = rows[0, :k].T @ rows[0, :k]
+    close(proj, P @ P.T, 1e-10, "top-k span")
+    assert np.all(np.abs(lam[0, k:]) < 1e-12), "eigenvalues beyond the samples' rank"
+
+
+def pin_fit_invariants(L, fit=oracle.fit_basis):
+    """Orthonormal rows; M b_m = lambda_m b_m for M summed sample by sample; the
+    eigenvalues decrease and add up to the mean squared norm; the sign rule holds."""
+    rng = np.random.default_rng(14)
+    X = rng.standard_normal((3, 25, 5)) * np.array([2.0, 1.0, 0.7, 0.5, 0.2])
+    rows, lam = fit(X, 3)
+    for h in range(3):
+        M = np.zeros((5, 5))
+        for q in X[h]:
+            M += np.outer(q, q)
+        M /= X.shape[1]
+        close(rows[h] @ rows[h].T, np.eye(3), 1e-12, "orthonormal rows")
+        for m in range(3):
+            close(M @ rows[h, m], lam[h, m] * rows[h, m], 1e-10, "eigen-equation")
+            big = int(np.argmax(np.abs(rows[h, m])))
+            assert rows[h, m, big] > 0, "sign rule"
+        assert np.all(np.diff(lam[h]) <= 1e-12), "eigenvalues not decreasing"
+        close(lam[h].sum(), np.mean(np.sum(X[h] ** 2, axis=1)), 1e-12, "trace")
+
+
+def pin_fit_is_uncentred(L, fit=oracle.fit_basis):
+    """Samples around a large common offset mu: the uncentred second moment is led by
+    mu / |mu| (a centred covariance would be led by the spread instead)."""
+    rng = np.random.default_rng(15)
+    mu = np.array([3.0, -4.0, 0.0, 0.0])
+    X = (mu + rng.standard_normal((200, 4)) * np.array([0.0, 0.0, 1.0, 0.1]))[None]
+    rows, _ = fit(X, 1)
+    assert abs(abs(rows[0, 0] @ mu) / np.linalg.norm(mu) - 1.0) < 1e-3, "not led by the offset"
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]
+FIT_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_fit_")]

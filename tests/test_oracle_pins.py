@@ -97,3 +97,37 @@ def test_oracle_reproduces_c1_fixture(oracle_lib):
     np.testing.assert_allclose(out["Sk"][-1][0], fx["Sk_last_u0"], rtol=1e-12, atol=1e-15)
     fro = np.linalg.norm(out["S_win"].reshape(out["S_win"].shape[0], -1), axis=1)
     np.testing.assert_allclose(fro, fx["S_win_frobenius"], rtol=1e-12)
+
+
+# Planted mistakes in the basis fit (oracle.fit_basis, numpy): each copy of its source
+# with one change must fail at least one of the fit pins.
+FIT_MUTANTS = [
+    ("fit_centred", "M = X[h].T @ X[h] / S",
+     "M = (X[h] - X[h].mean(0)).T @ (X[h] - X[h].mean(0)) / S"),
+    ("fit_not_normalised", "M = X[h].T @ X[h] / S", "M = X[h].T @ X[h]"),
+    ("fit_ascending", 'order = np.argsort(-w, kind="stable")', 'order = np.argsort(w, kind="stable")'),
+    ("fit_rows_of_V", "v = V[:, order[m]]", "v = V[order[m], :]"),
+    ("fit_no_sign_rule", "out[h, m] = v if v[big] > 0 else -v", "out[h, m] = v"),
+    ("fit_sign_by_first_entry", "big = int(np.argmax(np.abs(v)))", "big = 0"),
+]
+
+
+def _mutated_fit(old, new):
+    import inspect
+    src = inspect.getsource(oracle.fit_basis)
+    assert src.count(old) == 1, f"pattern found {src.count(old)} times"
+    ns = dict(oracle.__dict__)
+    exec(src.replace(old, new), ns)
+    return ns["fit_basis"]
+
+
+@pytest.mark.parametrize("name,old,new", FIT_MUTANTS, ids=[m[0] for m in FIT_MUTANTS])
+def test_planted_fit_mistake_is_caught(name, old, new):
+    fit = _mutated_fit(old, new)
+    failures = []
+    for pin in oracle_pins.FIT_PINS:
+        try:
+            pin(None, fit=fit)
+        except AssertionError as e:
+            failures.append(f"{pin.__name__}: {e}")
+    assert failures, f"planted mistake {name!r} passed every fit pin"
