@@ -100,6 +100,9 @@ def main() -> int:
     ap.add_argument("--config", default="c3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compare", action="store_true", help="skip the full-read comparison pass")
+    ap.add_argument("--fit-basis", action="store_true",
+                    help="fit the basis on the device (ssm_fit_basis) from the workload's sampled "
+                         "queries instead of taking the host one; reports the fit's time")
     ap.add_argument("--no-cold", action="store_true",
                     help="skip the cold-cache (Infinity Cache flushed) kernel timings")
     ap.add_argument("--cpu-units", type=int, default=512, help="oracle sample: units")
@@ -176,6 +179,27 @@ def main() -> int:
                             max(ranks), a.sketch_dtype)
     else:
         basis = to_dev(workloads.basis(cfg))
+    basis_fit = None
+    if a.fit_basis:
+        # the basis fitted on the device from the workload's sampled queries (4096 per head)
+        # replaces the host one for every GPU leg; timed once warm, outside the timed region
+        if ranks is not None:
+            print("--fit-basis fits one uniform rank", file=sys.stderr)
+            return 2
+        d_fit = ssm.Dims.make(cfg.rule, cfg.in_dtype, cfg.batch, cfg.heads, cfg.d_k, cfg.d_v, W,
+                              cfg.rank)
+        samples = to_dev(workloads.pca_samples(cfg))
+        n_fit = samples.shape[1]
+        ssm.fit_basis(d_fit, samples, n_fit, basis)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(3):
+            ssm.fit_basis(d_fit, samples, n_fit, basis)
+        ev[1].record()
+        torch.cuda.synchronize()
+        basis_fit = {"ms": ev[0].elapsed_time(ev[1]) / 3, "samples_per_head": n_fit,
+                     "heads": cfg.heads, "rank": cfg.rank}
+        del samples
     inputs = [(to_dev(s.q), to_dev(s.k), to_dev(s.v), to_dev(s.decay), to_dev(s.beta))
               for s in steps_host]
     gen_s = time.time() - t0
@@ -555,7 +579,8 @@ def main() -> int:
                    "heads": cfg.heads, "d_k": cfg.d_k, "d_v": cfg.d_v, "window": W,
                    "rank": cfg.rank if ranks is None else f"per head {sorted(set(ranks))}, mean "
                    f"{sum(ranks) / len(ranks):g}", "inputs": cfg.in_dtype, "state": "f32",
-                   "sketch": a.sketch_dtype, "coefficients": a.coefficients},
+                   "sketch": a.sketch_dtype, "coefficients": a.coefficients,
+                   "basis": "device fit" if a.fit_basis else "host"},
         "roofline": {"bound": "hbm", "kernel": "update_refresh_kernel", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                      "traffic": traffic, "bytes_per_launch": upd_bytes,
@@ -578,6 +603,7 @@ def main() -> int:
         "read_path_bytes_ratio": bm["full_step"] / bm["sketch_step"],
         "approx_error": approx,
         "cold_cache": cold,
+        "basis_fit": basis_fit,
         "copy_probe_gbs": copy_gbs,
         "update_refresh_frac_of_copy": achieved / copy_gbs,
         "input_gen_s": gen_s,

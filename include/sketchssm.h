@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 2
+#define SSM_ABI_VERSION 3
 
 typedef enum { SSM_MAMBA2 = 0, SSM_GDN = 1, SSM_KDA = 2 } ssm_rule;
 typedef enum { SSM_IN_BF16 = 0, SSM_IN_F32 = 1 } ssm_in_dtype;
@@ -287,6 +287,28 @@ ssm_status ssm_recurrent_decode_step(const ssm_dims* d,
                                      const void* k_t, const void* v_t,
                                      const float* decay_t, const float* beta_t,
                                      float* y, void* stream);
+
+/*
+ * Offline basis fit on the device. The pages fix the query basis offline
+ * (readsearch.ai listing, Abstract; agihunt.info "Confirmed", mechanism bullet:
+ * queries are compressed onto a small low-rank basis); the Mamba-2 workload's
+ * recipe takes the top PCA directions of sampled queries and makes them
+ * orthonormal. For every head h, with X_h = samples[h] (n_samples queries of
+ * d_k entries), basis[h] receives the d->rank unit eigenvectors of the
+ * uncentred second moment X_h^T X_h / n_samples with the largest eigenvalues,
+ * one per row, in decreasing order of eigenvalue, orthonormal in fp32, each
+ * signed so that its entry of largest magnitude (the first on a tie) is
+ * positive. Rows for equal eigenvalues are some orthonormal basis of their
+ * eigenspace.
+ *   samples: [H][n_samples][d_k], d->in_dtype, device, read only;
+ *   basis:   [H][rank][d_k] fp32, device, out: the layout the window and
+ *            sketch calls read.
+ * Uses heads, d_k, rank and in_dtype of d; the other fields are checked but
+ * not used. 1 <= n_samples <= 2^24. The basis must not overlap the samples.
+ * Setup-time work: one workgroup per head, nothing allocated.
+ */
+ssm_status ssm_fit_basis(const ssm_dims* d, const void* samples, int32_t n_samples,
+                         float* basis, void* stream);
 
 #ifdef __cplusplus
 }

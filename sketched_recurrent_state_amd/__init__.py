@@ -106,6 +106,8 @@ def _load():
     lib.ssm_window_update_refresh_ls.argtypes = [dp] + [vp] * 8 + [i32, vp]
     lib.ssm_sketch_decode_step_ls.restype = i32
     lib.ssm_sketch_decode_step_ls.argtypes = [dp] + [vp] * 11 + [i32, vp, vp]
+    lib.ssm_fit_basis.restype = i32
+    lib.ssm_fit_basis.argtypes = [dp, vp, i32, vp, vp]
     return lib
 
 
@@ -291,6 +293,18 @@ def recurrent_decode_step(d: Dims, state, q, k_t, v_t, decay_t, beta_t, y, strea
         _addr(k_t, "k_t", tin, n["k_t"]), _addr(v_t, "v_t", tin, n["v_t"]),
         _addr(decay_t, "decay_t", f32, n["decay_t"]), _addr(beta_t, "beta_t", f32, n["beta_t"]),
         _addr(y, "y", f32, n["y"]), _stream(stream)))
+
+
+def fit_basis(d: Dims, samples, n_samples: int, basis, stream=None) -> None:
+    """ssm_fit_basis: per head, the d.rank leading eigenvectors of the samples' uncentred
+    second moment as orthonormal rows of basis. samples [H][n_samples][d_k] (d.in_dtype),
+    basis [H][rank][d_k] fp32."""
+    if isinstance(stream, int) and _all_raw((samples, basis)):
+        return _check(_lib.ssm_fit_basis(ctypes.byref(d), samples, int(n_samples), basis, stream))
+    tin, f32 = _types(d, (samples, basis))
+    _check(_lib.ssm_fit_basis(
+        ctypes.byref(d), _addr(samples, "samples", tin, d.heads * int(n_samples) * d.d_k),
+        int(n_samples), _addr(basis, "basis", f32, d.heads * d.rank * d.d_k), _stream(stream)))
 
 
 # ----------------------------------------------------------------------------

@@ -388,6 +388,25 @@ ssm_status ssm_recurrent_decode_step(const ssm_dims* d, float* state, const void
                   fn);
 }
 
+ssm_status ssm_fit_basis(const ssm_dims* d, const void* samples, int32_t n_samples,
+                         float* basis, void* stream) {
+  static const char* fn = "ssm_fit_basis";
+  ssm_status st = check_dims(d, fn);
+  if (st != SSM_OK) return st;
+  if (samples == nullptr) return fail(SSM_E_NULL, "%s: samples is NULL", fn);
+  if (basis == nullptr) return fail(SSM_E_NULL, "%s: basis is NULL", fn);
+  if (n_samples < 1 || n_samples > (1 << 24))
+    return fail(SSM_E_SHAPE, "%s: n_samples %d not in [1, 2^24]", fn, n_samples);
+  const Sizes z = sizes_of(*d);
+  const size_t sample_bytes = (size_t)d->heads * (size_t)n_samples * d->d_k * z.elem;
+  st = check_arrays(fn, {{samples, sample_bytes, false, "samples"}, {basis, z.basis, true, "basis"}});
+  if (st != SSM_OK) return st;
+  (void)hipGetLastError();
+  return launched(ssm::launch_fit_basis(*d, samples, n_samples, basis,
+                                        reinterpret_cast<hipStream_t>(stream)),
+                  fn);
+}
+
 ssm_status ssm_window_update_refresh(const ssm_dims* d, float* state, void* sketch,
                                      const float* basis, const void* k_buf, const void* v_buf,
                                      const float* decay_buf, const float* beta_buf,

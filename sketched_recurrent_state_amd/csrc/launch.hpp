@@ -139,4 +139,7 @@ hipError_t launch_recurrent_step(const ssm_dims& d, float* state, const void* q,
                                  const void* v_t, const float* decay_t, const float* beta_t,
                                  float* y, hipStream_t stream);
 
+hipError_t launch_fit_basis(const ssm_dims& d, const void* samples, int n_samples, float* basis,
+                            hipStream_t stream);
+
 }  // namespace ssm

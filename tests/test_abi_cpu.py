@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert ssm.abi_version() == 2
+    assert ssm.abi_version() == 3
     lib = ssm.library()
     for code in range(7):
         assert lib.ssm_status_string(code).decode()
@@ -302,3 +302,22 @@ def test_varlen_validation():
     st, msg = status_of(ssm.sketch_decode_step_varlen, d, 8, p[9], p[10], p[1], p[2], p[3],
                         p[4], p[5], p[6], p[7], p[10])
     assert st == 5
+
+
+def test_fit_basis_validation():
+    p = addrs(4)
+    d = dims()
+    st, msg = status_of(ssm.fit_basis, d, None, 64, p[1])
+    assert st == 1 and "samples" in msg
+    st, msg = status_of(ssm.fit_basis, d, p[0], 64, None)
+    assert st == 1 and "basis" in msg
+    for n in (0, -3, (1 << 24) + 1):
+        st, msg = status_of(ssm.fit_basis, d, p[0], n, p[1])
+        assert st == 2 and "n_samples" in msg
+    st, msg = status_of(ssm.fit_basis, d, p[0] + 8, 64, p[1])
+    assert st == 3 and "samples" in msg
+    # basis written inside the samples
+    st, msg = status_of(ssm.fit_basis, d, p[0], 64, p[0] + 1024)
+    assert st == 5 and "overlaps" in msg
+    st, msg = status_of(ssm.fit_basis, dims(d_k=16, rank=17), p[0], 64, p[1])
+    assert st == 2 and "rank" in msg

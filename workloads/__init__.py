@@ -262,6 +262,14 @@ def basis(cfg: Config) -> np.ndarray:
     return out.astype(np.float32)
 
 
+def pca_samples(cfg: Config, n: int = 4096) -> np.ndarray:
+    """The sampled queries of the ``pca`` basis recipe: per head, n queries drawn like
+    the decode queries on the PCA stream, ``[H][n][d_k]`` in the config's input type
+    (bf16 bits or fp32). :func:`basis` draws the same numbers before the bf16 rounding."""
+    rng = _rng(cfg, STREAM_PCA)
+    return np.stack([_pack(cfg, _queries(cfg, rng, (n, cfg.d_k))) for _ in range(cfg.heads)])
+
+
 def basis_ranked(cfg: Config, ranks) -> np.ndarray:
     """Per-head ranks: head h keeps the first ranks[h] rows of its d_k-row basis
     (the same draws as basis() with r = d_k). fp32 [sum(ranks)][d_k]."""
