@@ -190,6 +190,7 @@ constexpr int DPP_QUAD_1032 = 0xB1;  // quad_perm:[1,0,3,2]
 constexpr int DPP_QUAD_2301 = 0x4E;  // quad_perm:[2,3,0,1]
 constexpr int DPP_ROR4 = 0x124;      // row_ror:4
 constexpr int DPP_ROR8 = 0x128;      // row_ror:8
+constexpr int DPP_HALF_MIRROR = 0x141;  // row_half_mirror: lane p <-> 7 - p in each 8 lanes
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {

@@ -34,7 +34,7 @@ constexpr float kLsRelTol = 1e-5f;
 // `sketch`, and the read map Y = Q S^T [r][d_k] in `rmap`; a read then gives
 // Q^T (Y q~), the projection of S^T q~ on the span of the sketch rows.
 template <int RULE, int DK, int DV, typename TIN, typename TSK, bool LS, typename RT, typename RM>
-__global__ void __launch_bounds__(2 * DV)
+__global__ void __launch_bounds__(2 * DV, 4)
 update_refresh_kernel(float* __restrict__ state, TSK* __restrict__ sketch,
                       float* __restrict__ rmap,
                       const float* __restrict__ basis, const TIN* __restrict__ kbuf,
@@ -118,53 +118,63 @@ update_refresh_kernel(float* __restrict__ state, TSK* __restrict__ sketch,
   // 6. refresh the sketch from the register-resident state: Sk[m] = S^T b_m.
   //    Eight basis rows at a time; the d_k reduction is a reduce-scatter over
   //    the 8 row groups, after which lane group rg holds basis row m0 + rg.
-  // Least-squares refresh, after the rows of Sk are in LDS (lQ):
-  //   a. wave 0 makes them orthonormal: classical Gram-Schmidt, two passes per row
-  //      (the second removes what rounding left of the first); a row whose residual
-  //      is below kLsRelTol of the largest row norm is set to zero;
-  //   b. every wave forms Y = Q S^T over its 32 columns: per row of S a dot product
+  // Least-squares refresh, after the rows of Sk are in LDS (lQ). The rows are made
+  // orthonormal as Gram-Schmidt would, through the Cholesky factor of their Gram
+  // matrix (Sk = L Q with Q orthonormal rows, L lower triangular, G = Sk Sk^T = L L^T):
+  //   a. G in fp64 (products of fp32 values are exact there), four lanes per entry;
+  //   b. wave 0 factors G = L L^T column by column, lane i owning row i; a row whose
+  //      pivot, its squared residual against the rows before it, is below
+  //      kLsRelTol^2 of the largest squared row norm is dropped (zero column of L);
+  //   c. Q = L^-1 Sk in place, one column of the sketch per thread (forward
+  //      substitution in fp64 with the inverse pivots that step b leaves on the
+  //      diagonal; dropped rows are zero);
+  //   d. every wave forms Y = Q S^T over its 32 columns: per row of S a dot product
   //      of 4 columns, summed over the 8 lanes of the row group (lane bits 0..2);
-  //   c. the waves' partial Y are added in a fixed order and stored with Q.
+  //   e. the waves' partial Y are added in a fixed order and stored with Q.
   float* lQ = lB + rank * DK;  // [rank][DV] (LS only)
   float* lP = lQ + rank * DV;  // [DV / 32][rank][DK] per-wave partial Y (LS only)
+  double* lG = reinterpret_cast<double*>(lP + (DV / 32) * rank * DK);  // [rank][rank] (LS only)
   auto ls_epilogue = [&](float* Qu) {
     __syncthreads();
-    if (wave == 0) {
-      constexpr int EPL = (DV + 63) / 64;  // row elements per lane
-      auto wsum = [](float x) { return group_allreduce<64>(x); };
-      float maxn2 = 0.f;
-      for (int m = 0; m < rank; ++m) {
-        float a = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e)
-          if (lane + 64 * e < DV) a = fmaf(lQ[m * DV + lane + 64 * e], lQ[m * DV + lane + 64 * e], a);
-        maxn2 = fmaxf(maxn2, wsum(a));
+    for (int e0 = 0; e0 < rank * rank; e0 += NT / 4) {  // a. Gram matrix, lower triangle
+      const int e = e0 + tid / 4, part = tid & 3;
+      double g = 0.0;
+      if (e < rank * rank) {
+        const float* ri = lQ + (e / rank) * DV;
+        const float* rj = lQ + (e % rank) * DV;
+        for (int c = part; c < DV; c += 4) g = fma((double)ri[c], (double)rj[c], g);
       }
-      const float thr2 = kLsRelTol * kLsRelTol * maxn2;
-      for (int m = 0; m < rank; ++m) {
-        float x[EPL];
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) x[e] = lane + 64 * e < DV ? lQ[m * DV + lane + 64 * e] : 0.f;
-        for (int pass = 0; pass < 2; ++pass) {
-          for (int p = 0; p < m; ++p) {  // rows p < m are final: subtract x's part along each
-            float a = 0.f;
-#pragma unroll
-            for (int e = 0; e < EPL; ++e)
-              if (lane + 64 * e < DV) a = fmaf(x[e], lQ[p * DV + lane + 64 * e], a);
-            const float dp = wsum(a);
-#pragma unroll
-            for (int e = 0; e < EPL; ++e)
-              if (lane + 64 * e < DV) x[e] = fmaf(-dp, lQ[p * DV + lane + 64 * e], x[e]);
-          }
+      g += __shfl_xor(g, 1);
+      g += __shfl_xor(g, 2);
+      if (e < rank * rank && part == 0 && e % rank <= e / rank) lG[e] = g;
+    }
+    __syncthreads();
+    if (wave == 0) {  // b. Cholesky, left-looking
+      double maxd = 0.0;
+      for (int i = 0; i < rank; ++i) maxd = fmax(maxd, lG[i * rank + i]);
+      const double thr = (double)kLsRelTol * (double)kLsRelTol * maxd;
+      const int i = lane;
+      for (int k = 0; k < rank; ++k) {
+        // every lane reads row k (and its own row) before lanes i >= k write column k
+        double dk = lG[k * rank + k];
+        for (int p = 0; p < k; ++p) dk = fma(-lG[k * rank + p], lG[k * rank + p], dk);
+        const double lkk = dk > thr ? sqrt(dk) : 0.0;
+        double x = 0.0;
+        if (i > k && i < rank && lkk > 0.0) {
+          x = lG[i * rank + k];
+          for (int p = 0; p < k; ++p) x = fma(-lG[i * rank + p], lG[k * rank + p], x);
+          x /= lkk;
         }
-        float a = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) a = fmaf(x[e], x[e], a);
-        const float n2 = wsum(a);
-        const float scale = n2 > thr2 ? 1.f / sqrtf(n2) : 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e)
-          if (lane + 64 * e < DV) lQ[m * DV + lane + 64 * e] = x[e] * scale;
+        if (i > k && i < rank) lG[i * rank + k] = x;
+        if (i == k) lG[k * rank + k] = lkk > 0.0 ? 1.0 / lkk : 0.0;  // kept: the inverse pivot
+      }
+    }
+    __syncthreads();
+    for (int c = tid; c < DV; c += NT) {  // c. Q = L^-1 Sk, column c
+      for (int m = 0; m < rank; ++m) {
+        double x = lQ[m * DV + c];
+        for (int p = 0; p < m; ++p) x = fma(-lG[m * rank + p], (double)lQ[p * DV + c], x);
+        lQ[m * DV + c] = (float)(x * lG[m * rank + m]);  // zero for a dropped row
       }
     }
     __syncthreads();
@@ -176,9 +186,9 @@ update_refresh_kernel(float* __restrict__ state, TSK* __restrict__ sketch,
         a = fmaf(qm.y, s[mm].y, a);
         a = fmaf(qm.z, s[mm].z, a);
         a = fmaf(qm.w, s[mm].w, a);
-        a += dpp<DPP_QUAD_1032>(a);  // lane bit 0
-        a += dpp<DPP_QUAD_2301>(a);  // lane bit 1
-        a += __shfl_xor(a, 4);       // lane bit 2
+        a += dpp<DPP_QUAD_1032>(a);    // lane bit 0
+        a += dpp<DPP_QUAD_2301>(a);    // lane bit 1
+        a += dpp<DPP_HALF_MIRROR>(a);  // the other quad of the 8 lanes (lane bit 2)
         // every lane of the row group now holds the 32-column sum for row mm * 8 + rg;
         // lane cg stores the rows with mm % 8 == cg
         if ((mm & 7) == cg) lP[(wave * rank + m) * DK + mm * 8 + rg] = a;
@@ -311,8 +321,11 @@ size_t update_refresh_lds_bytes(const ssm_dims& d, int n, int max_rank, bool ls)
                                        decltype(DV)::value>(n);
     return hipSuccess;
   });
-  // least squares: the sketch rows [r][d_v] and the waves' partial read maps [d_v/32][r][d_k]
-  const size_t ls_floats = ls ? (size_t)max_rank * d.d_v + (size_t)(d.d_v / 32) * max_rank * d.d_k : 0;
+  // least squares: the sketch rows [r][d_v], the waves' partial read maps [d_v/32][r][d_k]
+  // and the Gram matrix / Cholesky factor [r][r] in fp64
+  const size_t ls_floats = ls ? (size_t)max_rank * d.d_v + (size_t)(d.d_v / 32) * max_rank * d.d_k +
+                                    2 * (size_t)max_rank * max_rank
+                              : 0;
   return (floats + (size_t)max_rank * d.d_k + ls_floats) * sizeof(float);
 }
 
