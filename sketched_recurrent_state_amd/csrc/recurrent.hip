@@ -5,9 +5,12 @@
 // step reads the full recurrent state). Each step applies the current token to
 // the full state, writes the state back and reads y = S^T q.
 //
-// Same state-tile layout as the windowed update: one workgroup per unit,
-// d_v/32 waves, 4 columns x d_k/8 rows per lane, d_k reductions over lane bits
-// 3..5 (DPP row_ror:8 and the gfx950 permlane swaps).
+// Same state-tile layout and memory order as the windowed update: one
+// workgroup per unit, d_v/32 waves, 4 columns x d_k/8 rows per lane with lane
+// group rg owning the interleaved rows rg, rg + 8, ... (each load instruction
+// of the workgroup covers 8 whole rows of S), and the block index remapped so
+// each XCD streams one contiguous run of units. The d_k reductions run over
+// lane bits 3..5 (DPP row_ror:8 and the gfx950 permlane swaps).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -22,25 +25,60 @@ recurrent_step_kernel(float* __restrict__ state, const TIN* __restrict__ q,
                       const float* __restrict__ d_t, const float* __restrict__ b_t,
                       float* __restrict__ y) {
   constexpr int RPL = DK / 8;
-  const int unit = blockIdx.x;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int NT = 2 * DV;
+  constexpr int J = (DK + NT - 1) / NT;  // d_k elements staged per thread
+  constexpr int NA = (RULE == KDA) ? DK : 1;
+  // one pad slot past d_k takes the clamped lanes' stores
+  __shared__ __align__(16) float lk[DK + 4];
+  __shared__ __align__(16) float lq[DK + 4];
+  __shared__ __align__(16) float la[NA + 4];
+
+  // XCD x = blockIdx.x % 8 receives blocks x, x + 8, ...: give it the contiguous
+  // run of units [x * q8 + min(x, rem), ...) instead (a bijection on the grid).
+  const int G = gridDim.x, xcd = blockIdx.x & 7, q8 = G >> 3, rem = G & 7;
+  const int unit = xcd * q8 + min(xcd, rem) + (blockIdx.x >> 3);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const int cg = lane & 7, rg = lane >> 3;
   const int col = wave * 32 + cg * 4;
-  const int row0 = rg * RPL;
+  const int row0 = rg * RPL;  // this lane's d_k / 8 values in lk, lq, la (interleaved_pos)
 
   // the token's small inputs first: issued behind the 64 KB state stream they
-  // would wait for all of it
-  float kr[RPL], qr[RPL], vv[4];
-  Vec<TIN, RPL>::load(k_t + (size_t)unit * DK + row0, kr);
-  Vec<TIN, RPL>::load(q + (size_t)unit * DK + row0, qr);
+  // would wait for all of it. Indices are clamped so every lane issues the same
+  // loads (the wait for them before the LDS writes stays exact).
+  float kx[J], qx[J], ax[J];
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int i = min(tid + j * NT, DK - 1);
+    Vec<TIN, 1>::load(k_t + (size_t)unit * DK + i, &kx[j]);
+    Vec<TIN, 1>::load(q + (size_t)unit * DK + i, &qx[j]);
+    if constexpr (RULE == KDA) ax[j] = d_t[(size_t)unit * DK + i];
+  }
+  float vv[4];
   Vec<TIN, 4>::load(v_t + (size_t)unit * DV + col, vv);
   const float4 v4 = make_float4(vv[0], vv[1], vv[2], vv[3]);
-  float ar[(RULE == KDA) ? RPL : 1];  // KDA's per-row gates
-  if constexpr (RULE == KDA) Vec<float, RPL>::load(d_t + (size_t)unit * DK + row0, ar);
   float* Su = state + (size_t)unit * (DK * DV);
   float4 s[RPL];
 #pragma unroll
-  for (int m = 0; m < RPL; ++m) s[m] = load_stream(Su + (size_t)(row0 + m) * DV + col);
+  for (int m = 0; m < RPL; ++m) s[m] = load_stream(Su + (size_t)(m * 8 + rg) * DV + col);
+
+  // k, q (and KDA's per-row gates) to LDS in the interleaved order while the
+  // state is in flight; s[m] holds row m * 8 + rg. The stores are unconditional
+  // (clamped lanes write the pad slot) so the loads above stay where they are.
+#pragma unroll
+  for (int j = 0; j < J; ++j) {
+    const int i = tid + j * NT;
+    const int pos = (i < DK) ? interleaved_pos<DK>(i) : DK;
+    lk[pos] = kx[j];
+    lq[pos] = qx[j];
+    if constexpr (RULE == KDA) la[pos] = ax[j];
+  }
+  __syncthreads();
+  float kr[RPL], qr[RPL];
+  Vec<float, RPL>::load(lk + row0, kr);
+  Vec<float, RPL>::load(lq + row0, qr);
+  float ar[(RULE == KDA) ? RPL : 1];
+  if constexpr (RULE == KDA) Vec<float, RPL>::load(la + row0, ar);
 
   // S <- M S + b k v^T
   if constexpr (RULE == MAMBA2) {
@@ -70,7 +108,7 @@ recurrent_step_kernel(float* __restrict__ state, const TIN* __restrict__ q,
     for (int m = 0; m < RPL; ++m) s[m] = fma4(kr[m], w, s[m]);
   }
 #pragma unroll
-  for (int m = 0; m < RPL; ++m) store_stream(Su + (size_t)(row0 + m) * DV + col, s[m]);
+  for (int m = 0; m < RPL; ++m) store_stream(Su + (size_t)(m * 8 + rg) * DV + col, s[m]);
 
   // y = S^T q on the updated state
   float4 out = f4(0.f);

@@ -212,7 +212,8 @@ def test_empty_batch_on_device():
 
 
 RECURRENT = [small("mamba2"), small("gdn"), small("kda"), small("gdn", "f32", d_k=64, d_v=32),
-             small("kda", d_k=16, d_v=128), small("mamba2", "f32", d_k=32, d_v=64)]
+             small("kda", d_k=16, d_v=128), small("mamba2", "f32", d_k=32, d_v=64),
+             small("kda", "f32", d_k=128, d_v=32)]  # d_k staged in two passes of 64 threads
 
 
 @pytest.mark.parametrize("cfg", RECURRENT, ids=lambda c: c.name)
