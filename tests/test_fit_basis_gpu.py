@@ -188,3 +188,41 @@ def test_fit_feeds_the_decode():
     got = H.run_gpu(cfg, inp)
     ref = H.run_oracle(cfg, inp)
     H.compare(cfg, got, ref)
+
+
+def test_fitted_basis_makes_low_rank_queries_exact():
+    """The method's premise end to end: when the queries lie in an r-dimensional subspace per
+    head, a basis fitted on the device from sampled queries spans it, and for Mamba-2 (whose
+    transposed transitions only scale q, so q~ stays in that subspace) the sketch read equals
+    the exact read. fp32 inputs keep the queries in the subspace up to fp32 rounding (~6e-8
+    relative); the fitted span is off by ~E / gap with E ~ (S + 8 d_k) 2^-24, so the sketch
+    read must agree with the exact read to ~1e-5. The oracle decodes with its own fp64 fit of
+    the same samples."""
+    cfg = workloads.C2.with_(batch=4, heads=4, steps=16, in_dtype="f32")
+    H_, dk, r = cfg.heads, cfg.d_k, cfg.rank
+    rng = np.random.default_rng([0x10F1, dk, r])
+    U = np.stack([np.linalg.qr(rng.standard_normal((dk, r)))[0] for _ in range(H_)])  # [H][dk][r]
+    draw = lambda lead: (np.einsum("hkr,...hr->...hk", U, rng.standard_normal(lead + (H_, r)))
+                         / np.sqrt(r)).astype(np.float32)
+    samples = np.ascontiguousarray(np.moveaxis(draw((512,)), 0, 1))  # [H][S][dk]
+    basis_gpu = fit_gpu(samples, r, "f32")
+    basis_oracle, lam = oracle.fit_basis(workloads.widen(samples), r)
+    assert np.all(lam[:, r - 1] > 1e3 * np.abs(lam[:, r:]).max(initial=0.0) + 1e-3), \
+        "the samples do not span r directions"
+    inp = H.Inputs(cfg, np.arange(cfg.units), cfg.steps)
+    hq = []
+    for t in range(cfg.steps):
+        q = draw((cfg.batch,))                                      # [N][H][dk]
+        inp.q[t] = torch.from_numpy(q).cuda()
+        hq.append(q.reshape(cfg.units, dk)[inp.units].astype(np.float64))
+    inp.host["q"] = np.stack(hq)
+    inp.basis = torch.from_numpy(np.ascontiguousarray(basis_gpu)).cuda()
+    inp.host_basis = basis_oracle[inp.units % H_]
+    got = H.run_gpu(cfg, inp)
+    ref = H.run_oracle(cfg, inp)
+    H.compare(cfg, got, ref)
+    e_oracle = H.rel_rows(ref["y_sketch"], ref["y_exact"]).max()
+    e_gpu = H.rel_rows(got["y_sketch"], got["y_full"]).max()
+    H.note(f"sketch vs exact read, low-rank queries: oracle {e_oracle:.2e}, GPU {e_gpu:.2e}")
+    assert e_oracle <= 1e-5, f"oracle: sketch read off the exact read by {e_oracle:.2e}"
+    assert e_gpu <= 1e-4, f"GPU: sketch read off the exact read by {e_gpu:.2e}"
