@@ -460,6 +460,19 @@ def main() -> int:
     copy_gbs = 2 * n_copy * 4 / (copy_ms * 1e-3) / 1e9
     del src, dst
 
+    # ---- attainable HBM rate for the state's read + write: the library's in-place stream
+    # probe over a buffer of the state's size, in the update's access order (shape 0) and in
+    # flat 128 KB runs per workgroup (shape 1, the fastest plain shape measured) -----------
+    n_tiles = (S0_dev.numel() * 4 // 65536) & ~1
+    probe = torch.ones(n_tiles * 16384, device=dev)
+    probe_gbs = []
+    for shape in (0, 1):
+        ms = kernel_time(lambda i: ssm.stream_probe(probe, n_tiles, shape, stream=sp), 10)
+        probe_gbs.append(2 * n_tiles * 65536 / (ms * 1e-3) / 1e9)
+    del probe
+    stream_probe = {"bytes_each_way": n_tiles * 65536, "launches": 10,
+                    "update_order_gbs": probe_gbs[0], "flat_runs_gbs": probe_gbs[1]}
+
     # ---- cold-cache kernel times: the 256 MB Infinity Cache flushed before each launch ----
     # A 512 MiB read between launches, outside the events, replaces the cached lines with
     # clean ones. (A write would leave them dirty, and the timed kernel would pay for their
@@ -606,6 +619,8 @@ def main() -> int:
         "basis_fit": basis_fit,
         "copy_probe_gbs": copy_gbs,
         "update_refresh_frac_of_copy": achieved / copy_gbs,
+        "stream_probe": stream_probe,
+        "update_refresh_frac_of_stream": achieved / max(probe_gbs),
         "input_gen_s": gen_s,
         "device": torch.cuda.get_device_name(0),
     }

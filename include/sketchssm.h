@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 3
+#define SSM_ABI_VERSION 4
 
 typedef enum { SSM_MAMBA2 = 0, SSM_GDN = 1, SSM_KDA = 2 } ssm_rule;
 typedef enum { SSM_IN_BF16 = 0, SSM_IN_F32 = 1 } ssm_in_dtype;
@@ -309,6 +309,23 @@ ssm_status ssm_recurrent_decode_step(const ssm_dims* d,
  */
 ssm_status ssm_fit_basis(const ssm_dims* d, const void* samples, int32_t n_samples,
                          float* basis, void* stream);
+
+/*
+ * Measurement aid, not a step of the method: the HBM rate that a state-sized
+ * read + write reaches on this device, to set the window update's bandwidth
+ * against. Streams buf in place: every value is read, multiplied by 1.0f and
+ * written back, all of a thread's loads before its stores, non-temporal.
+ *   buf:     fp32, device, n_tiles * 16384 floats (64 KB tiles), in/out;
+ *   shape 0: the window update's access order: one 256-thread workgroup per
+ *            tile seen as a 128 x 128 state; each wave holds 32 columns, lane
+ *            group g of a wave the rows g, g + 8, ...; consecutive tiles go to
+ *            one XCD;
+ *   shape 1: two tiles per 512-thread workgroup, read as one flat run; each
+ *            load instruction of the workgroup covers 8 KB contiguous.
+ * 1 <= n_tiles < 2^24; shape 1 needs an even n_tiles (else SSM_E_SHAPE);
+ * shape outside {0, 1} gives SSM_E_RANGE. One launch per call.
+ */
+ssm_status ssm_stream_probe(float* buf, int64_t n_tiles, int32_t shape, void* stream);
 
 #ifdef __cplusplus
 }

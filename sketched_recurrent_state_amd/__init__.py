@@ -22,7 +22,9 @@ __all__ = [
     "abi_version", "buffer_append", "window_update_refresh", "sketch_decode_step",
     "full_read_decode_step", "recurrent_decode_step", "window_update_refresh_ranked",
     "sketch_decode_step_ranked", "rank_offsets", "window_update_refresh_varlen",
-    "sketch_decode_step_varlen", "LIB_PATH", "HEADER", "declared_symbols",
+    "sketch_decode_step_varlen", "window_update_refresh_ls", "sketch_decode_step_ls",
+    "fit_basis", "stream_probe", "SKETCH_F32", "SKETCH_BF16", "LIB_PATH", "HEADER",
+    "declared_symbols", "numel", "library",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -108,6 +110,8 @@ def _load():
     lib.ssm_sketch_decode_step_ls.argtypes = [dp] + [vp] * 11 + [i32, vp, vp]
     lib.ssm_fit_basis.restype = i32
     lib.ssm_fit_basis.argtypes = [dp, vp, i32, vp, vp]
+    lib.ssm_stream_probe.restype = i32
+    lib.ssm_stream_probe.argtypes = [vp, ctypes.c_int64, i32, vp]
     return lib
 
 
@@ -305,6 +309,13 @@ def fit_basis(d: Dims, samples, n_samples: int, basis, stream=None) -> None:
     _check(_lib.ssm_fit_basis(
         ctypes.byref(d), _addr(samples, "samples", tin, d.heads * int(n_samples) * d.d_k),
         int(n_samples), _addr(basis, "basis", f32, d.heads * d.rank * d.d_k), _stream(stream)))
+
+
+def stream_probe(buf, n_tiles: int, shape: int, stream=None) -> None:
+    """ssm_stream_probe (a measurement aid): stream buf, n_tiles 64 KB fp32 tiles, in place
+    in access shape 0 (the window update's order) or 1 (flat runs of two tiles)."""
+    ptr = buf if isinstance(buf, int) else _addr(buf, "buf", _f32(), int(n_tiles) * 16384)
+    _check(_lib.ssm_stream_probe(ptr, int(n_tiles), int(shape), _stream(stream)))
 
 
 # ----------------------------------------------------------------------------

@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsketchssm.so")
 SOURCES = ["abi.hip", "update_refresh.hip", "decode.hip", "sketch_decode_mamba2.hip",
            "sketch_decode_gdn.hip", "sketch_decode_kda.hip", "append.hip", "recurrent.hip",
-           "fit_basis.hip"]
+           "fit_basis.hip", "stream_probe.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

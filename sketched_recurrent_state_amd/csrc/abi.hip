@@ -407,6 +407,22 @@ ssm_status ssm_fit_basis(const ssm_dims* d, const void* samples, int32_t n_sampl
                   fn);
 }
 
+ssm_status ssm_stream_probe(float* buf, int64_t n_tiles, int32_t shape, void* stream) {
+  static const char* fn = "ssm_stream_probe";
+  if (buf == nullptr) return fail(SSM_E_NULL, "%s: buf is NULL", fn);
+  if (shape != 0 && shape != 1) return fail(SSM_E_RANGE, "%s: shape %d is not 0 or 1", fn, shape);
+  if (n_tiles < 1 || n_tiles >= kMaxUnits)
+    return fail(SSM_E_SHAPE, "%s: n_tiles %lld not in [1, 2^24)", fn, (long long)n_tiles);
+  if (shape == 1 && (n_tiles & 1))
+    return fail(SSM_E_SHAPE, "%s: shape 1 needs an even n_tiles (got %lld)", fn, (long long)n_tiles);
+  ssm_status st = check_arrays(fn, {{buf, (size_t)n_tiles * 65536, true, "buf"}});
+  if (st != SSM_OK) return st;
+  (void)hipGetLastError();
+  return launched(ssm::launch_stream_probe(buf, (long long)n_tiles, shape,
+                                           reinterpret_cast<hipStream_t>(stream)),
+                  fn);
+}
+
 ssm_status ssm_window_update_refresh(const ssm_dims* d, float* state, void* sketch,
                                      const float* basis, const void* k_buf, const void* v_buf,
                                      const float* decay_buf, const float* beta_buf,

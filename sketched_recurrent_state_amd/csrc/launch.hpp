@@ -142,4 +142,6 @@ hipError_t launch_recurrent_step(const ssm_dims& d, float* state, const void* q,
 hipError_t launch_fit_basis(const ssm_dims& d, const void* samples, int n_samples, float* basis,
                             hipStream_t stream);
 
+hipError_t launch_stream_probe(float* buf, long long n_tiles, int shape, hipStream_t stream);
+
 }  // namespace ssm

@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert ssm.abi_version() == 3
+    assert ssm.abi_version() == 4
     lib = ssm.library()
     for code in range(7):
         assert lib.ssm_status_string(code).decode()
@@ -321,3 +321,19 @@ def test_fit_basis_validation():
     assert st == 5 and "overlaps" in msg
     st, msg = status_of(ssm.fit_basis, dims(d_k=16, rank=17), p[0], 64, p[1])
     assert st == 2 and "rank" in msg
+
+
+def test_stream_probe_validation():
+    p = addrs(1)
+    st, msg = status_of(ssm.stream_probe, None, 8, 0)
+    assert st == 1 and "buf" in msg
+    for shape in (-1, 2):
+        st, msg = status_of(ssm.stream_probe, p[0], 8, shape)
+        assert st == 4 and "shape" in msg
+    for n in (0, -1, 1 << 24):
+        st, msg = status_of(ssm.stream_probe, p[0], n, 0)
+        assert st == 2 and "n_tiles" in msg
+    st, msg = status_of(ssm.stream_probe, p[0], 7, 1)
+    assert st == 2 and "even" in msg
+    st, msg = status_of(ssm.stream_probe, p[0] + 4, 8, 0)
+    assert st == 3 and "buf" in msg

@@ -561,3 +561,17 @@ def test_graph_replay_matches_eager(rule):
             assert torch.equal(gy[t], want_y[t]), f"replay {rep}: step {t} output differs"
         assert torch.equal(state_g, want_S), f"replay {rep}: state differs"
         assert torch.equal(dec_g.sketch, want_Sk), f"replay {rep}: sketch differs"
+
+
+@pytest.mark.parametrize("shape,n_tiles", [(0, 5), (0, 16), (1, 6)])
+def test_stream_probe_in_place(shape, n_tiles):
+    """The bandwidth probe reads and writes every value of its buffer in place (times 1.0):
+    a guard band on both sides stays untouched."""
+    H.note(f"stream_probe shape={shape} n_tiles={n_tiles}")
+    g = torch.Generator(device="cuda").manual_seed(7)
+    buf = torch.randn((n_tiles + 2) * 16384, device="cuda", generator=g)
+    before = buf.clone()
+    inner = buf[16384:(n_tiles + 1) * 16384]
+    ssm.stream_probe(inner, n_tiles, shape)
+    torch.cuda.synchronize()
+    assert torch.equal(buf, before)
