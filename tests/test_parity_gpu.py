@@ -456,9 +456,20 @@ def test_bf16_sketch(cfg):
     H.note(f"case bf16 sketch {cfg.name}")
     inp = H.Inputs(cfg, np.arange(cfg.units), cfg.steps)
     got = H.run_gpu(cfg, inp, sketch_dtype="bf16")
-    ref = H.run_oracle(cfg, inp, sketch_bf16=True)
-    H.compare(cfg, got, ref, sketch_bf16=True)
+    ref = H.run_oracle(cfg, inp, sketch_bf16=True, want_ls=True)  # want_ls: q~ for the slack
+    H.compare(cfg, got, ref, sketch_bf16=True, host_basis=inp.host_basis)
     assert got["sketch"].dtype == torch.bfloat16
+
+
+def test_bf16_sketch_workload_sampled():
+    """The GDN workload at full size with the bf16 sketch, as bench.py times it; 40 sampled
+    units, every step and window."""
+    cfg = workloads.C3
+    H.note("case bf16 sketch c3 (sampled units)")
+    inp = H.Inputs(cfg, workloads.sample_units(cfg, 40), cfg.steps)
+    got = H.run_gpu(cfg, inp, sketch_dtype="bf16")
+    ref = H.run_oracle(cfg, inp, sketch_bf16=True, want_ls=True)  # want_ls: q~ for the slack
+    H.compare(cfg, got, ref, sketch_bf16=True, host_basis=inp.host_basis)
 
 
 # Least-squares coefficients: the read is the projection of the exact window-start
@@ -472,13 +483,9 @@ LS_CASES = [
 ]
 
 
-@pytest.mark.parametrize("cfg", LS_CASES, ids=lambda c: c.name)
-def test_least_squares_coefficients(cfg):
-    H.note(f"case least squares {cfg.name}")
-    inp = H.Inputs(cfg, np.arange(cfg.units), cfg.steps)
-    got = H.run_gpu(cfg, inp, coefficients="least_squares")
-    ref = H.run_oracle(cfg, inp, want_ls=True)
-    nw = got["S"].shape[0]
+def check_least_squares(cfg, got, ref):
+    """Least-squares parity on the units the run sampled."""
+    nw, n = got["S"].shape[0], got["S"].shape[1]
     e_y = H.rel_rows(got["y_sketch"], ref["y_ls"])
     e_x = H.rel_rows(got["y_full"], ref["y_exact"])
     e_S = H.rel_mats(got["S"], ref["S_win"][:nw])
@@ -488,8 +495,8 @@ def test_least_squares_coefficients(cfg):
     e_orth = np.abs(gram - np.eye(cfg.rank)).max()
     Sk = ref["Sk"][:nw]
     resid = Sk - np.einsum("wuij,wujk->wuik", np.einsum("wuij,wukj->wuik", Sk, Q), Q)
-    e_span = float((np.linalg.norm(resid.reshape(nw, cfg.units, -1), axis=-1)
-                    / np.linalg.norm(Sk.reshape(nw, cfg.units, -1), axis=-1)).max())
+    e_span = float((np.linalg.norm(resid.reshape(nw, n, -1), axis=-1)
+                    / np.linalg.norm(Sk.reshape(nw, n, -1), axis=-1)).max())
     approx_ls = H.rel_rows(ref["y_ls"], ref["y_exact"]).mean()
     approx_pr = H.rel_rows(ref["y_sketch"], ref["y_exact"]).mean()
     H.note(f"least squares {cfg.name}: y {e_y.max():.2e} exact {e_x.max():.2e} S {e_S.max():.2e} "
@@ -500,6 +507,26 @@ def test_least_squares_coefficients(cfg):
     assert e_span <= H.S_TOL, f"sketch rows do not span the sketch: {e_span:.2e}"
     if cfg.rank == cfg.d_k:
         assert H.rel_rows(got["y_sketch"], ref["y_exact"]).max() <= H.Y_TOL
+
+
+@pytest.mark.parametrize("cfg", LS_CASES, ids=lambda c: c.name)
+def test_least_squares_coefficients(cfg):
+    H.note(f"case least squares {cfg.name}")
+    inp = H.Inputs(cfg, np.arange(cfg.units), cfg.steps)
+    got = H.run_gpu(cfg, inp, coefficients="least_squares")
+    ref = H.run_oracle(cfg, inp, want_ls=True)
+    check_least_squares(cfg, got, ref)
+
+
+def test_least_squares_workload_sampled():
+    """The GDN workload at full size (N=256, H=32, 128x128, W=8, r=8) with least-squares
+    coefficients, as bench.py times it; 40 sampled units, every step and window."""
+    cfg = workloads.C3
+    H.note("case least squares c3 (sampled units)")
+    inp = H.Inputs(cfg, workloads.sample_units(cfg, 40), cfg.steps)
+    got = H.run_gpu(cfg, inp, coefficients="least_squares")
+    ref = H.run_oracle(cfg, inp, want_ls=True)
+    check_least_squares(cfg, got, ref)
 
 
 def test_least_squares_zero_state():
