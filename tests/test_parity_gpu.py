@@ -6,6 +6,8 @@ sizes are compared on a sample of units (always the first and the last) at
 every step and after every window, in the same launch configuration the
 benchmark times.
 """
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -602,3 +604,94 @@ def test_stream_probe_in_place(shape, n_tiles):
     ssm.stream_probe(inner, n_tiles, shape)
     torch.cuda.synchronize()
     assert torch.equal(buf, before)
+
+
+def test_staggered_windows_workload_sampled():
+    """The GDN workload at full size (N=256, H=32, 128x128, W=8, r=8) on the staggered schedule
+    bench.py times: sequence n joins at step n mod W, so from step W - 1 on every step reads
+    all rows at their own window positions (one varlen read, identity slots) and updates the
+    N/W rows whose window just filled (one varlen update). Rows that have not joined are
+    padding (tau = 0) and keep their output. 40 sampled units are checked against the oracle
+    over their local steps: every output, and the final state and sketch."""
+    import oracle
+    cfg = workloads.C3
+    N, Hh, dk, dv, W = cfg.batch, cfg.heads, cfg.d_k, cfg.d_v, cfg.window
+    T = 64 + W - 1                               # the last joiner still runs 64 local steps
+    join = np.arange(N) % W
+    H.note("case staggered windows c3 (sampled units)")
+    S0 = workloads.initial_state(cfg)
+    B = workloads.basis(cfg)
+    with ThreadPoolExecutor(8) as ex:                            # local step j, row n
+        local = list(ex.map(lambda j: workloads.step_inputs(cfg, j), range(T)))
+    dev = "cuda"
+    state = H._to_dev(S0, dev).view(N, Hh, dk, dv).clone()
+    basis = H._to_dev(B, dev)
+    d = H.dims_of(cfg)
+    sketch = torch.empty((N, Hh, cfg.rank, dv), device=dev)
+    kb = torch.zeros((N, Hh, W, dk), device=dev, dtype=torch.bfloat16)
+    vb = torch.zeros((N, Hh, W, dv), device=dev, dtype=torch.bfloat16)
+    db = torch.zeros((N, Hh, W), device=dev)
+    bb = torch.zeros((N, Hh, W), device=dev)
+    ssm.window_update_refresh(d, state, sketch, basis, None, None, None, None, 0)
+    units = workloads.sample_units(cfg, 40)
+    idx = torch.as_tensor(units, device=dev)
+    sentinel = 777.0
+    y = torch.empty((N, Hh, dv), device=dev)
+    got = {int(u): [] for u in units}
+    rows = np.arange(N)
+
+    def mix(field, t):
+        """Global step t's input: row n from sequence n's local step t - join[n] (zeros
+        before it joins)."""
+        out = np.zeros_like(getattr(local[0], field))
+        for s in range(W):
+            live = (join == s) & (t >= s)
+            if live.any():
+                out[live] = getattr(local[t - s], field)[live]
+        return out
+
+    for t in range(T):
+        tau = np.where(t >= join, (t - join) % W + 1, 0).astype(np.int32)
+        y.fill_(sentinel)
+        td = lambda f: H._to_dev(np.ascontiguousarray(mix(f, t)), dev)
+        ssm.sketch_decode_step_varlen(d, N, None, H._to_dev(tau, dev), sketch, basis, td("q"),
+                                      kb, vb, db, bb, y, k_t=td("k"), v_t=td("v"),
+                                      decay_t=td("decay"), beta_t=td("beta"))
+        yc = y.view(N * Hh, dv)[idx].cpu().double().numpy()
+        for i, u in enumerate(units):
+            n = u // Hh
+            if t >= join[n]:
+                got[int(u)].append(yc[i])
+            else:
+                assert (yc[i] == sentinel).all(), f"padding row {n} written at step {t}"
+        ups = rows[tau == W].astype(np.int32)
+        if len(ups):
+            ssm.window_update_refresh_varlen(H.dims_of(cfg.with_(batch=len(ups))), N,
+                                             H._to_dev(ups, dev),
+                                             H._to_dev(np.full(len(ups), W, np.int32), dev),
+                                             state, sketch, basis, kb, vb, db, bb)
+    torch.cuda.synchronize()
+    S_end = state.view(N * Hh, dk, dv)[idx].cpu().double().numpy()
+    K_end = sketch.view(N * Hh, cfg.rank, dv)[idx].cpu().double().numpy()
+    worst = 0.0
+    for s in range(W):
+        sel = [i for i, u in enumerate(units) if join[u // Hh] == s]
+        if not sel:
+            continue
+        us = units[sel]
+        Tn = T - s
+        flat = lambda x, e: x.reshape((N * Hh,) + ((e,) if e else ()))[us]
+        pick = lambda f, e: np.stack([flat(getattr(local[j], f), e) for j in range(Tn)])
+        ref = oracle.run(cfg.rule, S0.reshape(N * Hh, dk, dv)[us].astype(np.float64),
+                         B[us % Hh].astype(np.float64), workloads.widen(pick("q", dk)),
+                         workloads.widen(pick("k", dk)), workloads.widen(pick("v", dv)),
+                         pick("decay", 0).astype(np.float64), pick("beta", 0).astype(np.float64),
+                         W)
+        g = np.stack([np.stack(got[int(u)]) for u in us], axis=1)    # [Tn][U][dv]
+        e = H.rel_rows(g, ref["y_sketch"])
+        worst = max(worst, float(e.max()))
+        assert e.max() <= H.Y_TOL, f"phase {s}: sketch read {e.max():.3e}"
+        nw = Tn // W
+        assert H.rel_mats(S_end[sel][None], ref["S_win"][nw][None]).max() <= H.S_TOL, f"phase {s}: state"
+        assert H.rel_mats(K_end[sel][None], ref["Sk"][nw][None]).max() <= H.S_TOL, f"phase {s}: sketch"
+    H.note(f"staggered c3: worst sketch-read error {worst:.2e}")
