@@ -380,6 +380,12 @@ def main() -> int:
         return float(np.mean([s_.elapsed_time(e_) for s_, e_ in evs]))
 
     tau_mid = W // 2 + 1
+    # bytes of one read at window position tau_mid, the token already buffered (no append):
+    # q + tau_mid buffered tokens + y, plus the sketch (and read map) or the full state
+    s_in = 2 if cfg.in_dtype == "bf16" else 4
+    common = cfg.d_k * s_in + tau_mid * bm["tok"] + 4 * cfg.d_v
+    sk_b = U * (bm["state_bytes_sketch"] + (4 * cfg.rank * cfg.d_k if ls else 0) + common)
+    full_b = U * (bm["state_bytes_full"] + common)
     q0 = ptrs[0][0]
     sketch_ms = kernel_time(lambda i: sketch_step(sk_p, bp, q0, kb, vb, db, bb, tau_mid, yp,
                                                   stream=sp), 20)
@@ -469,9 +475,16 @@ def main() -> int:
     for shape in (0, 1):
         ms = kernel_time(lambda i: ssm.stream_probe(probe, n_tiles, shape, stream=sp), 10)
         probe_gbs.append(2 * n_tiles * 65536 / (ms * 1e-3) / 1e9)
-    del probe
+    # and over a buffer whose read + write equals one sketch read's bytes: the ceiling of a
+    # single short streaming launch of that size, launch and ramp included
+    n_small = max(2, int(round(sk_b / 2 / 65536)) & ~1)
+    small = probe[:n_small * 16384]
+    small_ms = kernel_time(lambda i: ssm.stream_probe(small, n_small, 1, stream=sp), 20)
+    del probe, small
     stream_probe = {"bytes_each_way": n_tiles * 65536, "launches": 10,
-                    "update_order_gbs": probe_gbs[0], "flat_runs_gbs": probe_gbs[1]}
+                    "update_order_gbs": probe_gbs[0], "flat_runs_gbs": probe_gbs[1],
+                    "sketch_size_bytes": 2 * n_small * 65536,
+                    "sketch_size_gbs": 2 * n_small * 65536 / (small_ms * 1e-3) / 1e9}
 
     # ---- cold-cache kernel times: the 256 MB Infinity Cache flushed before each launch ----
     # A 512 MiB read between launches, outside the events, replaces the cached lines with
@@ -506,12 +519,6 @@ def main() -> int:
         c_sk = cold_time(lambda: sketch_step(skc_p, bp, q0, kb, vb, db, bb, tau_mid, yp, stream=sp))
         c_full = cold_time(lambda: ssm.full_read_decode_step(d, stc_p, q0, kb, vb, db, bb,
                                                              tau_mid, yp, stream=sp))
-        # bytes of one read at window position tau_mid, the token already buffered (no append):
-        # q + tau_mid buffered tokens + y, plus the sketch (and read map) or the full state
-        s_in = 2 if cfg.in_dtype == "bf16" else 4
-        common = cfg.d_k * s_in + tau_mid * bm["tok"] + 4 * cfg.d_v
-        sk_b = U * (bm["state_bytes_sketch"] + (4 * cfg.rank * cfg.d_k if ls else 0) + common)
-        full_b = U * (bm["state_bytes_full"] + common)
         cold = {"flush_bytes": flush.numel() * 4, "tau": tau_mid,
                 "update_refresh_ms": c_upd, "update_refresh_gbs": bm["update"] * U / (c_upd * 1e-3) / 1e9,
                 "sketch_decode_ms": c_sk, "sketch_decode_gbs": sk_b / (c_sk * 1e-3) / 1e9,
@@ -602,8 +609,9 @@ def main() -> int:
         "tokens_per_s": value * cfg.batch,
         "kernels_ms": {"update_refresh": upd_avg_ms, "sketch_decode": sketch_ms,
                        "full_read_decode": full_ms},
-        "sketch_decode_gbs": bm["sketch_step"] * U / (sketch_ms * 1e-3) / 1e9,
-        "full_read_decode_gbs": bm["full_step"] * U / (full_ms * 1e-3) / 1e9,
+        "sketch_decode_gbs": sk_b / (sketch_ms * 1e-3) / 1e9,
+        "full_read_decode_gbs": full_b / (full_ms * 1e-3) / 1e9,
+        "sketch_read_frac_of_stream": (sk_b / (sketch_ms * 1e-3) / 1e9) / stream_probe["sketch_size_gbs"],
         "eager_steps_per_s": a.steps / eager_s,
         "full_read_path": full,
         "speedup_vs_full_read": (value / full["steps_per_s"]) if full else None,
