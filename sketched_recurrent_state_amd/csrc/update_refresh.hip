@@ -129,7 +129,8 @@ update_refresh_kernel(float* __restrict__ state, TSK* __restrict__ sketch,
   //      substitution in fp64 with the inverse pivots that step b leaves on the
   //      diagonal; dropped rows are zero);
   //   d. every wave forms Y = Q S^T over its 32 columns: per row of S a dot product
-  //      of 4 columns, summed over the 8 lanes of the row group (lane bits 0..2);
+  //      of 4 columns, summed over the 8 lanes of the row group (lane bits 0..2) as a
+  //      reduce-scatter over four rows of Q at a time;
   //   e. the waves' partial Y are added in a fixed order and stored with Q.
   float* lQ = lB + rank * DK;  // [rank][DV] (LS only)
   float* lP = lQ + rank * DV;  // [DV / 32][rank][DK] per-wave partial Y (LS only)
@@ -178,20 +179,36 @@ update_refresh_kernel(float* __restrict__ state, TSK* __restrict__ sketch,
       }
     }
     __syncthreads();
-    for (int m = 0; m < rank; ++m) {
-      const float4 qm = *reinterpret_cast<const float4*>(lQ + m * DV + col);
+    // Four rows of Q at a time, summed over the 8 lanes of the row group as a
+    // reduce-scatter: slot sl of lane cg holds Q row m0 + (sl ^ f) with f = lane bits 2, 1
+    // of cg, so the lane that row_half_mirror pairs it with (cg ^ 7) holds the same row in
+    // slot sl ^ 3, and quad_perm 2301's partner (cg ^ 2) in slot sl ^ 1. Four adds leave
+    // row m0 + f summed over all 8 lanes (twelve as four separate all-reduces).
+    const int f = ((cg >> 1) & 1) | ((cg >> 2) << 1);
+    for (int m0 = 0; m0 < rank; m0 += 4) {
+      float4 qv[4];
+#pragma unroll
+      for (int sl = 0; sl < 4; ++sl) {
+        const int m = m0 + (sl ^ f);
+        const float4 x = *reinterpret_cast<const float4*>(lQ + min(m, rank - 1) * DV + col);
+        qv[sl] = m < rank ? x : f4(0.f);
+      }
 #pragma unroll
       for (int mm = 0; mm < RPL; ++mm) {
-        float a = qm.x * s[mm].x;
-        a = fmaf(qm.y, s[mm].y, a);
-        a = fmaf(qm.z, s[mm].z, a);
-        a = fmaf(qm.w, s[mm].w, a);
-        a += dpp<DPP_QUAD_1032>(a);    // lane bit 0
-        a += dpp<DPP_QUAD_2301>(a);    // lane bit 1
-        a += dpp<DPP_HALF_MIRROR>(a);  // the other quad of the 8 lanes (lane bit 2)
-        // every lane of the row group now holds the 32-column sum for row mm * 8 + rg;
-        // lane cg stores the rows with mm % 8 == cg
-        if ((mm & 7) == cg) lP[(wave * rank + m) * DK + mm * 8 + rg] = a;
+        float a[4];
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+          a[sl] = qv[sl].x * s[mm].x;
+          a[sl] = fmaf(qv[sl].y, s[mm].y, a[sl]);
+          a[sl] = fmaf(qv[sl].z, s[mm].z, a[sl]);
+          a[sl] = fmaf(qv[sl].w, s[mm].w, a[sl]);
+        }
+        a[0] += dpp<DPP_HALF_MIRROR>(a[3]);  // lanes cg, cg ^ 7
+        a[1] += dpp<DPP_HALF_MIRROR>(a[2]);
+        a[0] += dpp<DPP_QUAD_2301>(a[1]);    // and cg ^ 2, cg ^ 5
+        a[0] += dpp<DPP_QUAD_1032>(a[0]);    // and the other four (cg ^ 1 shares f)
+        // row m0 + f of Q against row mm * 8 + rg of S, over this wave's 32 columns
+        if (!(cg & 1) && m0 + f < rank) lP[(wave * rank + m0 + f) * DK + mm * 8 + rg] = a[0];
       }
     }
     __syncthreads();
