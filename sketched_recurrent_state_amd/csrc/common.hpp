@@ -231,6 +231,14 @@ __device__ __forceinline__ float halve8(float lo, float hi, bool upper) {
   return keep + dpp<DPP_ROR8>(send);
 }
 
+// Lane k's value of x, in every lane (two v_readlane_b32; k must be uniform).
+__device__ __forceinline__ double readlane_f64(double x, int k) {
+  const uint64_t u = __builtin_bit_cast(uint64_t, x);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, k);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), k);
+  return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
 // Sum over the 8 lanes that differ in bits 3..5 (the tile layout's d_k split).
 __device__ __forceinline__ float tile_allreduce(float x) {
   x += dpp<DPP_ROR8>(x);

@@ -155,19 +155,46 @@ update_refresh_kernel(float* __restrict__ state, TSK* __restrict__ sketch,
       for (int i = 0; i < rank; ++i) maxd = fmax(maxd, lG[i * rank + i]);
       const double thr = (double)kLsRelTol * (double)kLsRelTol * maxd;
       const int i = lane;
-      for (int k = 0; k < rank; ++k) {
-        // every lane reads row k (and its own row) before lanes i >= k write column k
-        double dk = lG[k * rank + k];
-        for (int p = 0; p < k; ++p) dk = fma(-lG[k * rank + p], lG[k * rank + p], dk);
-        const double lkk = dk > thr ? sqrt(dk) : 0.0;
-        double x = 0.0;
-        if (i > k && i < rank && lkk > 0.0) {
-          x = lG[i * rank + k];
-          for (int p = 0; p < k; ++p) x = fma(-lG[i * rank + p], lG[k * rank + p], x);
-          x /= lkk;
+      if (rank <= 8) {
+        // In registers: lane i holds row i of G, then of L; row k of L comes from lane k
+        // by readlane, so the factorisation makes no LDS round trip. Entries above the
+        // diagonal are never written back.
+        double g[8];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) g[p] = lG[min(i, rank - 1) * rank + min(p, rank - 1)];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          if (k < rank) {
+            double d = g[k];  // in lane k: its pivot, G[k][k] less its row of L so far
+#pragma unroll
+            for (int p = 0; p < k; ++p) d = fma(-g[p], g[p], d);
+            d = readlane_f64(d, k);
+            const double lkk = d > thr ? sqrt(d) : 0.0;
+            const double inv = lkk > 0.0 ? 1.0 / lkk : 0.0;
+            double x = g[k];
+#pragma unroll
+            for (int p = 0; p < k; ++p) x = fma(-g[p], readlane_f64(g[p], k), x);
+            g[k] = (i == k) ? inv : x * inv;  // the diagonal keeps the inverse pivot
+          }
         }
-        if (i > k && i < rank) lG[i * rank + k] = x;
-        if (i == k) lG[k * rank + k] = lkk > 0.0 ? 1.0 / lkk : 0.0;  // kept: the inverse pivot
+#pragma unroll
+        for (int p = 0; p < 8; ++p)
+          if (i < rank && p <= i) lG[i * rank + p] = g[p];
+      } else {  // larger ranks: through LDS
+        for (int k = 0; k < rank; ++k) {
+          // every lane reads row k (and its own row) before lanes i >= k write column k
+          double dk = lG[k * rank + k];
+          for (int p = 0; p < k; ++p) dk = fma(-lG[k * rank + p], lG[k * rank + p], dk);
+          const double lkk = dk > thr ? sqrt(dk) : 0.0;
+          double x = 0.0;
+          if (i > k && i < rank && lkk > 0.0) {
+            x = lG[i * rank + k];
+            for (int p = 0; p < k; ++p) x = fma(-lG[i * rank + p], lG[k * rank + p], x);
+            x /= lkk;
+          }
+          if (i > k && i < rank) lG[i * rank + k] = x;
+          if (i == k) lG[k * rank + k] = lkk > 0.0 ? 1.0 / lkk : 0.0;  // kept: the inverse pivot
+        }
       }
     }
     __syncthreads();
