@@ -143,7 +143,13 @@ update_refresh_kernel(float* __restrict__ state, TSK* __restrict__ sketch,
       if (e < rank * rank) {
         const float* ri = lQ + (e / rank) * DV;
         const float* rj = lQ + (e % rank) * DV;
-        for (int c = part; c < DV; c += 4) g = fma((double)ri[c], (double)rj[c], g);
+        // the rows all start on the same LDS bank: each entry walks the columns from its own
+        // offset, so the lanes of a wave read different banks
+        const int rot = 8 * (e % rank) + 32 * ((e / rank) & 1);
+        for (int c = part; c < DV; c += 4) {
+          const int cc = (c + rot) & (DV - 1);
+          g = fma((double)ri[cc], (double)rj[cc], g);
+        }
       }
       g += __shfl_xor(g, 1);
       g += __shfl_xor(g, 2);
