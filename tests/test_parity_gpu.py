@@ -491,10 +491,14 @@ def check_least_squares(cfg, got, ref):
     e_y = H.rel_rows(got["y_sketch"], ref["y_ls"])
     e_x = H.rel_rows(got["y_full"], ref["y_exact"])
     e_S = H.rel_mats(got["S"], ref["S_win"][:nw])
-    # the stored rows are orthonormal and span the oracle's sketch rows
+    # the stored rows are orthonormal, or exactly zero where the factorisation dropped a
+    # dependent row, and span the oracle's sketch rows
     Q = got["Sk"]
     gram = np.einsum("wuij,wukj->wuik", Q, Q)
-    e_orth = np.abs(gram - np.eye(cfg.rank)).max()
+    kept = np.einsum("wuii->wui", gram) > 0.5
+    assert np.all(Q[~kept] == 0.0), "a dropped sketch row is not stored as zero"
+    target = np.where(kept[..., :, None] & kept[..., None, :], np.eye(cfg.rank), 0.0)
+    e_orth = np.abs(gram - target).max()
     Sk = ref["Sk"][:nw]
     resid = Sk - np.einsum("wuij,wujk->wuik", np.einsum("wuij,wukj->wuik", Sk, Q), Q)
     e_span = float((np.linalg.norm(resid.reshape(nw, n, -1), axis=-1)
@@ -529,6 +533,30 @@ def test_least_squares_workload_sampled():
     got = H.run_gpu(cfg, inp, coefficients="least_squares")
     ref = H.run_oracle(cfg, inp, want_ls=True)
     check_least_squares(cfg, got, ref)
+
+
+@pytest.mark.parametrize("r", [8, 12])
+def test_least_squares_low_rank_state(r):
+    """A rank-2 window-start state: its sketch rows span two directions, so r - 2 rows are
+    dropped by the factorisation (r = 8 in registers, r = 12 through LDS) and the first
+    window's read, the projection of the exact read on that span, equals the exact read."""
+    cfg = small("gdn", N=2, Hh=3, W=4, T=8, r=r)
+    H.note(f"case least squares, rank-2 state, r={r}")
+    inp = H.Inputs(cfg, np.arange(cfg.units), cfg.steps)
+    rng = np.random.default_rng([0x2A, r])
+    U = rng.standard_normal((cfg.units, cfg.d_k, 2))
+    V = rng.standard_normal((cfg.units, 2, cfg.d_v))
+    S0 = (0.1 * U @ V).astype(np.float32)
+    inp.S0.copy_(torch.from_numpy(S0.reshape(inp.S0.shape)))
+    inp.host_S0 = S0.astype(np.float64)
+    got = H.run_gpu(cfg, inp, coefficients="least_squares")
+    ref = H.run_oracle(cfg, inp, want_ls=True)
+    check_least_squares(cfg, got, ref)
+    Q0 = got["Sk"][0]                                   # the first window's stored rows
+    n_rows = (np.linalg.norm(Q0, axis=-1) > 0.5).sum(axis=-1)
+    assert np.all(n_rows == 2), f"kept rows per unit: {n_rows}"
+    e = H.rel_rows(got["y_sketch"][:cfg.window], got["y_full"][:cfg.window])
+    assert e.max() <= H.Y_TOL, f"first window: least-squares read off the exact read by {e.max():.2e}"
 
 
 def test_least_squares_zero_state():
