@@ -125,9 +125,9 @@ update_refresh_kernel(float* __restrict__ state, TSK* __restrict__ sketch,
   //   b. wave 0 factors G = L L^T column by column, lane i owning row i; a row whose
   //      pivot, its squared residual against the rows before it, is below
   //      kLsRelTol^2 of the largest squared row norm is dropped (zero column of L);
-  //   c. Q = L^-1 Sk in place, one column of the sketch per thread (forward
-  //      substitution in fp64 with the inverse pivots that step b leaves on the
-  //      diagonal; dropped rows are zero);
+  //   c. step b also forms L^-1 (fp64, in place of L, the inverse pivots on the
+  //      diagonal; a dropped row is zero), then Q = L^-1 Sk in place, one column of
+  //      the sketch per thread, each row from the exact fp32 sketch;
   //   d. every wave forms Y = Q S^T over its 32 columns: per row of S a dot product
   //      of 4 columns, summed over the 8 lanes of the row group (lane bits 0..2) as a
   //      reduce-scatter over four rows of Q at a time;
@@ -163,8 +163,8 @@ update_refresh_kernel(float* __restrict__ state, TSK* __restrict__ sketch,
       const int i = lane;
       if (rank <= 8) {
         // In registers: lane i holds row i of G, then of L; row k of L comes from lane k
-        // by readlane, so the factorisation makes no LDS round trip. Entries above the
-        // diagonal are never written back.
+        // by readlane, so the factorisation makes no LDS round trip (entries above the
+        // diagonal are scratch). Only L^-1 goes back to LDS.
         double g[8];
 #pragma unroll
         for (int p = 0; p < 8; ++p) g[p] = lG[min(i, rank - 1) * rank + min(p, rank - 1)];
@@ -183,9 +183,22 @@ update_refresh_kernel(float* __restrict__ state, TSK* __restrict__ sketch,
             g[k] = (i == k) ? inv : x * inv;  // the diagonal keeps the inverse pivot
           }
         }
+        // L^-1 by columns, lane j taking column j: entry r > j is -inv_r times the sum over
+        // j <= k < r of L[r][k] L^-1[k][j] (the entries above the diagonal are zero)
+        double w[8];
 #pragma unroll
-        for (int p = 0; p < 8; ++p)
-          if (i < rank && p <= i) lG[i * rank + p] = g[p];
+        for (int r = 0; r < 8; ++r) {
+          if (r < rank) {
+            const double inv_r = readlane_f64(g[r], r);
+            double x = 0.0;
+#pragma unroll
+            for (int k = 0; k < r; ++k) x = fma(readlane_f64(g[k], r), w[k], x);
+            w[r] = (i == r) ? inv_r : (i < r ? -inv_r * x : 0.0);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r)
+          if (i < rank && r < rank && r >= i) lG[r * rank + i] = w[r];  // L^-1[r][i]
       } else {  // larger ranks: through LDS
         for (int k = 0; k < rank; ++k) {
           // every lane reads row k (and its own row) before lanes i >= k write column k
@@ -201,14 +214,28 @@ update_refresh_kernel(float* __restrict__ state, TSK* __restrict__ sketch,
           if (i > k && i < rank) lG[i * rank + k] = x;
           if (i == k) lG[k * rank + k] = lkk > 0.0 ? 1.0 / lkk : 0.0;  // kept: the inverse pivot
         }
+        // L^-1 by columns into the upper triangle (L^-1[r][j] at row j, column r), lane j
+        // taking column j; L^-1[k][j] for k >= j is then lG[j][k], the diagonal included.
+        // Once done (L is no longer read), each lane moves its column below the diagonal.
+        if (i < rank) {
+          for (int r = i + 1; r < rank; ++r) {
+            double x = 0.0;
+            for (int k = i; k < r; ++k) x = fma(lG[r * rank + k], lG[i * rank + k], x);
+            lG[i * rank + r] = -lG[r * rank + r] * x;
+          }
+        }
+        for (int r = i + 1; r < rank; ++r) lG[r * rank + i] = lG[i * rank + r];
       }
     }
     __syncthreads();
-    for (int c = tid; c < DV; c += NT) {  // c. Q = L^-1 Sk, column c
-      for (int m = 0; m < rank; ++m) {
-        double x = lQ[m * DV + c];
-        for (int p = 0; p < m; ++p) x = fma(-lG[m * rank + p], (double)lQ[p * DV + c], x);
-        lQ[m * DV + c] = (float)(x * lG[m * rank + m]);  // zero for a dropped row
+    // c. Q = L^-1 Sk, one column per thread, last row first so that row m still reads the
+    //    sketch rows p <= m it needs (in place); each row is formed in fp64 from the exact
+    //    sketch values, with no rounded row of Q feeding the next
+    for (int c = tid; c < DV; c += NT) {
+      for (int m = rank - 1; m >= 0; --m) {
+        double x = 0.0;
+        for (int p = 0; p <= m; ++p) x = fma(lG[m * rank + p], (double)lQ[p * DV + c], x);
+        lQ[m * DV + c] = (float)x;  // zero for a dropped row
       }
     }
     __syncthreads();

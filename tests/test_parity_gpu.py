@@ -559,6 +559,25 @@ def test_least_squares_low_rank_state(r):
     assert e.max() <= H.Y_TOL, f"first window: least-squares read off the exact read by {e.max():.2e}"
 
 
+def test_least_squares_ill_conditioned_sketch():
+    """A window-start state that is rank one up to a 1e-4 perturbation: its eight sketch rows
+    are dependent to about 1e-4, far from the drop threshold on most rows but near it. The
+    stored rows must still be orthonormal to 1e-5 (a forward substitution through rows of Q
+    rounded to fp32 loses about 5e-5 here)."""
+    cfg = small("gdn", N=2, Hh=3, W=4, T=8, r=8)
+    H.note("case least squares, ill-conditioned sketch")
+    inp = H.Inputs(cfg, np.arange(cfg.units), cfg.steps)
+    rng = np.random.default_rng(0x111)
+    u = rng.standard_normal((cfg.units, cfg.d_k, 1))
+    v = rng.standard_normal((cfg.units, 1, cfg.d_v))
+    S0 = (0.1 * (u @ v + 1e-4 * rng.standard_normal((cfg.units, cfg.d_k, cfg.d_v)))).astype(np.float32)
+    inp.S0.copy_(torch.from_numpy(S0.reshape(inp.S0.shape)))
+    inp.host_S0 = S0.astype(np.float64)
+    got = H.run_gpu(cfg, inp, coefficients="least_squares")
+    ref = H.run_oracle(cfg, inp, want_ls=True)
+    check_least_squares(cfg, got, ref)
+
+
 def test_least_squares_zero_state():
     """A zero state has a zero sketch: every row is dropped and the read is the window
     term alone, equal to the exact read within the first window."""
