@@ -1,0 +1,56 @@
+"""The algorithmic byte counts behind bench.py's roofline, checked on the CPU against the
+per-unit formulas written out here:
+  update + refresh:  8 d_k d_v (S in and out) + s_sk r d_v (sketch out) + W tok (the window)
+  sketch step:       s_sk r d_v + d_k s_in (q) + tau_mean tok (buffered tokens, the current
+                     one included) + tok (the current token written) + 4 d_v (y)
+with tok = (d_k + d_v) s_in + g, g = 4 (Mamba-2), 8 (GDN) or 4 d_k + 4 (KDA), and
+tau_mean = (W + 1) / 2."""
+import importlib.util
+import os
+
+import pytest
+
+import workloads
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+@pytest.fixture(scope="module")
+def bench():
+    spec = importlib.util.spec_from_file_location("bench", os.path.join(HERE, "..", "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def expected(cfg, s_sk=4):
+    s_in = 2 if cfg.in_dtype == "bf16" else 4
+    g = {"mamba2": 4, "gdn": 8, "kda": 4 * cfg.d_k + 4}[cfg.rule]
+    tok = (cfg.d_k + cfg.d_v) * s_in + g
+    update = 8 * cfg.d_k * cfg.d_v + s_sk * cfg.rank * cfg.d_v + cfg.window * tok
+    step = (s_sk * cfg.rank * cfg.d_v + cfg.d_k * s_in + (cfg.window + 1) / 2 * tok + tok
+            + 4 * cfg.d_v)
+    return update, step
+
+
+CASES = [workloads.get(n) for n in ("c1", "c2", "c3", "c4")] + \
+        [workloads.c5(r, w) for r in (4, 8, 16, 32) for w in (4, 8, 16)]
+
+
+@pytest.mark.parametrize("cfg", CASES, ids=lambda c: c.name)
+@pytest.mark.parametrize("s_sk", [4, 2])
+def test_byte_model(bench, cfg, s_sk):
+    m = bench.bytes_model(cfg, s_sk)
+    update, step = expected(cfg, s_sk)
+    assert m["update"] == update
+    assert m["sketch_step"] == pytest.approx(step)
+    assert m["state_bytes_full"] == 4 * cfg.d_k * cfg.d_v
+    assert m["state_bytes_sketch"] == s_sk * cfg.rank * cfg.d_v
+
+
+def test_gdn_workload_update_bytes(bench):
+    """GDN 128x128, W = 8, r = 8, bf16: 131072 + 4096 + 8 * 520 bytes per unit, and 8192 units
+    per launch for the roofline's algorithmic bytes."""
+    cfg = workloads.C3
+    assert bench.bytes_model(cfg)["update"] == 139_328
+    assert bench.bytes_model(cfg)["update"] * cfg.units == 1_141_374_976
