@@ -285,7 +285,8 @@ hipError_t launch_fit(const void* samples, int n_samples, int heads, int rank, f
                       hipStream_t stream) {
   constexpr size_t lds = fit_lds_floats<DK>() * sizeof(float);
   auto kern = fit_basis_kernel<DK, TIN>;
-  static const hipError_t attr = hipFuncSetAttribute(
+  // on every call (a setup-time launch), so it holds on whichever device is current
+  const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (attr != hipSuccess) return attr;
   hipLaunchKernelGGL(kern, dim3(heads), dim3(256), lds, stream, static_cast<const TIN*>(samples),
