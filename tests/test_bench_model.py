@@ -54,3 +54,41 @@ def test_gdn_workload_update_bytes(bench):
     cfg = workloads.C3
     assert bench.bytes_model(cfg)["update"] == 139_328
     assert bench.bytes_model(cfg)["update"] * cfg.units == 1_141_374_976
+
+
+@pytest.mark.parametrize("steps,warmup,want", [(20, 5, (24, 8)), (64, 16, (64, 16)),
+                                               (1, 0, (8, 0)), (0, 0, (8, 0)), (9, 17, (16, 24))])
+def test_step_rounding(bench, steps, warmup, want):
+    """Any --steps / --warmup is accepted: both are rounded up to whole windows (W = 8 here),
+    with at least one timed window, so every window's update + refresh is inside the region
+    it belongs to and the timed count is what ms_per_step describes."""
+    a = bench.parse_args(["--gpus", "1", "--steps", str(steps), "--warmup", str(warmup)])
+    assert (a.steps, a.warmup) == (steps, warmup)
+    got = bench.plan_steps(a.steps, a.warmup, workloads.C3.window)
+    assert got == want
+    assert got[0] % 8 == 0 and got[1] % 8 == 0 and got[0] >= steps and got[1] >= warmup
+
+
+def test_step_rounding_sweep_windows(bench):
+    """The sweep rounds to the largest window (16), a multiple of every sweep window."""
+    steps, warmup = bench.plan_steps(20, 5, max(workloads.C5_WINDOWS))
+    assert (steps, warmup) == (32, 16)
+    assert all(steps % w == 0 and warmup % w == 0 for w in workloads.C5_WINDOWS)
+
+
+def test_error_summary(bench):
+    """The approximation-error record: the global Frobenius ratio over all outputs and the
+    per-vector distribution, from per-vector squared norms."""
+    num = [[1.0, 4.0], [0.0, 9.0]]     # ||dy||^2 per (step, unit)
+    den = [[1.0, 16.0], [4.0, 9.0]]    # ||y_exact||^2
+    s = bench.error_summary(num, den)
+    assert s["frobenius"] == pytest.approx((14.0 / 30.0) ** 0.5)
+    assert s["max"] == pytest.approx(1.0)
+    assert s["mean"] == pytest.approx((1.0 + 0.5 + 0.0 + 1.0) / 4)
+    assert s["vectors"] == 4
+
+
+def test_bench_rejects_only_gpu_counts(bench, capsys):
+    """--gpus above 1 is the only argument the bench refuses, with a message."""
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU only" in capsys.readouterr().err
