@@ -12,6 +12,21 @@
 
 namespace ssm {
 
+// Lane j's value of x within each aligned group of G consecutive lanes (G = 16 or 32;
+// j uniform): one v_readlane per group of the wave, then a select by the lane's group.
+template <int G>
+__device__ __forceinline__ float group_bcast(float x, int j) {
+  static_assert(G == 16 || G == 32, "group size");
+  const int grp = (int)(__lane_id() / G);
+  float r = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), j));
+#pragma unroll
+  for (int g = 1; g < 64 / G; ++g) {
+    const float o = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), g * G + j));
+    r = grp == g ? o : r;
+  }
+  return r;
+}
+
 // u <- M^T u for one token on E key elements held by this lane, given s = k . u.
 //   Mamba-2: M^T u = a u;  GDN: a (u - beta s k);  KDA: alpha (.) (u - beta s k)
 template <int RULE, int E>

@@ -17,12 +17,22 @@ namespace {
 // ---------------------------------------------------------------------------
 // sketch read: G consecutive lanes per unit (G = 32, or 16 when d_k = 16).
 // A workgroup serves 256/G sequences of ONE head, so the head's basis is
-// staged once in LDS for all of them. Every global load of the step (query,
-// the tau buffered tokens, the first eight sketch rows, the basis) is issued
-// before any arithmetic: a step pays one memory latency instead of one per
-// token and one per basis vector. WMAX >= W bounds the unrolled token slots.
-// Scalar gates stay one per lane (lane i of a unit holds token i's) and are
-// broadcast when the walk reaches that token.
+// staged once in LDS for all of them.
+//
+// Issue order. Every global load of the step is issued before any arithmetic,
+// in the order the step consumes them: the head's basis (its first chunk goes
+// to LDS right away), the scalar gates, the query, the buffered tokens newest
+// first (slot j holds token tau-1-j: the walk starts at slot 0), then the first
+// eight sketch rows.
+// The number of loads does not depend on tau or the rank: a slot past tau, or a
+// sketch row past the rank, loads a clamped address (token 0, row rank-1) and its
+// result is discarded with a select, never with a branch. With a fixed count,
+// each use waits only for its own load (the memory counter is in order), so the
+// walk runs while the older tokens and the sketch rows are still arriving; and
+// no load sits in a conditional block that the compiler could sink it into.
+// A group whose batch row is inactive loads row 0 / slot 0 and stores nothing.
+// WMAX >= W bounds the token slots. Scalar gates stay one per lane (lane j of a
+// unit holds slot j's) and are broadcast when the walk reaches that slot.
 // ---------------------------------------------------------------------------
 template <int DK>
 constexpr int sketch_group() { return DK >= 32 ? 32 : 16; }
@@ -53,136 +63,156 @@ sketch_decode_kernel(const TSK* __restrict__ sketch, const float* __restrict__ b
   const int rank = rt.rank(head);
   const int row = (blockIdx.x / heads) * UPB + threadIdx.x / G;  // batch row
   const int sub = threadIdx.x % G;
+  const int tid = threadIdx.x;
   int seq = 0, tau = 0;                       // the row's persistent slot and window position
   const bool active = row < batch && rm.row(row, seq, tau);  // whole G-lane groups
-  const size_t unit = (size_t)row * heads + head;            // per-step arrays
-  const size_t punit = (size_t)seq * heads + head;           // state, sketch, buffer
+  // an inactive group reads row 0 / slot 0 (valid memory) and writes nothing
+  const int ntok = active ? tau : 1;
+  const size_t unit = (size_t)(active ? row : 0) * heads + head;    // per-step arrays
+  const int aseq = active ? seq : 0;
+  const size_t punit = (size_t)aseq * heads + head;   // state, sketch, buffer
   const size_t slot0 = punit * window;
   const bool fused = (k_t != nullptr);
 
-  // ---- issue every load ----
+  // ---- issue every load, in the order they are consumed ----
+  const float* Bh = basis + (size_t)rt.offset(head) * DK;
+  float4 b4 = f4(0.f);
+  if constexpr (!MAP) b4 = *reinterpret_cast<const float4*>(Bh + min(tid * 4, rank * DK - 4));
+  __builtin_amdgcn_sched_barrier(0);  // keep the issue order (the scheduler regroups loads)
   Packed<TIN, EK> qr, kr[WMAX];
   Packed<TIN, EV> vr[WMAX];
-  float ak[(RULE == KDA) ? WMAX : 1][EK];     // KDA: per-channel gates of each token
-  float a_lane = 1.f, b_lane = 1.f;           // scalar gates of token `sub`
+  float ak[(RULE == KDA) ? WMAX : 1][EK];     // KDA: per-channel gates of each slot
+  float a_lane = 1.f, b_lane = 1.f;           // scalar gates of slot `sub`
   float sk[RCH][EV];
   float ym[MAP ? RCH : 1][EK];                // MAP: the first read-map rows
   const float* Yu = basis + (MAP ? punit * (size_t)rank * DK + sub * EK : 0);
-  const TSK* Sku = sketch + ((size_t)seq * rt.total() + rt.offset(head)) * DV + sub * EV;
-  if (active) {
-    qr.load(q + unit * DK + sub * EK);
-#pragma unroll
-    for (int i = 0; i < WMAX; ++i) {
-      if (i < tau) {
-        const bool cur = fused && (i == tau - 1);
-        const size_t slot = slot0 + i;
-        kr[i].load((cur ? k_t + unit * DK : kbuf + slot * DK) + sub * EK);
-        vr[i].load((cur ? v_t + unit * DV : vbuf + slot * DV) + sub * EV);
-        if constexpr (RULE == KDA)
-          Vec<float, EK>::load((cur ? d_t + unit * DK : dbuf + slot * DK) + sub * EK, ak[i]);
-      }
-    }
-    if (sub < tau) {
-      const bool cur = fused && (sub == tau - 1);
-      if constexpr (RULE != KDA) a_lane = cur ? d_t[unit] : dbuf[slot0 + sub];
-      if constexpr (RULE != MAMBA2) b_lane = cur ? b_t[unit] : bbuf[slot0 + sub];
-    }
-#pragma unroll
-    for (int m = 0; m < RCH; ++m)
-      if (m < rank) Vec<TSK, EV>::load(Sku + (size_t)m * DV, sk[m]);
-    if constexpr (MAP) {
-#pragma unroll
-      for (int m = 0; m < RCH; ++m)
-        if (m < rank) Vec<float, EK>::load(Yu + (size_t)m * DK, ym[m]);
-    }
+  const TSK* Sku = sketch + ((size_t)aseq * rt.total() + rt.offset(head)) * DV + sub * EV;
+  {
+    const int js = min(sub, WMAX - 1);
+    const size_t slot = slot0 + max(ntok - 1 - js, 0);
+    const bool cur = fused && js == 0;
+    if constexpr (RULE != KDA) a_lane = cur ? d_t[unit] : dbuf[slot];
+    if constexpr (RULE != MAMBA2) b_lane = cur ? b_t[unit] : bbuf[slot];
   }
-  if constexpr (!MAP) {
-    const float* Bh = basis + (size_t)rt.offset(head) * DK;
-    for (int e = threadIdx.x * 4; e < rank * DK; e += 256 * 4)
-      *reinterpret_cast<float4*>(lB + e) = *reinterpret_cast<const float4*>(Bh + e);
+  __builtin_amdgcn_sched_barrier(0);
+  qr.load(q + unit * DK + sub * EK);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < WMAX; ++j) {
+    const size_t slot = slot0 + max(ntok - 1 - j, 0);
+    const bool cur = fused && j == 0;         // slot 0 is the current token
+    kr[j].load((cur ? k_t + unit * DK : kbuf + slot * DK) + sub * EK);
+    vr[j].load((cur ? v_t + unit * DV : vbuf + slot * DV) + sub * EV);
+    if constexpr (RULE == KDA)
+      Vec<float, EK>::load((cur ? d_t + unit * DK : dbuf + slot * DK) + sub * EK, ak[j]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int m = 0; m < RCH; ++m) Vec<TSK, EV>::load(Sku + (size_t)min(m, rank - 1) * DV, sk[m]);
+  if constexpr (MAP) {
+#pragma unroll
+    for (int m = 0; m < RCH; ++m) Vec<float, EK>::load(Yu + (size_t)min(m, rank - 1) * DK, ym[m]);
+  }
+  // the basis chunk to LDS (its load was the first issued; duplicate clamped chunks write
+  // the same values)
+  if constexpr (!MAP) *reinterpret_cast<float4*>(lB + min(tid * 4, rank * DK - 4)) = b4;
+
+  // ---- fused append: the current token (slot 0) into buffer slot tau-1 ----
+  if (active && fused) {
+    const size_t slot = slot0 + tau - 1;
+    kr[0].store(kbuf + slot * DK + sub * EK);
+    vr[0].store(vbuf + slot * DV + sub * EV);
+    if constexpr (RULE == KDA) Vec<float, EK>::store(dbuf + slot * DK + sub * EK, ak[0]);
+    if (sub == 0) {
+      if constexpr (RULE != KDA) dbuf[slot] = a_lane;
+      if constexpr (RULE != MAMBA2) bbuf[slot] = b_lane;
+    }
   }
 
+  // ---- walk the window newest to oldest; slots past tau leave u and intra as they are ----
   float u[EK], acc[EV];
+  qr.unpack(u);
 #pragma unroll
   for (int e = 0; e < EV; ++e) acc[e] = 0.f;
-  if (active) {
-    // ---- fused append: the current token into slot tau-1 ----
-    if (fused) {
-      const size_t slot = slot0 + tau - 1;
 #pragma unroll
-      for (int i = 0; i < WMAX; ++i) {
-        if (i == tau - 1) {
-          kr[i].store(kbuf + slot * DK + sub * EK);
-          vr[i].store(vbuf + slot * DV + sub * EV);
-          if constexpr (RULE == KDA) Vec<float, EK>::store(dbuf + slot * DK + sub * EK, ak[i]);
-        }
-      }
-      if (sub == tau - 1) {
-        if constexpr (RULE != KDA) dbuf[slot] = a_lane;
-        if constexpr (RULE != MAMBA2) bbuf[slot] = b_lane;
-      }
+  for (int j = 0; j < WMAX; ++j) {
+    float kk[EK], vv[EV], a[(RULE == KDA) ? EK : 1];
+    kr[j].unpack(kk);
+    vr[j].unpack(vv);
+    if constexpr (RULE == KDA) {
+#pragma unroll
+      for (int e = 0; e < EK; ++e) a[e] = ak[j][e];
+    } else {
+      a[0] = group_bcast<G>(a_lane, j);
     }
-
-    // ---- walk the window newest to oldest ----
-    qr.unpack(u);
+    const float b = (RULE == MAMBA2) ? 1.f : group_bcast<G>(b_lane, j);
+    float s = 0.f;
 #pragma unroll
-    for (int i = WMAX - 1; i >= 0; --i) {
-      if (i < tau) {
-        float kk[EK], vv[EV], a[(RULE == KDA) ? EK : 1];
-        kr[i].unpack(kk);
-        vr[i].unpack(vv);
-        if constexpr (RULE == KDA) {
+    for (int e = 0; e < EK; ++e) s = fmaf(kk[e], u[e], s);
+    s = group_allreduce<G>(s);
+    const float bs = b * s;
+    const bool live = j < ntok;
+    float un[EK];
 #pragma unroll
-          for (int e = 0; e < EK; ++e) a[e] = ak[i][e];
-        } else {
-          a[0] = __shfl(a_lane, i, G);
-        }
-        const float b = (RULE == MAMBA2) ? 1.f : __shfl(b_lane, i, G);
-        float s = 0.f;
+    for (int e = 0; e < EK; ++e) un[e] = u[e];
+    carry_back<RULE, EK>(un, kk, a, bs);
 #pragma unroll
-        for (int e = 0; e < EK; ++e) s = fmaf(kk[e], u[e], s);
-        s = group_allreduce<G>(s);
-        const float bs = b * s;
+    for (int e = 0; e < EV; ++e) acc[e] = live ? fmaf(bs, vv[e], acc[e]) : acc[e];
 #pragma unroll
-        for (int e = 0; e < EV; ++e) acc[e] = fmaf(bs, vv[e], acc[e]);
-        carry_back<RULE, EK>(u, kk, a, bs);
-      }
-    }
+    for (int e = 0; e < EK; ++e) u[e] = live ? un[e] : u[e];
   }
-  if constexpr (!MAP) __syncthreads();  // the basis is in LDS
-  if (!active) return;
+  if constexpr (!MAP) {
+    // basis chunks past the first (rank * d_k > 4 * 256), then every wave's chunk is in LDS
+    for (int e = (tid + 256) * 4; e < rank * DK; e += 256 * 4)
+      *reinterpret_cast<float4*>(lB + e) = *reinterpret_cast<const float4*>(Bh + e);
+    __syncthreads();
+  }
 
   // ---- c_m = b_m . q~ ; y = intra + sum_m c_m Sk[m] ----
-  for (int m0 = 0; m0 < rank; m0 += RCH) {
-    if (m0 > 0) {
+  // the first RCH rows (issued with the step's loads); rows past the rank are discarded
 #pragma unroll
-      for (int m = 0; m < RCH; ++m) {
-        if (m0 + m < rank) {
-          Vec<TSK, EV>::load(Sku + (size_t)(m0 + m) * DV, sk[m]);
-          if constexpr (MAP) Vec<float, EK>::load(Yu + (size_t)(m0 + m) * DK, ym[m]);
-        }
-      }
+  for (int m = 0; m < RCH; ++m) {
+    float bm[EK];
+    if constexpr (MAP) {
+#pragma unroll
+      for (int e = 0; e < EK; ++e) bm[e] = ym[m][e];
+    } else {
+      Vec<float, EK>::load(lB + min(m, rank - 1) * DK + sub * EK, bm);
+    }
+    float c = 0.f;
+#pragma unroll
+    for (int e = 0; e < EK; ++e) c = fmaf(bm[e], u[e], c);
+    c = group_allreduce<G>(c);
+    const bool live = m < rank;
+#pragma unroll
+    for (int e = 0; e < EV; ++e) acc[e] = live ? fmaf(c, sk[m][e], acc[e]) : acc[e];
+  }
+  // further rows, RCH at a time, one more memory round trip each
+  for (int m0 = RCH; m0 < rank; m0 += RCH) {
+#pragma unroll
+    for (int m = 0; m < RCH; ++m) {
+      Vec<TSK, EV>::load(Sku + (size_t)min(m0 + m, rank - 1) * DV, sk[m]);
+      if constexpr (MAP) Vec<float, EK>::load(Yu + (size_t)min(m0 + m, rank - 1) * DK, ym[m]);
     }
 #pragma unroll
     for (int m = 0; m < RCH; ++m) {
-      if (m0 + m < rank) {
-        float bm[EK];
-        if constexpr (MAP) {
+      float bm[EK];
+      if constexpr (MAP) {
 #pragma unroll
-          for (int e = 0; e < EK; ++e) bm[e] = ym[m][e];
-        } else {
-          Vec<float, EK>::load(lB + (m0 + m) * DK + sub * EK, bm);
-        }
-        float c = 0.f;
-#pragma unroll
-        for (int e = 0; e < EK; ++e) c = fmaf(bm[e], u[e], c);
-        c = group_allreduce<G>(c);
-#pragma unroll
-        for (int e = 0; e < EV; ++e) acc[e] = fmaf(c, sk[m][e], acc[e]);
+        for (int e = 0; e < EK; ++e) bm[e] = ym[m][e];
+      } else {
+        Vec<float, EK>::load(lB + min(m0 + m, rank - 1) * DK + sub * EK, bm);
       }
+      float c = 0.f;
+#pragma unroll
+      for (int e = 0; e < EK; ++e) c = fmaf(bm[e], u[e], c);
+      c = group_allreduce<G>(c);
+      const bool live = m0 + m < rank;
+#pragma unroll
+      for (int e = 0; e < EV; ++e) acc[e] = live ? fmaf(c, sk[m][e], acc[e]) : acc[e];
     }
   }
-  Vec<float, EV>::store(y + unit * DV + sub * EV, acc);
+  if (active) Vec<float, EV>::store(y + unit * DV + sub * EV, acc);
 }
 
 }  // namespace
