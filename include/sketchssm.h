@@ -65,7 +65,7 @@
 extern "C" {
 #endif
 
-#define SSM_ABI_VERSION 4
+#define SSM_ABI_VERSION 5
 
 typedef enum { SSM_MAMBA2 = 0, SSM_GDN = 1, SSM_KDA = 2 } ssm_rule;
 typedef enum { SSM_IN_BF16 = 0, SSM_IN_F32 = 1 } ssm_in_dtype;
@@ -236,6 +236,42 @@ ssm_status ssm_sketch_decode_step_varlen(const ssm_dims* d, int32_t num_slots,
                                          const float* decay_t, const float* beta_t,
                                          void* k_buf, void* v_buf, float* decay_buf,
                                          float* beta_buf, float* y, void* stream);
+
+/*
+ * One serving decode step over a slot pool in a single launch (ABI version 5).
+ * Source: the pages' once-per-window state write and every-step sketch read
+ * (readsearch.ai listing of arXiv 2609.33051, Abstract; agihunt.info summary,
+ * "Mechanism details"), for a batch whose sequences sit at different window
+ * positions; the schedule itself is not on the pages. For every batch row n
+ * with slot s = slot[n] (or n when slot is NULL) and tau[n] in [1, W]:
+ *   1. the current token (k_t, v_t, decay_t, beta_t of row n) is appended into
+ *      window slot tau[n] - 1 of slot s;
+ *   2. y[n] is the sketch read at window position tau[n], as
+ *      ssm_sketch_decode_step, from sketch0 when parity[n] is 0 and from
+ *      sketch1 otherwise;
+ *   3. if n is one of the n_update rows listed in update_rows (DEVICE int32
+ *      batch-row indices, distinct) and tau[n] == W, the window's W tokens (the
+ *      current one included) are applied to state[s], and the refreshed sketch
+ *      is stored in the other buffer (sketch1 when parity[n] is 0, else
+ *      sketch0). A listed row with tau[n] != W is not updated.
+ * The two sketch buffers let a row at tau = W read its window's sketch while
+ * the same launch writes the next one; the caller flips parity[n] for the
+ * row's next window. Rows with tau outside [1, W] or slot outside
+ * [0, num_slots) are skipped (nothing is read for them and y[n] is not
+ * written). slot, tau and parity are DEVICE int32 [batch] arrays (4-byte
+ * aligned; parity required); the counts in them are not read on the host.
+ * Rows must map to distinct slots. Layouts as the other _varlen entry points,
+ * sketch0 and sketch1 each [num_slots][H][r][d_v] in d->sketch_dtype; uniform
+ * rank. Outputs: y, state, sketch0, sketch1 and the window buffers, none of
+ * which may overlap an input or each other.
+ */
+ssm_status ssm_decode_step_varlen(const ssm_dims* d, int32_t num_slots, const int32_t* slot,
+                                  const int32_t* tau, const int32_t* parity, int32_t n_update,
+                                  const int32_t* update_rows, float* state, void* sketch0,
+                                  void* sketch1, const float* basis, const void* q,
+                                  const void* k_t, const void* v_t, const float* decay_t,
+                                  const float* beta_t, void* k_buf, void* v_buf,
+                                  float* decay_buf, float* beta_buf, float* y, void* stream);
 
 /*
  * Least-squares coefficients: the other reading of the pages' "low-rank

@@ -22,7 +22,8 @@ __all__ = [
     "abi_version", "buffer_append", "window_update_refresh", "sketch_decode_step",
     "full_read_decode_step", "recurrent_decode_step", "window_update_refresh_ranked",
     "sketch_decode_step_ranked", "rank_offsets", "window_update_refresh_varlen",
-    "sketch_decode_step_varlen", "window_update_refresh_ls", "sketch_decode_step_ls",
+    "sketch_decode_step_varlen", "decode_step_varlen", "window_update_refresh_ls",
+    "sketch_decode_step_ls",
     "fit_basis", "stream_probe", "SKETCH_F32", "SKETCH_BF16", "LIB_PATH", "HEADER",
     "declared_symbols", "numel", "library",
 ]
@@ -100,6 +101,8 @@ def _load():
     lib.ssm_window_update_refresh_varlen.argtypes = [dp, i32] + [vp] * 9 + [vp]
     lib.ssm_sketch_decode_step_varlen.restype = i32
     lib.ssm_sketch_decode_step_varlen.argtypes = [dp, i32] + [vp] * 15
+    lib.ssm_decode_step_varlen.restype = i32
+    lib.ssm_decode_step_varlen.argtypes = [dp, i32, vp, vp, vp, i32] + [vp] * 15 + [vp]
     lib.ssm_recurrent_decode_step.restype = i32
     lib.ssm_recurrent_decode_step.argtypes = [dp] + [vp] * 7 + [vp]
     lib.ssm_full_read_decode_step.restype = i32
@@ -445,6 +448,39 @@ def sketch_decode_step_varlen(d: Dims, num_slots: int, slot, tau, sketch, basis,
         _addr(decay_t, "decay_t", f32, n["decay_t"]), _addr(beta_t, "beta_t", f32, n["beta_t"]),
         _addr(k_buf, "k_buf", tin, n["k_buf"]), _addr(v_buf, "v_buf", tin, n["v_buf"]),
         _addr(decay_buf, "decay_buf", f32, n["decay_buf"]),
+        _addr(beta_buf, "beta_buf", f32, n["beta_buf"]), _addr(y, "y", f32, n["y"]),
+        _stream(stream)))
+
+
+def decode_step_varlen(d: Dims, num_slots: int, slot, tau, parity, n_update: int, update_rows,
+                       state, sketch0, sketch1, basis, q, k_t, v_t, decay_t, beta_t, k_buf,
+                       v_buf, decay_buf, beta_buf, y, stream=None) -> None:
+    """ssm_decode_step_varlen: one serving step in one launch. Every row reads y at its own
+    window position tau (device int32 [batch]) from sketch0 or sketch1 (parity, device int32
+    [batch]) with the current token appended; the n_update rows listed in update_rows (device
+    int32) whose window fills (tau == W) also apply the window to the state and store the
+    refreshed sketch in the other buffer."""
+    args = (slot, tau, parity, update_rows, state, sketch0, sketch1, basis, q, k_t, v_t, decay_t,
+            beta_t, k_buf, v_buf, decay_buf, beta_buf, y)
+    if isinstance(stream, int) and _all_raw(args):
+        return _check(_lib.ssm_decode_step_varlen(
+            ctypes.byref(d), int(num_slots), slot, tau, parity, int(n_update), update_rows, state,
+            sketch0, sketch1, basis, q, k_t, v_t, decay_t, beta_t, k_buf, v_buf, decay_buf,
+            beta_buf, y, stream))
+    tin, f32 = _types(d, args)
+    i32 = None if tin is None else _i32()
+    n = _pool_numel(d, num_slots)
+    sk = _sk_types(d, f32)
+    _check(_lib.ssm_decode_step_varlen(
+        ctypes.byref(d), int(num_slots), _addr(slot, "slot", i32, n["rows"]),
+        _addr(tau, "tau", i32, n["rows"]), _addr(parity, "parity", i32, n["rows"]),
+        int(n_update), _addr(update_rows, "update_rows", i32, int(n_update) if n_update else None),
+        _addr(state, "state", f32, n["state"]), _addr(sketch0, "sketch0", sk, n["sketch"]),
+        _addr(sketch1, "sketch1", sk, n["sketch"]), _addr(basis, "basis", f32, n["basis"]),
+        _addr(q, "q", tin, n["q"]), _addr(k_t, "k_t", tin, n["k_t"]),
+        _addr(v_t, "v_t", tin, n["v_t"]), _addr(decay_t, "decay_t", f32, n["decay_t"]),
+        _addr(beta_t, "beta_t", f32, n["beta_t"]), _addr(k_buf, "k_buf", tin, n["k_buf"]),
+        _addr(v_buf, "v_buf", tin, n["v_buf"]), _addr(decay_buf, "decay_buf", f32, n["decay_buf"]),
         _addr(beta_buf, "beta_buf", f32, n["beta_buf"]), _addr(y, "y", f32, n["y"]),
         _stream(stream)))
 

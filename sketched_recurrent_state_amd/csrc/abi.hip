@@ -549,4 +549,52 @@ ssm_status ssm_sketch_decode_step_varlen(const ssm_dims* d, int32_t num_slots,
                   fn);
 }
 
+ssm_status ssm_decode_step_varlen(const ssm_dims* d, int32_t num_slots, const int32_t* slot,
+                                  const int32_t* tau, const int32_t* parity, int32_t n_update,
+                                  const int32_t* update_rows, float* state, void* sketch0,
+                                  void* sketch1, const float* basis, const void* q,
+                                  const void* k_t, const void* v_t, const float* decay_t,
+                                  const float* beta_t, void* k_buf, void* v_buf,
+                                  float* decay_buf, float* beta_buf, float* y, void* stream) {
+  static const char* fn = "ssm_decode_step_varlen";
+  ssm_status st = check_dims(d, fn);
+  if (st != SSM_OK) return st;
+  if (n_update < 0 || n_update > d->batch)
+    return fail(SSM_E_RANGE, "%s: n_update %d not in [0, batch = %d]", fn, n_update, d->batch);
+  if (d->batch == 0) return ok();
+  if ((st = check_pool(*d, num_slots, slot, tau, "tau", fn)) != SSM_OK) return st;
+  if (parity == nullptr) return fail(SSM_E_NULL, "%s: parity is NULL", fn);
+  if (n_update > 0 && update_rows == nullptr)
+    return fail(SSM_E_NULL, "%s: update_rows is NULL with n_update = %d", fn, n_update);
+  if (state == nullptr) return fail(SSM_E_NULL, "%s: state is NULL", fn);
+  if (sketch0 == nullptr) return fail(SSM_E_NULL, "%s: sketch0 is NULL", fn);
+  if (sketch1 == nullptr) return fail(SSM_E_NULL, "%s: sketch1 is NULL", fn);
+  if (basis == nullptr) return fail(SSM_E_NULL, "%s: basis is NULL", fn);
+  if (q == nullptr) return fail(SSM_E_NULL, "%s: q is NULL", fn);
+  if (y == nullptr) return fail(SSM_E_NULL, "%s: y is NULL", fn);
+  if (k_t == nullptr)
+    return fail(SSM_E_NULL, "%s: k_t is NULL (the step appends the current token)", fn);
+  if ((st = check_token(*d, k_t, v_t, decay_t, beta_t, fn)) != SSM_OK) return st;
+  if ((st = check_buffers(*d, k_buf, v_buf, decay_buf, beta_buf, fn)) != SSM_OK) return st;
+  const Sizes z = pool_sizes(*d, num_slots);
+  const size_t rows = (size_t)d->batch * 4;
+  st = check_arrays(fn, {{state, z.state, true, "state"}, {sketch0, z.sketch, true, "sketch0"},
+                         {sketch1, z.sketch, true, "sketch1"}, {basis, z.basis, false, "basis"},
+                         {q, z.qk, false, "q"}, {k_t, z.qk, false, "k_t"}, {v_t, z.v, false, "v_t"},
+                         {decay_t, z.dtok, false, "decay_t"}, {beta_t, z.btok, false, "beta_t"},
+                         {k_buf, z.kbuf, true, "k_buf"}, {v_buf, z.vbuf, true, "v_buf"},
+                         {decay_buf, z.dbuf, true, "decay_buf"},
+                         {beta_buf, z.bbuf, true, "beta_buf"}, {y, z.y, true, "y"},
+                         {slot, rows, false, "slot", 4}, {tau, rows, false, "tau", 4},
+                         {parity, rows, false, "parity", 4},
+                         {update_rows, (size_t)n_update * 4, false, "update_rows", 4}});
+  if (st != SSM_OK) return st;
+  (void)hipGetLastError();
+  return launched(ssm::launch_decode_step(*d, num_slots, slot, tau, parity, n_update,
+                                          update_rows, state, sketch0, sketch1, basis, q, k_t,
+                                          v_t, decay_t, beta_t, k_buf, v_buf, decay_buf,
+                                          beta_buf, y, reinterpret_cast<hipStream_t>(stream)),
+                  fn);
+}
+
 }  // extern "C"

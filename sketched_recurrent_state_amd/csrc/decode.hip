@@ -15,6 +15,16 @@ hipError_t launch_sketch_decode_rule(const ssm_dims& d, const int32_t* rank_offs
                                      float* decay_buf, float* beta_buf, int tau, float* y,
                                      hipStream_t stream, const Varlen* varlen, bool per_unit_map);
 
+template <int RULE>
+hipError_t launch_decode_step_rule(const ssm_dims& d, int num_slots, const int32_t* slot,
+                                   const int32_t* tau, const int32_t* parity, int n_update,
+                                   const int32_t* update_rows, float* state, void* sketch0,
+                                   void* sketch1, const float* basis, const void* q,
+                                   const void* k_t, const void* v_t, const float* decay_t,
+                                   const float* beta_t, void* k_buf, void* v_buf,
+                                   float* decay_buf, float* beta_buf, float* y,
+                                   hipStream_t stream);
+
 namespace {
 
 // ---------------------------------------------------------------------------
@@ -120,6 +130,31 @@ hipError_t launch_sketch_decode(const ssm_dims& d, const int32_t* rank_offsets,
       return launch_sketch_decode_rule<KDA>(d, rank_offsets, sketch, basis, q, k_t, v_t, decay_t,
                                             beta_t, k_buf, v_buf, decay_buf, beta_buf, tau, y,
                                             stream, varlen, per_unit_map);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_step(const ssm_dims& d, int num_slots, const int32_t* slot,
+                              const int32_t* tau, const int32_t* parity, int n_update,
+                              const int32_t* update_rows, float* state, void* sketch0,
+                              void* sketch1, const float* basis, const void* q, const void* k_t,
+                              const void* v_t, const float* decay_t, const float* beta_t,
+                              void* k_buf, void* v_buf, float* decay_buf, float* beta_buf,
+                              float* y, hipStream_t stream) {
+  switch (d.rule) {
+    case SSM_MAMBA2:
+      return launch_decode_step_rule<MAMBA2>(d, num_slots, slot, tau, parity, n_update,
+                                             update_rows, state, sketch0, sketch1, basis, q, k_t,
+                                             v_t, decay_t, beta_t, k_buf, v_buf, decay_buf,
+                                             beta_buf, y, stream);
+    case SSM_GDN:
+      return launch_decode_step_rule<GDN>(d, num_slots, slot, tau, parity, n_update, update_rows,
+                                          state, sketch0, sketch1, basis, q, k_t, v_t, decay_t,
+                                          beta_t, k_buf, v_buf, decay_buf, beta_buf, y, stream);
+    case SSM_KDA:
+      return launch_decode_step_rule<KDA>(d, num_slots, slot, tau, parity, n_update, update_rows,
+                                          state, sketch0, sketch1, basis, q, k_t, v_t, decay_t,
+                                          beta_t, k_buf, v_buf, decay_buf, beta_buf, y, stream);
   }
   return hipErrorInvalidValue;
 }

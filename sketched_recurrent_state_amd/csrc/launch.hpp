@@ -124,6 +124,17 @@ hipError_t launch_sketch_decode(const ssm_dims& d, const int32_t* rank_offsets,
                                 hipStream_t stream, const Varlen* varlen = nullptr,
                                 bool per_unit_map = false);
 
+// The single-launch serving step (decode_step.hpp): the read of every batch row at its own
+// window position with the fused append, and the window update of the n_update listed rows,
+// with a double-buffered sketch chosen per row by parity.
+hipError_t launch_decode_step(const ssm_dims& d, int num_slots, const int32_t* slot,
+                              const int32_t* tau, const int32_t* parity, int n_update,
+                              const int32_t* update_rows, float* state, void* sketch0,
+                              void* sketch1, const float* basis, const void* q, const void* k_t,
+                              const void* v_t, const float* decay_t, const float* beta_t,
+                              void* k_buf, void* v_buf, float* decay_buf, float* beta_buf,
+                              float* y, hipStream_t stream);
+
 hipError_t launch_full_read_decode(const ssm_dims& d, const float* state, const void* q,
                                    const void* k_t, const void* v_t, const float* decay_t,
                                    const float* beta_t, void* k_buf, void* v_buf,

@@ -40,16 +40,19 @@ constexpr int sketch_group() { return DK >= 32 ? 32 : 16; }
 // MAP: `basis` is a per-unit read map [N][H][r][d_k] (least-squares coefficients,
 // row m giving c_m = row . q~), read from memory like the sketch rows, instead of
 // the head's basis in LDS.
+//
+// Block `blk` of a read launch: heads * ceil(batch / (256 / G)) blocks of 256 threads.
+// sketch_alt / parity (both null, or both set): a double-buffered sketch, the row's
+// current one being sketch_alt where parity[row] is non-zero, else sketch.
 template <int RULE, int DK, int DV, typename TIN, typename TSK, int WMAX, bool MAP, typename RT,
           typename RM>
-__global__ void __launch_bounds__(256)
-sketch_decode_kernel(const TSK* __restrict__ sketch, const float* __restrict__ basis,
-                     const TIN* __restrict__ q, const TIN* __restrict__ k_t,
-                     const TIN* __restrict__ v_t, const float* __restrict__ d_t,
-                     const float* __restrict__ b_t, TIN* __restrict__ kbuf,
-                     TIN* __restrict__ vbuf, float* __restrict__ dbuf, float* __restrict__ bbuf,
-                     float* __restrict__ y, int batch, int heads, int window, const RT rt,
-                     const RM rm) {
+__device__ __forceinline__ void sketch_read_block(
+    int blk, const TSK* __restrict__ sketch, const float* __restrict__ basis,
+    const TIN* __restrict__ q, const TIN* __restrict__ k_t, const TIN* __restrict__ v_t,
+    const float* __restrict__ d_t, const float* __restrict__ b_t, TIN* kbuf, TIN* vbuf,
+    float* dbuf, float* bbuf, float* __restrict__ y, int batch, int heads, int window,
+    const RT& rt, const RM& rm, const TSK* __restrict__ sketch_alt,
+    const int32_t* __restrict__ parity) {
   constexpr int G = sketch_group<DK>();
   static_assert(WMAX <= G, "one gate per lane");
   constexpr int UPB = 256 / G;                // sequences per workgroup
@@ -59,9 +62,9 @@ sketch_decode_kernel(const TSK* __restrict__ sketch, const float* __restrict__ b
   extern __shared__ float4 lds4[];
   float* lB = reinterpret_cast<float*>(lds4);  // [rank][DK]
 
-  const int head = blockIdx.x % heads;
+  const int head = blk % heads;
   const int rank = rt.rank(head);
-  const int row = (blockIdx.x / heads) * UPB + threadIdx.x / G;  // batch row
+  const int row = (blk / heads) * UPB + threadIdx.x / G;  // batch row
   const int sub = threadIdx.x % G;
   const int tid = threadIdx.x;
   int seq = 0, tau = 0;                       // the row's persistent slot and window position
@@ -86,7 +89,8 @@ sketch_decode_kernel(const TSK* __restrict__ sketch, const float* __restrict__ b
   float sk[RCH][EV];
   float ym[MAP ? RCH : 1][EK];                // MAP: the first read-map rows
   const float* Yu = basis + (MAP ? punit * (size_t)rank * DK + sub * EK : 0);
-  const TSK* Sku = sketch + ((size_t)aseq * rt.total() + rt.offset(head)) * DV + sub * EV;
+  const TSK* skb = (parity != nullptr && active && parity[row] != 0) ? sketch_alt : sketch;
+  const TSK* Sku = skb + ((size_t)aseq * rt.total() + rt.offset(head)) * DV + sub * EV;
   {
     const int js = min(sub, WMAX - 1);
     const size_t slot = slot0 + max(ntok - 1 - js, 0);
@@ -213,6 +217,21 @@ sketch_decode_kernel(const TSK* __restrict__ sketch, const float* __restrict__ b
     }
   }
   if (active) Vec<float, EV>::store(y + unit * DV + sub * EV, acc);
+}
+
+template <int RULE, int DK, int DV, typename TIN, typename TSK, int WMAX, bool MAP, typename RT,
+          typename RM>
+__global__ void __launch_bounds__(256)
+sketch_decode_kernel(const TSK* __restrict__ sketch, const float* __restrict__ basis,
+                     const TIN* __restrict__ q, const TIN* __restrict__ k_t,
+                     const TIN* __restrict__ v_t, const float* __restrict__ d_t,
+                     const float* __restrict__ b_t, TIN* __restrict__ kbuf,
+                     TIN* __restrict__ vbuf, float* __restrict__ dbuf, float* __restrict__ bbuf,
+                     float* __restrict__ y, int batch, int heads, int window, const RT rt,
+                     const RM rm) {
+  sketch_read_block<RULE, DK, DV, TIN, TSK, WMAX, MAP, RT, RM>(
+      blockIdx.x, sketch, basis, q, k_t, v_t, d_t, b_t, kbuf, vbuf, dbuf, bbuf, y, batch, heads,
+      window, rt, rm, nullptr, nullptr);
 }
 
 }  // namespace

@@ -48,7 +48,7 @@ def test_every_declared_symbol_is_exported():
 
 
 def test_version_and_status_strings():
-    assert ssm.abi_version() == 4
+    assert ssm.abi_version() == 5
     lib = ssm.library()
     for code in range(7):
         assert lib.ssm_status_string(code).decode()
@@ -337,3 +337,46 @@ def test_stream_probe_validation():
     assert st == 2 and "even" in msg
     st, msg = status_of(ssm.stream_probe, p[0] + 4, 8, 0)
     assert st == 3 and "buf" in msg
+
+
+def test_decode_step_varlen_validation():
+    """The single-launch serving step: argument checks before anything is launched."""
+    p = addrs(24)
+    d = dims(batch=4)
+    P = 8  # pool slots
+
+    def call(**kw):
+        a = dict(num_slots=P, slot=p[0], tau=p[1], parity=p[2], n_update=1, update_rows=p[3],
+                 state=p[4], sketch0=p[5], sketch1=p[6], basis=p[7], q=p[8], k_t=p[9], v_t=p[10],
+                 decay_t=p[11], beta_t=p[12], k_buf=p[13], v_buf=p[14], decay_buf=p[15],
+                 beta_buf=p[16], y=p[17])
+        a.update(kw)
+        return status_of(ssm.decode_step_varlen, d, a.pop("num_slots"), a.pop("slot"),
+                         a.pop("tau"), a.pop("parity"), a.pop("n_update"), a.pop("update_rows"),
+                         **a)
+
+    st, msg = call(parity=None)
+    assert st == 1 and "parity" in msg
+    st, msg = call(update_rows=None)
+    assert st == 1 and "update_rows" in msg
+    for n in (-1, 5):
+        st, msg = call(n_update=n)
+        assert st == 4 and "n_update" in msg
+    st, msg = call(k_t=None, v_t=None, decay_t=None, beta_t=None)
+    assert st == 1 and "k_t" in msg
+    st, msg = call(sketch1=None)
+    assert st == 1 and "sketch1" in msg
+    # the two sketch buffers may not overlap each other (pool-sized: 8 slots x 3 heads x 4 x 64)
+    st, msg = call(sketch1=p[5] + 8 * 3 * 4 * 64 * 4 - 16)
+    assert st == 5 and "sketch0 overlaps sketch1" in msg
+    # nor may y overlap the parity array
+    st, msg = call(y=p[2])
+    assert st == 5 and "overlaps" in msg
+    st, msg = call(num_slots=2, slot=None)
+    assert st == 2 and "slot map" in msg
+    # no update rows: the list may be NULL; the call then stops at the NULL state
+    st, msg = call(n_update=0, update_rows=None, state=None)
+    assert st == 1 and "state" in msg
+    # an empty batch is a no-op
+    d0 = dims(batch=0)
+    assert status_of(ssm.decode_step_varlen, d0, P, *([None] * 3), 0, *([None] * 16))[0] == 0

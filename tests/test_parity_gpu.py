@@ -693,19 +693,15 @@ def test_stream_probe_in_place(shape, n_tiles):
     assert torch.equal(buf, before)
 
 
-def test_staggered_windows_workload_sampled():
-    """The GDN workload at full size (N=256, H=32, 128x128, W=8, r=8) on the staggered schedule
-    bench.py times: sequence n joins at step n mod W, so from step W - 1 on every step reads
-    all rows at their own window positions (one varlen read, identity slots) and updates the
-    N/W rows whose window just filled (one varlen update). Rows that have not joined are
-    padding (tau = 0) and keep their output. 40 sampled units are checked against the oracle
-    over their local steps: every output, and the final state and sketch."""
-    import oracle
-    cfg = workloads.C3
+def _staggered_run(cfg, T, units, single_launch: bool):
+    """The staggered schedule at full size: sequence n joins at step n mod W; every step reads
+    all rows at their own window positions (identity slots, padding rows at tau = 0 before
+    they join) and updates the N/W rows whose window just filled. single_launch: one
+    ssm_decode_step_varlen per step (double-buffered sketch, parity per row); else a varlen
+    read and a varlen update per step. Returns the sampled units' outputs per local step and
+    the final state and current sketch of those units."""
     N, Hh, dk, dv, W = cfg.batch, cfg.heads, cfg.d_k, cfg.d_v, cfg.window
-    T = 64 + W - 1                               # the last joiner still runs 64 local steps
     join = np.arange(N) % W
-    H.note("case staggered windows c3 (sampled units)")
     S0 = workloads.initial_state(cfg)
     B = workloads.basis(cfg)
     with ThreadPoolExecutor(8) as ex:                            # local step j, row n
@@ -714,13 +710,12 @@ def test_staggered_windows_workload_sampled():
     state = H._to_dev(S0, dev).view(N, Hh, dk, dv).clone()
     basis = H._to_dev(B, dev)
     d = H.dims_of(cfg)
-    sketch = torch.empty((N, Hh, cfg.rank, dv), device=dev)
+    sketch = [torch.empty((N, Hh, cfg.rank, dv), device=dev) for _ in range(2)]
     kb = torch.zeros((N, Hh, W, dk), device=dev, dtype=torch.bfloat16)
     vb = torch.zeros((N, Hh, W, dv), device=dev, dtype=torch.bfloat16)
     db = torch.zeros((N, Hh, W), device=dev)
     bb = torch.zeros((N, Hh, W), device=dev)
-    ssm.window_update_refresh(d, state, sketch, basis, None, None, None, None, 0)
-    units = workloads.sample_units(cfg, 40)
+    ssm.window_update_refresh(d, state, sketch[0], basis, None, None, None, None, 0)
     idx = torch.as_tensor(units, device=dev)
     sentinel = 777.0
     y = torch.empty((N, Hh, dv), device=dev)
@@ -739,11 +734,24 @@ def test_staggered_windows_workload_sampled():
 
     for t in range(T):
         tau = np.where(t >= join, (t - join) % W + 1, 0).astype(np.int32)
+        parity = np.where(t >= join, ((t - join) // W) % 2, 0).astype(np.int32)
         y.fill_(sentinel)
         td = lambda f: H._to_dev(np.ascontiguousarray(mix(f, t)), dev)
-        ssm.sketch_decode_step_varlen(d, N, None, H._to_dev(tau, dev), sketch, basis, td("q"),
-                                      kb, vb, db, bb, y, k_t=td("k"), v_t=td("v"),
-                                      decay_t=td("decay"), beta_t=td("beta"))
+        ups = rows[tau == W].astype(np.int32)
+        if single_launch:
+            ssm.decode_step_varlen(d, N, None, H._to_dev(tau, dev), H._to_dev(parity, dev),
+                                   len(ups), H._to_dev(ups, dev) if len(ups) else None, state,
+                                   sketch[0], sketch[1], basis, td("q"), td("k"), td("v"),
+                                   td("decay"), td("beta"), kb, vb, db, bb, y)
+        else:
+            ssm.sketch_decode_step_varlen(d, N, None, H._to_dev(tau, dev), sketch[0], basis,
+                                          td("q"), kb, vb, db, bb, y, k_t=td("k"), v_t=td("v"),
+                                          decay_t=td("decay"), beta_t=td("beta"))
+            if len(ups):
+                ssm.window_update_refresh_varlen(H.dims_of(cfg.with_(batch=len(ups))), N,
+                                                 H._to_dev(ups, dev),
+                                                 H._to_dev(np.full(len(ups), W, np.int32), dev),
+                                                 state, sketch[0], basis, kb, vb, db, bb)
         yc = y.view(N * Hh, dv)[idx].cpu().double().numpy()
         for i, u in enumerate(units):
             n = u // Hh
@@ -751,15 +759,20 @@ def test_staggered_windows_workload_sampled():
                 got[int(u)].append(yc[i])
             else:
                 assert (yc[i] == sentinel).all(), f"padding row {n} written at step {t}"
-        ups = rows[tau == W].astype(np.int32)
-        if len(ups):
-            ssm.window_update_refresh_varlen(H.dims_of(cfg.with_(batch=len(ups))), N,
-                                             H._to_dev(ups, dev),
-                                             H._to_dev(np.full(len(ups), W, np.int32), dev),
-                                             state, sketch, basis, kb, vb, db, bb)
     torch.cuda.synchronize()
     S_end = state.view(N * Hh, dk, dv)[idx].cpu().double().numpy()
-    K_end = sketch.view(N * Hh, cfg.rank, dv)[idx].cpu().double().numpy()
+    # each sequence's current sketch: after its last full window (single launch: the buffer
+    # its parity selects next)
+    K = [sk.view(N * Hh, cfg.rank, dv)[idx].cpu().double().numpy() for sk in sketch]
+    nwin = (T - join[units // Hh]) // W
+    cur = nwin % 2 if single_launch else np.zeros_like(nwin)
+    K_end = np.where(cur[:, None, None] == 1, K[1], K[0])
+    return got, S_end, K_end, S0, B, local, join
+
+
+def _staggered_check(cfg, T, units, got, S_end, K_end, S0, B, local, join):
+    import oracle
+    N, Hh, dk, dv, W = cfg.batch, cfg.heads, cfg.d_k, cfg.d_v, cfg.window
     worst = 0.0
     for s in range(W):
         sel = [i for i, u in enumerate(units) if join[u // Hh] == s]
@@ -781,4 +794,147 @@ def test_staggered_windows_workload_sampled():
         nw = Tn // W
         H.assert_mats(S_end[sel][None], ref["S_win"][nw][None], H.S_TOL, f"phase {s}: state")
         H.assert_mats(K_end[sel][None], ref["Sk"][nw][None], H.S_TOL, f"phase {s}: sketch")
+    return worst
+
+
+def test_staggered_windows_workload_sampled():
+    """The GDN workload at full size (N=256, H=32, 128x128, W=8, r=8) on the staggered schedule
+    bench.py times: sequence n joins at step n mod W, so from step W - 1 on every step reads
+    all rows at their own window positions (one varlen read, identity slots) and updates the
+    N/W rows whose window just filled (one varlen update). Rows that have not joined are
+    padding (tau = 0) and keep their output. 40 sampled units are checked against the oracle
+    over their local steps: every output, and the final state and sketch."""
+    cfg = workloads.C3
+    T = 64 + cfg.window - 1                      # the last joiner still runs 64 local steps
+    H.note("case staggered windows c3 (sampled units)")
+    units = workloads.sample_units(cfg, 40)
+    res = _staggered_run(cfg, T, units, single_launch=False)
+    worst = _staggered_check(cfg, T, units, *res)
     H.note(f"staggered c3: worst sketch-read error {worst:.2e}")
+
+
+def test_single_launch_step_staggered_workload_sampled():
+    """The same staggered schedule through ssm_decode_step_varlen, one launch per step (the
+    read of every row, the update of the rows whose window fills, a double-buffered sketch
+    chosen per row by parity), as bench.py times it: against the oracle, and bit for bit
+    equal to the two-launch schedule (same arithmetic; the update takes the window's newest
+    token from the step's inputs instead of the buffer, the same bits)."""
+    cfg = workloads.C3
+    T = 64 + cfg.window - 1
+    H.note("case single-launch staggered step c3 (sampled units)")
+    units = workloads.sample_units(cfg, 40)
+    one = _staggered_run(cfg, T, units, single_launch=True)
+    worst = _staggered_check(cfg, T, units, *one)
+    two = _staggered_run(cfg, T, units, single_launch=False)
+    for u in units:
+        assert np.array_equal(np.stack(one[0][int(u)]), np.stack(two[0][int(u)])), f"unit {u}"
+    assert np.array_equal(one[1], two[1]) and np.array_equal(one[2], two[2])
+    H.note(f"single-launch staggered c3: worst sketch-read error {worst:.2e}")
+
+
+@pytest.mark.parametrize("rule", ["mamba2", "gdn", "kda"])
+@pytest.mark.parametrize("sketch_dtype", ["f32", "bf16"])
+def test_single_launch_step_continuous_batching(rule, sketch_dtype):
+    """ssm_decode_step_varlen with sequences joining at different steps into permuted pool
+    slots, reversed row order and a padding row (tau = 0, its output left untouched): every
+    sequence against its own oracle run (outputs every step, state and current sketch at the
+    end). A bf16 sketch is compared with the oracle's rounding through oracle values only,
+    as in the harness (the stored element within its rounding window; the read beyond what
+    those windows allow within the fp32 tolerance)."""
+    import oracle
+    W, T = 4, 14
+    joins = [0, 1, 2, 3, 5, 6]
+    slots = [5, 0, 7, 2, 3, 6]
+    P = 8                                      # pool size
+    cfg = small(rule, d_k=64, d_v=64, W=W, r=8, N=len(joins), Hh=3, T=T)
+    H.note(f"case single-launch step, continuous batching {rule} {sketch_dtype}")
+    Hh, dk, dv = cfg.heads, cfg.d_k, cfg.d_v
+    S0 = np.concatenate([workloads.initial_state(cfg, [n]) for n in range(len(joins))])
+    B = workloads.basis(cfg)
+    steps = [workloads.step_inputs(cfg, j) for j in range(T)]   # local step j, row n = sequence n
+    d_pool = H.dims_of(cfg.with_(batch=P), sketch_dtype)
+    dev = "cuda"
+    tin = torch.bfloat16
+    skt = torch.bfloat16 if sketch_dtype == "bf16" else torch.float32
+
+    def td(x):
+        return None if x is None else H._to_dev(np.ascontiguousarray(x), dev)
+
+    state = torch.zeros((P, Hh, dk, dv), device=dev)
+    sketch = [torch.zeros((P, Hh, cfg.rank, dv), device=dev, dtype=skt) for _ in range(2)]
+    kb = torch.zeros((P, Hh, W, dk), device=dev, dtype=tin)
+    vb = torch.zeros((P, Hh, W, dv), device=dev, dtype=tin)
+    dshape = (P, Hh, W, dk) if rule == "kda" else (P, Hh, W)
+    db = torch.zeros(dshape, device=dev)
+    bb = torch.zeros((P, Hh, W), device=dev) if rule != "mamba2" else None
+    basis = td(B)
+    got_y = {n: [] for n in range(len(joins))}
+    sentinel = 777.0
+    for t in range(T):
+        joining = [n for n in range(len(joins)) if joins[n] == t]
+        for n in joining:
+            state[slots[n]] = torch.from_numpy(S0[n]).to(dev)
+        if joining:   # refresh-only pass into buffer 0 for the sequences that just joined
+            dj = H.dims_of(cfg.with_(batch=len(joining)), sketch_dtype)
+            ssm.window_update_refresh_varlen(
+                dj, P, td(np.array([slots[n] for n in joining], np.int32)),
+                td(np.zeros(len(joining), np.int32)), state, sketch[0], basis, kb, vb, db, bb)
+        active = [n for n in range(len(joins)) if joins[n] <= t][::-1]   # reversed row order
+        rows = active + [None]                                          # + one padding row
+        tau = [((t - joins[n]) % W) + 1 if n is not None else 0 for n in rows]
+        par = [((t - joins[n]) // W) % 2 if n is not None else 0 for n in rows]
+        slot_rows = [slots[n] if n is not None else 1 for n in rows]
+        pick = lambda x, n: x[n] if n is not None else np.zeros_like(x[0])
+        loc = lambda n: t - joins[n] if n is not None else 0
+        q = np.stack([pick(steps[loc(n)].q, n) for n in rows])
+        k = np.stack([pick(steps[loc(n)].k, n) for n in rows])
+        v = np.stack([pick(steps[loc(n)].v, n) for n in rows])
+        dc = np.stack([pick(steps[loc(n)].decay, n) for n in rows])
+        bt = (np.stack([pick(steps[loc(n)].beta, n) for n in rows]) if rule != "mamba2" else None)
+        ups = np.array([i for i in range(len(active)) if tau[i] == W], np.int32)
+        dr = H.dims_of(cfg.with_(batch=len(rows)), sketch_dtype)
+        y = torch.full((len(rows), Hh, dv), sentinel, device=dev)
+        ssm.decode_step_varlen(dr, P, td(np.array(slot_rows, np.int32)),
+                               td(np.array(tau, np.int32)), td(np.array(par, np.int32)),
+                               len(ups), td(ups) if len(ups) else None, state, sketch[0],
+                               sketch[1], basis, td(q), td(k), td(v), td(dc), td(bt), kb, vb, db,
+                               bb, y)
+        yc = y.cpu().double().numpy()
+        assert (yc[-1] == sentinel).all(), "padding row was written"
+        for i, n in enumerate(active):
+            got_y[n].append(yc[i])
+    torch.cuda.synchronize()
+    for n in range(len(joins)):
+        Tn = T - joins[n]
+        wid = lambda x, e: x.reshape((cfg.batch, Hh) + ((e,) if e else ()))[n]
+        hq = np.stack([workloads.widen(wid(steps[j].q, dk)) for j in range(Tn)])
+        hk = np.stack([workloads.widen(wid(steps[j].k, dk)) for j in range(Tn)])
+        hv = np.stack([workloads.widen(wid(steps[j].v, dv)) for j in range(Tn)])
+        hd = np.stack([wid(steps[j].decay, dk if rule == "kda" else 0) for j in range(Tn)]).astype(np.float64)
+        hb = (np.stack([wid(steps[j].beta, 0) for j in range(Tn)]).astype(np.float64)
+              if rule != "mamba2" else None)
+        bf = sketch_dtype == "bf16"
+        Bf = B.astype(np.float64)
+        ref = oracle.run(rule, S0[n].astype(np.float64), Bf, hq, hk, hv, hd, hb, W,
+                         sketch_bf16=bf, want_ls=bf)
+        nw = Tn // W
+        gy = np.stack(got_y[n])
+        gK = sketch[nw % 2][slots[n]].float().cpu().double().numpy()
+        if bf:
+            # oracle values only: the stored element lies in its rounding window around the
+            # unrounded sketch, and the read may move by what those windows allow
+            ref_exact = oracle.run(rule, S0[n].astype(np.float64), Bf, hq, hk, hv, hd, hb, W)
+            c_sub = cfg.with_(batch=1)
+            slack = H.bf16_read_slack(c_sub, ref, ref_exact, Bf)
+            e = H.rel_diff_rows(np.maximum(np.abs(gy - ref["y_sketch"]) - slack, 0.0),
+                                ref["y_sketch"])
+            lo, hi = H.bf16_window(ref_exact["Sk"][nw][None], H.S_TOL)
+            assert np.all((gK[None] >= lo) & (gK[None] <= hi)), f"sequence {n}: bf16 sketch"
+        else:
+            e = H.rel_rows(gy, ref["y_sketch"])
+            H.assert_mats(gK[None, None], ref["Sk"][nw][None, None], H.S_TOL, f"sequence {n}: sketch")
+        assert e.max() <= H.Y_TOL, f"sequence {n}: sketch read {e.max():.3e}"
+        gS = state[slots[n]].cpu().double().numpy()
+        H.assert_mats(gS[None, None], ref["S_win"][nw][None, None], H.S_TOL, f"sequence {n}: state")
+    # slots 4 and 1 were never assigned to a sequence: untouched
+    assert torch.count_nonzero(state[4]) == 0 and torch.count_nonzero(state[1]) == 0
