@@ -50,8 +50,8 @@ ssm_status check_dims(const ssm_dims* d, const char* fn) {
   if (d->heads < 1) return fail(SSM_E_SHAPE, "%s: heads %d < 1", fn, d->heads);
   if (!in_set(d->d_k, {16, 32, 64, 128}))
     return fail(SSM_E_SHAPE, "%s: d_k %d not in {16, 32, 64, 128}", fn, d->d_k);
-  if (!in_set(d->d_v, {32, 64, 128}))
-    return fail(SSM_E_SHAPE, "%s: d_v %d not in {32, 64, 128}", fn, d->d_v);
+  if (!in_set(d->d_v, {16, 32, 64, 128}))
+    return fail(SSM_E_SHAPE, "%s: d_v %d not in {16, 32, 64, 128}", fn, d->d_v);
   if (d->window < 1 || d->window > 16)
     return fail(SSM_E_SHAPE, "%s: window %d not in [1, 16]", fn, d->window);
   const int rmax = d->d_k < 32 ? d->d_k : 32;
@@ -264,6 +264,9 @@ static ssm_status update_refresh_impl(const char* fn, const ssm_dims* d, const i
   if (ls) {
     if (d->sketch_dtype != SSM_SKETCH_F32)
       return fail(SSM_E_RANGE, "%s: least-squares coefficients need an fp32 sketch", fn);
+    if (d->d_v < 32)
+      return fail(SSM_E_SHAPE, "%s: least-squares coefficients need d_v >= 32 (got %d)", fn,
+                  d->d_v);
     if (sketch == nullptr) return fail(SSM_E_NULL, "%s: sketch_q is NULL", fn);
     if (read_map == nullptr) return fail(SSM_E_NULL, "%s: read_map is NULL", fn);
   }
@@ -307,6 +310,9 @@ static ssm_status sketch_decode_impl(const char* fn, const ssm_dims* d, const in
   if (d->batch == 0) return ok();
   if (ls && d->sketch_dtype != SSM_SKETCH_F32)
     return fail(SSM_E_RANGE, "%s: least-squares coefficients need an fp32 sketch", fn);
+  if (ls && d->d_v < 32)
+    return fail(SSM_E_SHAPE, "%s: least-squares coefficients need d_v >= 32 (got %d)", fn,
+                d->d_v);
   if (sketch == nullptr) return fail(SSM_E_NULL, "%s: %s is NULL", fn, ls ? "sketch_q" : "sketch");
   if (basis == nullptr) return fail(SSM_E_NULL, "%s: %s is NULL", fn, ls ? "read_map" : "basis");
   if (q == nullptr) return fail(SSM_E_NULL, "%s: q is NULL", fn);

@@ -1,15 +1,18 @@
 // common.hpp -- device helpers shared by the SketchSSM kernels (gfx950 only).
 //
 // Lane layouts used by the kernels:
-//  * state tile ("tile"): one workgroup per (sequence, head) unit, one wave per
-//    32-column block of the d_k x d_v state. Lane l owns 4 adjacent columns
-//    (cg = l % 8, one 128-bit load per row, so 8 lanes cover a full 128-byte
-//    line) of d_k/8 rows (rg = l / 8): contiguous rows rg*d_k/8 ... in the
-//    read kernels, interleaved rows rg, rg + 8, rg + 16, ... in the window
-//    update (its 4 waves then cover 8 whole rows, 4 KB of contiguous memory,
-//    per load instruction). A reduction over d_k is a sum over the 8 lanes that
-//    share cg, i.e. over lane bits 3, 4 and 5: DPP row_ror:8 for bit 3 and the
-//    gfx950 permlane16/permlane32 swaps for bits 4 and 5.
+//  * state tile ("tile", TileLayout): one workgroup per (sequence, head) unit,
+//    one wave per 32-column block of the d_k x d_v state (one wave for d_v =
+//    16). Lane l owns 4 adjacent columns (column group cg = l % CG, one 128-bit
+//    load per row) of d_k/RG rows (row group rg = l / CG). CG = 8 for d_v >= 32:
+//    8 lanes cover a 128-byte line, RG = 8; CG = 4 for d_v = 16: 4 lanes cover
+//    the 64-byte row, RG = 16. Rows are contiguous per lane (rg*d_k/RG ...) in
+//    the read kernels and interleaved (rg, rg + RG, ...) in the window update,
+//    whose waves then cover RG whole rows of contiguous memory per load
+//    instruction. A reduction over d_k is a sum over the RG lanes that share cg,
+//    i.e. over lane bits 3, 4 and 5 (and 2 when CG = 4): DPP row_ror:8 for bit
+//    3, the gfx950 permlane16/permlane32 swaps for bits 4 and 5, and for bit 2
+//    a row_half_mirror followed by a quad_perm reversal (lane l ^ 4).
 //  * group: G = 16 or 32 consecutive lanes per unit, each holding d_k/G key
 //    elements and d_v/G value elements; reductions are DPP row operations plus,
 //    for G = 32, one permlane16 swap.
@@ -191,6 +194,7 @@ constexpr int DPP_QUAD_2301 = 0x4E;  // quad_perm:[2,3,0,1]
 constexpr int DPP_ROR4 = 0x124;      // row_ror:4
 constexpr int DPP_ROR8 = 0x128;      // row_ror:8
 constexpr int DPP_HALF_MIRROR = 0x141;  // row_half_mirror: lane p <-> 7 - p in each 8 lanes
+constexpr int DPP_QUAD_3210 = 0x1B;   // quad_perm:[3,2,1,0]
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float x) {
@@ -239,6 +243,24 @@ __device__ __forceinline__ double readlane_f64(double x, int k) {
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
+// The value of lane l ^ 4: reversing each 8 lanes (p -> 7 - p) and then each 4
+// (p -> 3 - p) maps position p to p ^ 4.
+__device__ __forceinline__ float xor4(float x) {
+  return dpp<DPP_QUAD_3210>(dpp<DPP_HALF_MIRROR>(x));
+}
+
+// The state tile for d_k x d_v (see the top of this file): column groups per wave,
+// row groups, rows per lane, waves and threads per unit.
+template <int DK, int DV>
+struct TileLayout {
+  static constexpr int CG = DV >= 32 ? 8 : 4;
+  static constexpr int RG = 64 / CG;
+  static constexpr int RPL = DK / RG;
+  static constexpr int WAVES = DV / (4 * CG);
+  static constexpr int NT = 64 * WAVES;
+  static_assert(RPL >= 1 && WAVES >= 1, "tile shape");
+};
+
 // Sum over the 8 lanes that differ in bits 3..5 (the tile layout's d_k split).
 __device__ __forceinline__ float tile_allreduce(float x) {
   x += dpp<DPP_ROR8>(x);
@@ -263,6 +285,25 @@ __device__ __forceinline__ float4 tile_allreduce(float4 v) {
   const auto b = __builtin_amdgcn_permlane32_swap(h[1], h[1], false, false);  // [0] y, [1] w
   return make_float4(__uint_as_float(a[0]), __uint_as_float(b[0]), __uint_as_float(a[1]),
                      __uint_as_float(b[1]));
+}
+
+// Sum over the lanes of a tile that share this lane's column group (all RG row
+// groups): lane bits 3..5, and bit 2 first when a wave holds 4 column groups.
+template <int CG>
+__device__ __forceinline__ float tile_sum(float x) {
+  if constexpr (CG == 4) x += xor4(x);
+  return tile_allreduce(x);
+}
+
+template <int CG>
+__device__ __forceinline__ float4 tile_sum(float4 v) {
+  if constexpr (CG == 4) {
+    v.x += xor4(v.x);
+    v.y += xor4(v.y);
+    v.z += xor4(v.z);
+    v.w += xor4(v.w);
+  }
+  return tile_allreduce(v);
 }
 
 // Sum over the 16 lanes of a DPP row.
@@ -392,12 +433,12 @@ __host__ __device__ inline int window_lds_floats(int n) {
   return n * DK + n * DV + pad4(n * DSTR) + ((RULE == MAMBA2) ? 0 : pad4(n));
 }
 
-// Position in LDS of d_k index i for the interleaved row layout (lane group
-// g owns rows g, g + 8, g + 16, ...): group g's d_k / 8 values are stored
-// contiguously so each lane reads them with vector loads.
-template <int DK>
+// Position in LDS of d_k index i for the interleaved row layout (row group g
+// of RG owns rows g, g + RG, g + 2 RG, ...): group g's d_k / RG values are
+// stored contiguously so each lane reads them with vector loads.
+template <int DK, int RG = 8>
 __host__ __device__ __forceinline__ int interleaved_pos(int i) {
-  return (i & 7) * (DK / 8) + (i >> 3);
+  return (i % RG) * (DK / RG) + i / RG;
 }
 
 // Cooperative copy by the NT threads of a workgroup, in two phases so that a
@@ -409,9 +450,9 @@ __host__ __device__ __forceinline__ int interleaved_pos(int i) {
 // stay exact); only lanes in range store. With a fused append the newest slot
 // (n - 1) is read from the current token and also written into the buffer. With
 // PERM the d_k-indexed rows (keys, and KDA's per-row gates) are stored in
-// interleaved_pos order. Requires n >= 1; the caller synchronises the workgroup
-// before reading the LDS.
-template <int RULE, int DK, int DV, typename TIN, int NT, bool PERM = false>
+// interleaved_pos order (RG row groups). Requires n >= 1; the caller synchronises
+// the workgroup before reading the LDS.
+template <int RULE, int DK, int DV, typename TIN, int NT, bool PERM = false, int RG = 8>
 struct WindowStage {
   static constexpr int DSTR = (RULE == KDA) ? DK : 1;
   static constexpr int VIN = 16 / sizeof(TIN);       // input elements per chunk
@@ -453,7 +494,7 @@ struct WindowStage {
       if constexpr (PERM) {
         const int t0 = e - e % DK, i0 = e % DK;
 #pragma unroll
-        for (int j = 0; j < VIN; ++j) lk[t0 + interleaved_pos<DK>(i0 + j)] = f[j];
+        for (int j = 0; j < VIN; ++j) lk[t0 + interleaved_pos<DK, RG>(i0 + j)] = f[j];
       } else {
         Vec<float, VIN>::store(lk + e, f);
       }
@@ -469,7 +510,7 @@ struct WindowStage {
       if constexpr (PERM && RULE == KDA) {
         const int t0 = e - e % DK, i0 = e % DK;
 #pragma unroll
-        for (int j = 0; j < VG; ++j) ld[t0 + interleaved_pos<DK>(i0 + j)] = g[j];
+        for (int j = 0; j < VG; ++j) ld[t0 + interleaved_pos<DK, RG>(i0 + j)] = g[j];
       } else {
         Vec<float, VG>::store(ld + e, g);
       }

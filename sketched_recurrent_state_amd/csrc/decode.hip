@@ -35,14 +35,14 @@ namespace {
 // its own (no synchronisation after the staging barrier).
 // ---------------------------------------------------------------------------
 template <int RULE, int DK, int DV, typename TIN>
-__global__ void __launch_bounds__(2 * DV)
+__global__ void __launch_bounds__((TileLayout<DK, DV>::NT))
 full_read_kernel(const float* __restrict__ state, const TIN* __restrict__ q,
                  const TIN* __restrict__ k_t, const TIN* __restrict__ v_t,
                  const float* __restrict__ d_t, const float* __restrict__ b_t,
                  TIN* __restrict__ kbuf, TIN* __restrict__ vbuf, float* __restrict__ dbuf,
                  float* __restrict__ bbuf, float* __restrict__ y, int window, int tau) {
-  constexpr int RPL = DK / 8;
-  constexpr int NT = 2 * DV;
+  using TL = TileLayout<DK, DV>;
+  constexpr int CG = TL::CG, RPL = TL::RPL, NT = TL::NT;
   constexpr int DSTR = (RULE == KDA) ? DK : 1;
   constexpr int EA = (RULE == KDA) ? RPL : 1;
 
@@ -52,8 +52,8 @@ full_read_kernel(const float* __restrict__ state, const TIN* __restrict__ q,
   const int unit = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int cg = lane & 7, rg = lane >> 3;
-  const int col = wave * 32 + cg * 4;
+  const int cg = lane % CG, rg = lane / CG;
+  const int col = wave * (4 * CG) + cg * 4;
   const int row0 = rg * RPL;
   const size_t slot0 = (size_t)unit * window;
   const bool fused = (k_t != nullptr);
@@ -96,7 +96,7 @@ full_read_kernel(const float* __restrict__ state, const TIN* __restrict__ q,
     float sd = 0.f;
 #pragma unroll
     for (int m = 0; m < RPL; ++m) sd = fmaf(kk[m], u[m], sd);
-    sd = tile_allreduce(sd);
+    sd = tile_sum<CG>(sd);
     const float bs = b * sd;
     acc = fma4(bs, vv, acc);
     carry_back<RULE, RPL>(u, kk, a, bs);
@@ -105,7 +105,7 @@ full_read_kernel(const float* __restrict__ state, const TIN* __restrict__ q,
   float4 out = f4(0.f);
 #pragma unroll
   for (int m = 0; m < RPL; ++m) out = fma4(u[m], s[m], out);
-  out = add4(tile_allreduce(out), acc);
+  out = add4(tile_sum<CG>(out), acc);
   if (rg == 0) *reinterpret_cast<float4*>(y + (size_t)unit * DV + col) = out;
 }
 
@@ -169,7 +169,8 @@ hipError_t launch_full_read_decode(const ssm_dims& d, const float* state, const 
     using TIN = typename decltype(T)::type;
     constexpr int kR = decltype(R)::value, kDK = decltype(DK)::value, kDV = decltype(DV)::value;
     const size_t lds = (size_t)window_lds_floats<kR, kDK, kDV>(tau) * sizeof(float);
-    hipLaunchKernelGGL((full_read_kernel<kR, kDK, kDV, TIN>), dim3(units), dim3(2 * kDV), lds,
+    hipLaunchKernelGGL((full_read_kernel<kR, kDK, kDV, TIN>), dim3(units),
+                       dim3(TileLayout<kDK, kDV>::NT), lds,
                        stream, state, static_cast<const TIN*>(q), static_cast<const TIN*>(k_t),
                        static_cast<const TIN*>(v_t), decay_t, beta_t, static_cast<TIN*>(k_buf),
                        static_cast<TIN*>(v_buf), decay_buf, beta_buf, y, d.window, tau);

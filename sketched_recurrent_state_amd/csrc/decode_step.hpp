@@ -78,9 +78,13 @@ decode_step_varlen_kernel(const DecodeStepArgs<TIN, TSK> a) {
         a.sketch1, a.parity);
     return;
   }
-  if (threadIdx.x >= 2 * DV) return;  // an update uses 2 d_v threads (whole waves)
-  const int head = idx % a.heads;
-  const int r = a.update_rows[idx / a.heads];
+  if (threadIdx.x >= TileLayout<DK, DV>::NT) return;  // an update's threads (whole waves)
+  // update block idx runs on XCD idx % 8 (see block_role): give each XCD a contiguous run
+  // of update units, as the window update's own launch does (a bijection on [0, nu))
+  const int nu = a.update_blocks, x = idx & 7, q8 = nu >> 3, rem = nu & 7;
+  const int uidx = x * q8 + min(x, rem) + (idx >> 3);
+  const int head = uidx % a.heads;
+  const int r = a.update_rows[uidx / a.heads];
   if (r < 0 || r >= a.batch) return;
   const int s = a.slot ? a.slot[r] : r;
   if (s < 0 || s >= a.num_slots || a.tau[r] != a.window) return;  // not a full window
@@ -111,7 +115,7 @@ hipError_t launch_decode_step_rule(const ssm_dims& d, int num_slots, const int32
   return dispatch_shape(d.in_dtype, d.d_k, d.d_v, [&](auto DK, auto DV, auto T) {
     using TIN = typename decltype(T)::type;
     constexpr int kDK = decltype(DK)::value, kDV = decltype(DV)::value;
-    constexpr unsigned UPB = 256u / sketch_group<kDK>();
+    constexpr unsigned UPB = 256u / sketch_group<kDK, kDV>();
     const int read_blocks = d.heads * (int)((d.batch + UPB - 1) / UPB);
     const int update_blocks = n_update * d.heads;
     const size_t rd_lds = (size_t)d.rank * kDK * sizeof(float);

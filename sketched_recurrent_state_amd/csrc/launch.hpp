@@ -30,6 +30,7 @@ template <typename F>
 hipError_t dispatch_shape(int in_dtype, int dk, int dv, F&& f) {
   auto with_dv = [&](auto DK, auto T) -> hipError_t {
     switch (dv) {
+      case 16: return f(DK, std::integral_constant<int, 16>{}, T);
       case 32: return f(DK, std::integral_constant<int, 32>{}, T);
       case 64: return f(DK, std::integral_constant<int, 64>{}, T);
       case 128: return f(DK, std::integral_constant<int, 128>{}, T);
@@ -56,6 +57,7 @@ template <typename F>
 hipError_t dispatch(int rule, int in_dtype, int dk, int dv, F&& f) {
   auto with_dv = [&](auto R, auto DK, auto T) -> hipError_t {
     switch (dv) {
+      case 16: return f(R, DK, std::integral_constant<int, 16>{}, T);
       case 32: return f(R, DK, std::integral_constant<int, 32>{}, T);
       case 64: return f(R, DK, std::integral_constant<int, 64>{}, T);
       case 128: return f(R, DK, std::integral_constant<int, 128>{}, T);

@@ -6,11 +6,11 @@
 // the full state, writes the state back and reads y = S^T q.
 //
 // Same state-tile layout and memory order as the windowed update: one
-// workgroup per unit, d_v/32 waves, 4 columns x d_k/8 rows per lane with lane
-// group rg owning the interleaved rows rg, rg + 8, ... (each load instruction
-// of the workgroup covers 8 whole rows of S), and the block index remapped so
-// each XCD streams one contiguous run of units. The d_k reductions run over
-// lane bits 3..5 (DPP row_ror:8 and the gfx950 permlane swaps).
+// workgroup per unit, d_v/32 waves (one for d_v = 16), 4 columns x d_k/RG rows
+// per lane with row group rg owning the interleaved rows rg, rg + RG, ... (each
+// load instruction of the workgroup covers RG whole rows of S), and the block
+// index remapped so each XCD streams one contiguous run of units. The d_k
+// reductions run over lane bits 3..5 (and 2 for d_v = 16).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -19,13 +19,13 @@ namespace ssm {
 namespace {
 
 template <int RULE, int DK, int DV, typename TIN>
-__global__ void __launch_bounds__(2 * DV)
+__global__ void __launch_bounds__((TileLayout<DK, DV>::NT))
 recurrent_step_kernel(float* __restrict__ state, const TIN* __restrict__ q,
                       const TIN* __restrict__ k_t, const TIN* __restrict__ v_t,
                       const float* __restrict__ d_t, const float* __restrict__ b_t,
                       float* __restrict__ y) {
-  constexpr int RPL = DK / 8;
-  constexpr int NT = 2 * DV;
+  using TL = TileLayout<DK, DV>;
+  constexpr int CG = TL::CG, RG = TL::RG, RPL = TL::RPL, NT = TL::NT;
   constexpr int J = (DK + NT - 1) / NT;  // d_k elements staged per thread
   constexpr int NA = (RULE == KDA) ? DK : 1;
   // one pad slot past d_k takes the clamped lanes' stores
@@ -39,9 +39,9 @@ recurrent_step_kernel(float* __restrict__ state, const TIN* __restrict__ q,
   const int unit = xcd * q8 + min(xcd, rem) + (blockIdx.x >> 3);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int cg = lane & 7, rg = lane >> 3;
-  const int col = wave * 32 + cg * 4;
-  const int row0 = rg * RPL;  // this lane's d_k / 8 values in lk, lq, la (interleaved_pos)
+  const int cg = lane % CG, rg = lane / CG;
+  const int col = wave * (4 * CG) + cg * 4;
+  const int row0 = rg * RPL;  // this lane's d_k / RG values in lk, lq, la (interleaved_pos)
 
   // the token's small inputs first: issued behind the 64 KB state stream they
   // would wait for all of it. Indices are clamped so every lane issues the same
@@ -60,15 +60,15 @@ recurrent_step_kernel(float* __restrict__ state, const TIN* __restrict__ q,
   float* Su = state + (size_t)unit * (DK * DV);
   float4 s[RPL];
 #pragma unroll
-  for (int m = 0; m < RPL; ++m) s[m] = load_stream(Su + (size_t)(m * 8 + rg) * DV + col);
+  for (int m = 0; m < RPL; ++m) s[m] = load_stream(Su + (size_t)(m * RG + rg) * DV + col);
 
   // k, q (and KDA's per-row gates) to LDS in the interleaved order while the
-  // state is in flight; s[m] holds row m * 8 + rg. The stores are unconditional
+  // state is in flight; s[m] holds row m * RG + rg. The stores are unconditional
   // (clamped lanes write the pad slot) so the loads above stay where they are.
 #pragma unroll
   for (int j = 0; j < J; ++j) {
     const int i = tid + j * NT;
-    const int pos = (i < DK) ? interleaved_pos<DK>(i) : DK;
+    const int pos = (i < DK) ? interleaved_pos<DK, RG>(i) : DK;
     lk[pos] = kx[j];
     lq[pos] = qx[j];
     if constexpr (RULE == KDA) la[pos] = ax[j];
@@ -90,7 +90,7 @@ recurrent_step_kernel(float* __restrict__ state, const TIN* __restrict__ q,
     float4 p = f4(0.f);
 #pragma unroll
     for (int m = 0; m < RPL; ++m) p = fma4(kr[m], s[m], p);
-    p = tile_allreduce(p);  // S^T k
+    p = tile_sum<CG>(p);  // S^T k
     const float4 w = scale4(b, sub4(v4, scale4(a, p)));
 #pragma unroll
     for (int m = 0; m < RPL; ++m) s[m] = fma4(kr[m], w, scale4(a, s[m]));
@@ -102,19 +102,19 @@ recurrent_step_kernel(float* __restrict__ state, const TIN* __restrict__ q,
       s[m] = scale4(ar[m], s[m]);
       p = fma4(kr[m], s[m], p);
     }
-    p = tile_allreduce(p);
+    p = tile_sum<CG>(p);
     const float4 w = scale4(b, sub4(v4, p));
 #pragma unroll
     for (int m = 0; m < RPL; ++m) s[m] = fma4(kr[m], w, s[m]);
   }
 #pragma unroll
-  for (int m = 0; m < RPL; ++m) store_stream(Su + (size_t)(m * 8 + rg) * DV + col, s[m]);
+  for (int m = 0; m < RPL; ++m) store_stream(Su + (size_t)(m * RG + rg) * DV + col, s[m]);
 
   // y = S^T q on the updated state
   float4 out = f4(0.f);
 #pragma unroll
   for (int m = 0; m < RPL; ++m) out = fma4(qr[m], s[m], out);
-  out = tile_allreduce(out);
+  out = tile_sum<CG>(out);
   if (rg == 0) *reinterpret_cast<float4*>(y + (size_t)unit * DV + col) = out;
 }
 
@@ -127,7 +127,8 @@ hipError_t launch_recurrent_step(const ssm_dims& d, float* state, const void* q,
   return dispatch(d.rule, d.in_dtype, d.d_k, d.d_v, [&](auto R, auto DK, auto DV, auto T) {
     using TIN = typename decltype(T)::type;
     constexpr int kR = decltype(R)::value, kDK = decltype(DK)::value, kDV = decltype(DV)::value;
-    hipLaunchKernelGGL((recurrent_step_kernel<kR, kDK, kDV, TIN>), dim3(units), dim3(2 * kDV), 0,
+    hipLaunchKernelGGL((recurrent_step_kernel<kR, kDK, kDV, TIN>), dim3(units),
+                       dim3(TileLayout<kDK, kDV>::NT), 0,
                        stream, state, static_cast<const TIN*>(q), static_cast<const TIN*>(k_t),
                        static_cast<const TIN*>(v_t), decay_t, beta_t, y);
     return hipGetLastError();

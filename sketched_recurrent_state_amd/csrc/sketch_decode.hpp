@@ -15,7 +15,7 @@ namespace ssm {
 namespace {
 
 // ---------------------------------------------------------------------------
-// sketch read: G consecutive lanes per unit (G = 32, or 16 when d_k = 16).
+// sketch read: G consecutive lanes per unit (G = 32, or 16 when d_k or d_v is 16).
 // A workgroup serves 256/G sequences of ONE head, so the head's basis is
 // staged once in LDS for all of them.
 //
@@ -34,8 +34,8 @@ namespace {
 // WMAX >= W bounds the token slots. Scalar gates stay one per lane (lane j of a
 // unit holds slot j's) and are broadcast when the walk reaches that slot.
 // ---------------------------------------------------------------------------
-template <int DK>
-constexpr int sketch_group() { return DK >= 32 ? 32 : 16; }
+template <int DK, int DV>
+constexpr int sketch_group() { return (DK >= 32 && DV >= 32) ? 32 : 16; }
 
 // MAP: `basis` is a per-unit read map [N][H][r][d_k] (least-squares coefficients,
 // row m giving c_m = row . q~), read from memory like the sketch rows, instead of
@@ -53,7 +53,7 @@ __device__ __forceinline__ void sketch_read_block(
     float* dbuf, float* bbuf, float* __restrict__ y, int batch, int heads, int window,
     const RT& rt, const RM& rm, const TSK* __restrict__ sketch_alt,
     const int32_t* __restrict__ parity) {
-  constexpr int G = sketch_group<DK>();
+  constexpr int G = sketch_group<DK, DV>();
   static_assert(WMAX <= G, "one gate per lane");
   constexpr int UPB = 256 / G;                // sequences per workgroup
   constexpr int EK = DK / G, EV = DV / G;
@@ -247,10 +247,11 @@ hipError_t launch_sketch_decode_rule(const ssm_dims& d, const int32_t* rank_offs
   return dispatch_shape(d.in_dtype, d.d_k, d.d_v, [&](auto DK, auto DV, auto T) {
     using TIN = typename decltype(T)::type;
     constexpr int kR = RULE, kDK = decltype(DK)::value, kDV = decltype(DV)::value;
-    constexpr unsigned UPB = 256u / sketch_group<kDK>();
+    constexpr unsigned UPB = 256u / sketch_group<kDK, kDV>();
     const unsigned blocks = (unsigned)d.heads * (((unsigned)d.batch + UPB - 1) / UPB);
     const size_t lds = (size_t)max_rank * kDK * sizeof(float);
-    if (per_unit_map) {  // least squares: fp32 sketch, uniform rank, lockstep (checked)
+    if (per_unit_map) {  // least squares: fp32 sketch, uniform rank, lockstep, d_v >= 32
+      if constexpr (kDV < 32) return hipErrorInvalidValue;  // rejected by the entry point
       auto go_map = [&](auto wmax) {
         constexpr int kW = decltype(wmax)::value;
         hipLaunchKernelGGL(

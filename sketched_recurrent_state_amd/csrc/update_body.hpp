@@ -41,17 +41,21 @@ struct CurrentToken {
   const float* b = nullptr;
 };
 
-// One unit's window update and refresh, the work of one workgroup of 2 * d_v threads:
-// head `head` of slot `seq`, applying its first n buffered tokens.
+// One unit's window update and refresh, the work of one workgroup of
+// TileLayout<DK, DV>::NT threads: head `head` of slot `seq`, applying its first n
+// buffered tokens.
 template <int RULE, int DK, int DV, typename TIN, typename TSK, bool LS, typename RT>
 __device__ __forceinline__ void update_refresh_unit(
     float* __restrict__ state, TSK* __restrict__ sketch, float* __restrict__ rmap,
     const float* __restrict__ basis, const TIN* kbuf, const TIN* vbuf, const float* dbuf,
     const float* bbuf, int heads, int window, const RT& rt, int head, int seq, int n,
     const CurrentToken<TIN>& cur) {
-  constexpr int RPL = DK / 8;          // rows of S per lane
-  constexpr int NT = 2 * DV;           // threads per unit: d_v/32 waves
+  using TL = TileLayout<DK, DV>;
+  constexpr int CG = TL::CG, RG = TL::RG;  // column groups per wave, row groups
+  constexpr int RPL = TL::RPL;             // rows of S per lane
+  constexpr int NT = TL::NT;               // threads per unit: one wave per 4 CG columns
   constexpr int DSTR = (RULE == KDA) ? DK : 1;
+  static_assert(!LS || CG == 8, "the least-squares refresh needs d_v >= 32");
 
   extern __shared__ float4 lds4[];
   float* lds = reinterpret_cast<float*>(lds4);
@@ -60,10 +64,10 @@ __device__ __forceinline__ void update_refresh_unit(
   const int rank = rt.rank(head);
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int cg = lane & 7, rg = lane >> 3;
-  const int col = wave * 32 + cg * 4;
-  // s[m] holds row m * 8 + rg of S; the LDS copies of keys, gates and basis
-  // keep this lane's d_k / 8 values at [row0, row0 + RPL) (interleaved_pos).
+  const int cg = lane % CG, rg = lane / CG;
+  const int col = wave * (4 * CG) + cg * 4;
+  // s[m] holds row m * RG + rg of S; the LDS copies of keys, gates and basis
+  // keep this lane's d_k / RG values at [row0, row0 + RPL) (interleaved_pos).
   const int row0 = rg * RPL;
 
   // 1. issue the staging reads: the window's tokens and the head's basis (each
@@ -73,7 +77,7 @@ __device__ __forceinline__ void update_refresh_unit(
                      const_cast<float*>(dbuf) + slot0 * DSTR,
                      (RULE == MAMBA2) ? nullptr : const_cast<float*>(bbuf) + slot0,
                      cur.k, cur.v, cur.d, cur.b};
-  WindowStage<RULE, DK, DV, TIN, NT, true> stage;
+  WindowStage<RULE, DK, DV, TIN, NT, true, RG> stage;
   if (n > 0) stage.issue(uw, n, tid);
   const float* Bh = basis + (size_t)rt.offset(head) * DK;
   float4 b4 = f4(0.f);
@@ -87,7 +91,7 @@ __device__ __forceinline__ void update_refresh_unit(
   float4 s[RPL];
 #pragma unroll
   for (int m = 0; m < RPL; ++m)
-    s[m] = load_stream(Su + (size_t)(m * 8 + rg) * DV + col);
+    s[m] = load_stream(Su + (size_t)(m * RG + rg) * DV + col);
   // 3. the staged data to LDS as fp32 while the state is in flight
   if (n > 0) stage.commit(lds, uw, n, tid);
   const float* lk = lds;
@@ -99,10 +103,10 @@ __device__ __forceinline__ void update_refresh_unit(
     auto put = [&](float4 x4, int e) {
       float* row = lB + (e - e % DK);
       const int i0 = e % DK;
-      row[interleaved_pos<DK>(i0)] = x4.x;
-      row[interleaved_pos<DK>(i0 + 1)] = x4.y;
-      row[interleaved_pos<DK>(i0 + 2)] = x4.z;
-      row[interleaved_pos<DK>(i0 + 3)] = x4.w;
+      row[interleaved_pos<DK, RG>(i0)] = x4.x;
+      row[interleaved_pos<DK, RG>(i0 + 1)] = x4.y;
+      row[interleaved_pos<DK, RG>(i0 + 2)] = x4.z;
+      row[interleaved_pos<DK, RG>(i0 + 3)] = x4.w;
     };
     if (tid * 4 < rank * DK) put(b4, tid * 4);
     for (int e = (tid + NT) * 4; e < rank * DK; e += NT * 4)
@@ -111,14 +115,15 @@ __device__ __forceinline__ void update_refresh_unit(
   __syncthreads();
 
   // 4. the window's tokens, in order: S <- M_t S + b_t k_t v_t^T on the
-  //    register-resident piece; the k^T S reduction over d_k crosses the 8
+  //    register-resident piece; the k^T S reduction over d_k crosses the RG
   //    lanes that share this lane's columns. Mamba-2 and GDN carry a scaled
   //    copy of the piece so the per-token decay costs nothing (below); KDA
   //    decays rows by different gates and updates S directly.
   // 5. write the state back (the only HBM write of S), then
   // 6. refresh the sketch from the register-resident state: Sk[m] = S^T b_m.
   //    Eight basis rows at a time; the d_k reduction is a reduce-scatter over
-  //    the 8 row groups, after which lane group rg holds basis row m0 + rg.
+  //    lane bits 5, 4 and 3 (after a sum over bit 2 when RG = 16), after which the
+  //    lanes with lane >> 3 = j hold basis row m0 + j.
   // Least-squares refresh, after the rows of Sk are in LDS (lQ). The rows are made
   // orthonormal as Gram-Schmidt would, through the Cholesky factor of their Gram
   // matrix (Sk = L Q with Q orthonormal rows, L lower triangular, G = Sk Sk^T = L L^T):
@@ -287,7 +292,7 @@ __device__ __forceinline__ void update_refresh_unit(
     if (n > 0) {
 #pragma unroll
       for (int m = 0; m < RPL; ++m)
-        store_stream(Su + (size_t)(m * 8 + rg) * DV + col, s[m]);
+        store_stream(Su + (size_t)(m * RG + rg) * DV + col, s[m]);
     }
     if (sketch == nullptr) return;
     TSK* Sku = sketch + ((size_t)seq * rt.total() + rt.offset(head)) * DV;
@@ -302,6 +307,12 @@ __device__ __forceinline__ void update_refresh_unit(
           Vec<float, RPL>::load(lB + (m0 + e) * DK + row0, bm);
 #pragma unroll
           for (int m = 0; m < RPL; ++m) P[e] = fma4(bm[m], s[m], P[e]);
+        }
+        if constexpr (CG == 4) {  // the two row groups that differ in lane bit 2
+          P[e].x += xor4(P[e].x);
+          P[e].y += xor4(P[e].y);
+          P[e].z += xor4(P[e].z);
+          P[e].w += xor4(P[e].w);
         }
       }
 #pragma unroll
@@ -323,11 +334,12 @@ __device__ __forceinline__ void update_refresh_unit(
       res.y = halve8(P[0].y, P[1].y, b3);
       res.z = halve8(P[0].z, P[1].z, b3);
       res.w = halve8(P[0].w, P[1].w, b3);
-      const int m = m0 + rg;
+      const int m = m0 + (lane >> 3);
+      const bool owner = CG == 8 || !(lane & 4);  // lanes l and l ^ 4 hold the same sums
       if constexpr (LS) {
         if (m < rank) *reinterpret_cast<float4*>(lQ + m * DV + col) = res;
       } else {
-        if (m < rank) store4(Sku + (size_t)m * DV + col, res);  // fp32, or bf16 rounded to nearest
+        if (m < rank && owner) store4(Sku + (size_t)m * DV + col, res);  // fp32, or bf16 rounded
       }
     }
     if constexpr (LS) ls_epilogue(Sku);
@@ -347,7 +359,7 @@ __device__ __forceinline__ void update_refresh_unit(
         s[m] = scale4(ar[m], s[m]);  // Diag(alpha) S
         p = fma4(kr[m], s[m], p);
       }
-      p = tile_allreduce(p);
+      p = tile_sum<CG>(p);
       const float4 w = scale4(b, sub4(vv, p));
 #pragma unroll
       for (int m = 0; m < RPL; ++m) s[m] = fma4(kr[m], w, s[m]);
@@ -380,7 +392,7 @@ __device__ __forceinline__ void update_refresh_unit(
         float4 p = f4(0.f);
 #pragma unroll
         for (int m = 0; m < RPL; ++m) p = fma4(kr[m], s[m], p);
-        p = tile_allreduce(p);  // X_{t-1}^T k for this lane's 4 columns
+        p = tile_sum<CG>(p);  // X_{t-1}^T k for this lane's 4 columns
         w = scale4(lb[t], sub4(w, p));
       }
 #pragma unroll

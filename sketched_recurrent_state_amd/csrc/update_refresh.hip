@@ -13,7 +13,7 @@ namespace ssm {
 namespace {
 
 template <int RULE, int DK, int DV, typename TIN, typename TSK, bool LS, typename RT, typename RM>
-__global__ void __launch_bounds__(2 * DV, 4)
+__global__ void __launch_bounds__((TileLayout<DK, DV>::NT), 4)
 update_refresh_kernel(float* __restrict__ state, TSK* __restrict__ sketch,
                       float* __restrict__ rmap,
                       const float* __restrict__ basis, const TIN* __restrict__ kbuf,
@@ -60,20 +60,24 @@ hipError_t launch_update_refresh(const ssm_dims& d, const int32_t* rank_offsets,
   return dispatch(d.rule, d.in_dtype, d.d_k, d.d_v, [&](auto R, auto DK, auto DV, auto T) {
     using TIN = typename decltype(T)::type;
     constexpr int kR = decltype(R)::value, kDK = decltype(DK)::value, kDV = decltype(DV)::value;
-    if (read_map != nullptr) {  // least squares: fp32 sketch, uniform rank, lockstep (checked)
-      hipLaunchKernelGGL(
-          (update_refresh_kernel<kR, kDK, kDV, TIN, float, true, UniformRank, Lockstep>),
-          dim3(units), dim3(2 * kDV), lds, stream, state, static_cast<float*>(sketch), read_map,
-          basis, static_cast<const TIN*>(k_buf), static_cast<const TIN*>(v_buf), decay_buf,
-          beta_buf, d.heads, d.window, UniformRank{d.rank, d.heads}, Lockstep{n});
-      return hipGetLastError();
+    constexpr unsigned NT = TileLayout<kDK, kDV>::NT;
+    if (read_map != nullptr) {  // least squares: fp32 sketch, uniform rank, lockstep, d_v >= 32
+      if constexpr (kDV >= 32) {
+        hipLaunchKernelGGL(
+            (update_refresh_kernel<kR, kDK, kDV, TIN, float, true, UniformRank, Lockstep>),
+            dim3(units), dim3(NT), lds, stream, state, static_cast<float*>(sketch), read_map,
+            basis, static_cast<const TIN*>(k_buf), static_cast<const TIN*>(v_buf), decay_buf,
+            beta_buf, d.heads, d.window, UniformRank{d.rank, d.heads}, Lockstep{n});
+        return hipGetLastError();
+      }
+      return hipErrorInvalidValue;  // rejected by the entry point's checks
     }
     return with_sketch_type(d, [&](auto SK) {
       using TSK = typename decltype(SK)::type;
       auto go = [&](auto rt, auto rm) {
         hipLaunchKernelGGL(
             (update_refresh_kernel<kR, kDK, kDV, TIN, TSK, false, decltype(rt), decltype(rm)>),
-            dim3(units), dim3(2 * kDV), lds, stream, state, static_cast<TSK*>(sketch), nullptr,
+            dim3(units), dim3(NT), lds, stream, state, static_cast<TSK*>(sketch), nullptr,
             basis, static_cast<const TIN*>(k_buf), static_cast<const TIN*>(v_buf), decay_buf,
             beta_buf, d.heads, d.window, rt, rm);
         return hipGetLastError();

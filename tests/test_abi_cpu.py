@@ -63,7 +63,7 @@ def test_null_dims():
 
 @pytest.mark.parametrize("field,value,code", [
     ("rule", 3, 4), ("rule", -1, 4), ("in_dtype", 2, 4),
-    ("batch", -1, 2), ("heads", 0, 2), ("d_k", 48, 2), ("d_k", 256, 2), ("d_v", 16, 2),
+    ("batch", -1, 2), ("heads", 0, 2), ("d_k", 48, 2), ("d_k", 256, 2), ("d_v", 8, 2),
     ("d_v", 256, 2), ("window", 0, 2), ("window", 17, 2), ("rank", 0, 2), ("rank", 33, 2),
     ("sketch_dtype", 2, 4), ("sketch_dtype", -1, 4),
 ])
@@ -380,3 +380,17 @@ def test_decode_step_varlen_validation():
     # an empty batch is a no-op
     d0 = dims(batch=0)
     assert status_of(ssm.decode_step_varlen, d0, P, *([None] * 3), 0, *([None] * 16))[0] == 0
+
+
+def test_least_squares_needs_d_v_32():
+    """d_v = 16 is a supported shape, but not for the least-squares refresh (its read map is
+    summed over the 8 column groups of a 32-column wave)."""
+    p = addrs(10)
+    d = dims(d_v=16)
+    st, msg = status_of(ssm.window_update_refresh_ls, d, *p[:8], 1)
+    assert st == 2 and "d_v >= 32" in msg
+    st, msg = status_of(ssm.sketch_decode_step_ls, d, *p[:7], 1, p[7])
+    assert st == 2 and "d_v >= 32" in msg
+    # the other entry points take d_v = 16: a valid call stops at its NULL state
+    st, msg = status_of(ssm.window_update_refresh, d, None, *p[1:7], 1)
+    assert st == 1 and "state" in msg

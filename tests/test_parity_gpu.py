@@ -62,6 +62,18 @@ MODEL_SHAPES = [
 ]
 SMALL += MODEL_SHAPES
 
+# d_v = 16: one wave per unit with 4 column groups and 16 row groups (the d_k reductions
+# take lane bit 2 as well); every rule, both input types, W from 1 to 16, ranks 1 to 32.
+DV16 = [
+    small("gdn", d_k=128, d_v=16, W=8, r=8),
+    small("kda", d_k=64, d_v=16, W=5, r=16),
+    small("mamba2", "f32", d_k=16, d_v=16, W=3, r=4),
+    small("gdn", "f32", d_k=32, d_v=16, W=16, r=32, T=35),
+    small("kda", d_k=128, d_v=16, W=1, r=1, T=5),
+    small("mamba2", d_k=128, d_v=16, W=4, r=12, N=7, Hh=9),
+]
+SMALL += DV16
+
 
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
 def test_small_all_units(cfg):
@@ -254,7 +266,8 @@ def test_empty_batch_on_device():
 
 RECURRENT = [small("mamba2"), small("gdn"), small("kda"), small("gdn", "f32", d_k=64, d_v=32),
              small("kda", d_k=16, d_v=128), small("mamba2", "f32", d_k=32, d_v=64),
-             small("kda", "f32", d_k=128, d_v=32)]  # d_k staged in two passes of 64 threads
+             small("kda", "f32", d_k=128, d_v=32),   # d_k staged in two passes of 64 threads
+             small("gdn", d_k=128, d_v=16), small("kda", "f32", d_k=32, d_v=16)]
 
 
 @pytest.mark.parametrize("cfg", RECURRENT, ids=lambda c: c.name)
@@ -320,6 +333,12 @@ def _ranked_case(cfg, ranks, steps=None):
 def test_per_head_ranks_small(rule):
     cfg = small(rule, N=3, Hh=5, W=4, T=11)
     H.note(f"case per-head ranks {rule}")
+    _ranked_case(cfg, [1, 8, 3, 16, 32])
+
+
+def test_per_head_ranks_d_v_16():
+    cfg = small("gdn", d_k=64, d_v=16, N=3, Hh=5, W=4, T=11)
+    H.note("case per-head ranks d_v=16")
     _ranked_case(cfg, [1, 8, 3, 16, 32])
 
 
@@ -488,6 +507,7 @@ BF16_SKETCH = [
     small("gdn"), small("kda", W=4, r=8), small("mamba2", d_k=128, d_v=64),
     small("gdn", "f32", d_k=64, d_v=32, W=5, r=3), small("kda", d_k=16, d_v=128, W=1, r=16),
     small("gdn", "bf16", d_k=128, d_v=128, W=16, r=32, N=2, Hh=3, T=33),
+    small("kda", d_k=64, d_v=16, W=4, r=8),
 ]
 
 
@@ -832,9 +852,11 @@ def test_single_launch_step_staggered_workload_sampled():
     H.note(f"single-launch staggered c3: worst sketch-read error {worst:.2e}")
 
 
-@pytest.mark.parametrize("rule", ["mamba2", "gdn", "kda"])
-@pytest.mark.parametrize("sketch_dtype", ["f32", "bf16"])
-def test_single_launch_step_continuous_batching(rule, sketch_dtype):
+@pytest.mark.parametrize("rule,sketch_dtype,d_v", [
+    ("mamba2", "f32", 64), ("gdn", "f32", 64), ("kda", "f32", 64),
+    ("mamba2", "bf16", 64), ("gdn", "bf16", 64), ("kda", "bf16", 64),
+    ("gdn", "f32", 16), ("kda", "bf16", 16)])
+def test_single_launch_step_continuous_batching(rule, sketch_dtype, d_v):
     """ssm_decode_step_varlen with sequences joining at different steps into permuted pool
     slots, reversed row order and a padding row (tau = 0, its output left untouched): every
     sequence against its own oracle run (outputs every step, state and current sketch at the
@@ -846,8 +868,8 @@ def test_single_launch_step_continuous_batching(rule, sketch_dtype):
     joins = [0, 1, 2, 3, 5, 6]
     slots = [5, 0, 7, 2, 3, 6]
     P = 8                                      # pool size
-    cfg = small(rule, d_k=64, d_v=64, W=W, r=8, N=len(joins), Hh=3, T=T)
-    H.note(f"case single-launch step, continuous batching {rule} {sketch_dtype}")
+    cfg = small(rule, d_k=64, d_v=d_v, W=W, r=8, N=len(joins), Hh=3, T=T)
+    H.note(f"case single-launch step, continuous batching {rule} {sketch_dtype} d_v={d_v}")
     Hh, dk, dv = cfg.heads, cfg.d_k, cfg.d_v
     S0 = np.concatenate([workloads.initial_state(cfg, [n]) for n in range(len(joins))])
     B = workloads.basis(cfg)
