@@ -288,6 +288,99 @@ __device__ __forceinline__ void update_refresh_unit(
     for (int e = tid; e < rank * DV; e += NT) Qu[e] = lQ[e];
   };
 
+  // The refresh on the matrix cores (heads of rank above 8), eight basis rows at a time, with
+  // v_mfma_f32_16x16x32_bf16 (A[i][*] from lane i + 16g, B[*][j] from lane j + 16g,
+  // element e of lane group g of A paired with element e of lane group g of B; D[i][j]
+  // in lane j + 16 (i / 4), element i % 4) and fp32 accumulation. Each fp32 value is
+  // split as x = hi + lo + d with hi = bf16(x), lo = bf16(x - hi) and |d| <= 2^-17 |x|;
+  // a product is taken as hi*hi + hi*lo + lo*hi (three passes), so it is off by at
+  // most about 2^-16 of |b| |s|, against the 1e-4 the sketch is held to.
+  //  - B operand: lane l = j + 16g (j = cg + 8 (rg & 1), g = rg >> 1) passes its own
+  //    state values of column c at rows 8m + rg for the 8 m of a block;
+  //  - A operand: the same lane passes b_{m0 + cg} at the same rows.
+  //  An element of D then pairs equal rows only on its diagonal 8 x 8 blocks (i, j < 8:
+  //  the even row groups; i, j >= 8: the odd ones); the other two blocks are not used.
+  //  Lane l < 32 with bit 3 clear adds lane l + 40's odd half (a permlane32 swap, then
+  //  row_ror:8) and holds basis rows m0 + 4 (l >> 4) + e, e = 0..3, at the 4 columns of
+  //  column group l & 7.
+  auto refresh_mfma = [&](TSK* Sku) {
+    typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+    constexpr int MB = (RPL + 7) / 8;  // blocks of 8 rows of this lane (zero-padded)
+    // two floats -> their hi parts packed (one v_cvt_pk_bf16_f32) and lo parts packed
+    auto split2 = [](float a, float b, uint32_t& hp, uint32_t& lp) {
+      hp = pack_bf16x2(a, b);
+      lp = pack_bf16x2(a - bf16_lo(hp), b - bf16_hi(hp));
+    };
+    auto as8 = [](const uint32_t* w) {  // 4 packed words -> 8 bf16 (element 2i in the low half)
+      return __builtin_bit_cast(bf16x8, make_uint4(w[0], w[1], w[2], w[3]));
+    };
+    bf16x8 sh[4][MB], sl[4][MB];      // [column][block]: hi and lo parts of the state
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int m = mb * 8 + 2 * i;
+          const float4 x0 = m < RPL ? s[m] : f4(0.f);
+          const float4 x1 = m + 1 < RPL ? s[m + 1] : f4(0.f);
+          const float a = c == 0 ? x0.x : c == 1 ? x0.y : c == 2 ? x0.z : x0.w;
+          const float b = c == 0 ? x1.x : c == 1 ? x1.y : c == 2 ? x1.z : x1.w;
+          split2(a, b, hw[i], lw[i]);
+        }
+        sh[c][mb] = as8(hw);
+        sl[c][mb] = as8(lw);
+      }
+    }
+    const bool owner = lane < 32 && (lane & 8) == 0;
+    const int ocol = wave * 32 + (lane & 7) * 4;
+    for (int m0 = 0; m0 < rank; m0 += 8) {
+      v4f acc[4] = {};
+      const float* brow = lB + min(m0 + cg, rank - 1) * DK + row0;  // b_{m0 + cg}, this lane's rows
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        float bx[8];
+        if constexpr (RPL >= 8) {
+          Vec<float, 8>::load(brow + mb * 8, bx);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) bx[i] = i < RPL ? brow[i] : 0.f;
+        }
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) split2(bx[2 * i], bx[2 * i + 1], hw[i], lw[i]);
+        const bf16x8 ah = as8(hw), al = as8(lw);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, sh[c][mb], acc[c], 0, 0, 0);
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, sl[c][mb], acc[c], 0, 0, 0);
+          acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, sh[c][mb], acc[c], 0, 0, 0);
+        }
+      }
+      float out[4][4];  // [e][c]: basis row m0 + 4 (lane >> 4) + e, column ocol + c
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float x = acc[c][e];
+          const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x),
+                                                          false, false);  // [1]: lane l | 32
+          out[e][c] = x + dpp<DPP_ROR8>(__uint_as_float(h[1]));
+        }
+      }
+      if (owner) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = m0 + 4 * (lane >> 4) + e;
+          if (m < rank)
+            store4(Sku + (size_t)m * DV + ocol, make_float4(out[e][0], out[e][1], out[e][2],
+                                                            out[e][3]));
+        }
+      }
+    }
+  };
+
   auto finish = [&]() {
     if (n > 0) {
 #pragma unroll
@@ -296,6 +389,15 @@ __device__ __forceinline__ void update_refresh_unit(
     }
     if (sketch == nullptr) return;
     TSK* Sku = sketch + ((size_t)seq * rt.total() + rt.offset(head)) * DV;
+    if constexpr (!LS && CG == 8) {
+      // above rank 8 the fp32 VALU refresh (2 r d_k d_v / NT FMAs per lane) outweighs the
+      // token loop's; there the matrix cores take it (measured: 17% off the GDN update at
+      // r = 32, W = 16; neutral at r = 8, 2% slower at r = 4)
+      if (rank > 8) {
+        refresh_mfma(Sku);
+        return;
+      }
+    }
     const bool b3 = (lane >> 3) & 1;
     for (int m0 = 0; m0 < rank; m0 += 8) {
       float4 P[8];
