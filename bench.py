@@ -40,7 +40,7 @@ sys.path.insert(0, HERE)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 # rocprofv3 FETCH_SIZE / WRITE_SIZE summary of the update + refresh kernel on this workload
 TRAFFIC_FILE = os.path.join(HERE, "profiles", "update_refresh_gdn_n256_h32_128x128_w8_r8.pmc.md")
-KERNEL_SOURCES = ["common.hpp", "update_body.hpp", "update_refresh.hip"]
+KERNEL_SOURCES = ["common.hpp", "update_body.hpp", "update_refresh.hpp"]
 
 
 def kernel_source_hash() -> str:

@@ -20,7 +20,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libsketchssm.so")
-SOURCES = ["abi.hip", "update_refresh.hip", "decode.hip", "sketch_decode_mamba2.hip",
+SOURCES = ["abi.hip", "update_refresh.hip", "update_refresh_mamba2.hip", "update_refresh_gdn.hip",
+           "update_refresh_kda.hip", "decode.hip", "sketch_decode_mamba2.hip",
            "sketch_decode_gdn.hip", "sketch_decode_kda.hip", "decode_step_mamba2.hip",
            "decode_step_gdn.hip", "decode_step_kda.hip", "append.hip", "recurrent.hip",
            "fit_basis.hip", "stream_probe.hip"]

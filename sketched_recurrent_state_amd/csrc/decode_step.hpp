@@ -65,7 +65,7 @@ __device__ __forceinline__ bool block_role(int b, int nr, int nu, int& idx) {
   return read;
 }
 
-template <int RULE, int DK, int DV, typename TIN, typename TSK, int WMAX>
+template <int RULE, int DK, int DV, typename TIN, typename TSK, int WMAX, bool MMA>
 __global__ void __launch_bounds__(256, 4)
 decode_step_varlen_kernel(const DecodeStepArgs<TIN, TSK> a) {
   constexpr int DSTR = (RULE == KDA) ? DK : 1;
@@ -95,7 +95,7 @@ decode_step_varlen_kernel(const DecodeStepArgs<TIN, TSK> a) {
   cur.d = a.d_t + u * DSTR;
   cur.b = (RULE == MAMBA2) ? nullptr : a.b_t + u;
   TSK* next = a.parity[r] != 0 ? a.sketch0 : a.sketch1;  // the buffer the next window reads
-  update_refresh_unit<RULE, DK, DV, TIN, TSK, false, UniformRank>(
+  update_refresh_unit<RULE, DK, DV, TIN, TSK, false, UniformRank, MMA>(
       a.state, next, nullptr, a.basis, a.kbuf, a.vbuf, a.dbuf, a.bbuf, a.heads, a.window, rt,
       head, s, a.window, cur);
 }
@@ -128,11 +128,19 @@ hipError_t launch_decode_step_rule(const ssm_dims& d, int num_slots, const int32
           decay_t, beta_t, static_cast<TIN*>(k_buf), static_cast<TIN*>(v_buf), decay_buf,
           beta_buf, y, slot, tau, parity, update_rows, d.batch, d.heads, d.window, d.rank,
           num_slots, read_blocks, update_blocks};
-      auto go = [&](auto wmax) {
+      auto launch = [&](auto wmax, auto mma) {
         constexpr int kW = decltype(wmax)::value;
-        hipLaunchKernelGGL((decode_step_varlen_kernel<RULE, kDK, kDV, TIN, TSK, kW>),
-                           dim3(read_blocks + update_blocks), dim3(256), lds, stream, a);
+        hipLaunchKernelGGL(
+            (decode_step_varlen_kernel<RULE, kDK, kDV, TIN, TSK, kW, decltype(mma)::value>),
+            dim3(read_blocks + update_blocks), dim3(256), lds, stream, a);
         return hipGetLastError();
+      };
+      // the refresh on the matrix cores above rank 8 (d_k >= 64, d_v >= 32)
+      auto go = [&](auto wmax) {
+        if constexpr (kDK >= 64 && kDV >= 32) {
+          if (d.rank > 8) return launch(wmax, std::true_type{});
+        }
+        return launch(wmax, std::false_type{});
       };
       if (d.window <= 4) return go(std::integral_constant<int, 4>{});
       if (d.window <= 8) return go(std::integral_constant<int, 8>{});

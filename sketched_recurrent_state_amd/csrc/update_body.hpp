@@ -44,7 +44,10 @@ struct CurrentToken {
 // One unit's window update and refresh, the work of one workgroup of
 // TileLayout<DK, DV>::NT threads: head `head` of slot `seq`, applying its first n
 // buffered tokens.
-template <int RULE, int DK, int DV, typename TIN, typename TSK, bool LS, typename RT>
+// MMA: the refresh on the matrix cores (refresh_mfma below), chosen by the host for ranks
+// above 8; else the fp32 VALU reduce-scatter.
+template <int RULE, int DK, int DV, typename TIN, typename TSK, bool LS, typename RT,
+          bool MMA = false>
 __device__ __forceinline__ void update_refresh_unit(
     float* __restrict__ state, TSK* __restrict__ sketch, float* __restrict__ rmap,
     const float* __restrict__ basis, const TIN* kbuf, const TIN* vbuf, const float* dbuf,
@@ -56,6 +59,7 @@ __device__ __forceinline__ void update_refresh_unit(
   constexpr int NT = TL::NT;               // threads per unit: one wave per 4 CG columns
   constexpr int DSTR = (RULE == KDA) ? DK : 1;
   static_assert(!LS || CG == 8, "the least-squares refresh needs d_v >= 32");
+  static_assert(!MMA || (!LS && CG == 8), "the matrix-core refresh: d_v >= 32, no least squares");
 
   extern __shared__ float4 lds4[];
   float* lds = reinterpret_cast<float*>(lds4);
@@ -288,7 +292,10 @@ __device__ __forceinline__ void update_refresh_unit(
     for (int e = tid; e < rank * DV; e += NT) Qu[e] = lQ[e];
   };
 
-  // The refresh on the matrix cores (heads of rank above 8), eight basis rows at a time, with
+  // The refresh on the matrix cores (MMA: chosen for ranks above 8, where the fp32 VALU
+  // refresh, 2 r d_k d_v / NT FMAs per lane, outweighs the token loop: 17% off the GDN
+  // update at r = 32, W = 16; within 1% at r = 8 and 2% slower at r = 4, so not used
+  // there). Eight basis rows at a time, with
   // v_mfma_f32_16x16x32_bf16 (A[i][*] from lane i + 16g, B[*][j] from lane j + 16g,
   // element e of lane group g of A paired with element e of lane group g of B; D[i][j]
   // in lane j + 16 (i / 4), element i % 4) and fp32 accumulation. Each fp32 value is
@@ -389,14 +396,9 @@ __device__ __forceinline__ void update_refresh_unit(
     }
     if (sketch == nullptr) return;
     TSK* Sku = sketch + ((size_t)seq * rt.total() + rt.offset(head)) * DV;
-    if constexpr (!LS && CG == 8) {
-      // above rank 8 the fp32 VALU refresh (2 r d_k d_v / NT FMAs per lane) outweighs the
-      // token loop's; there the matrix cores take it (measured: 17% off the GDN update at
-      // r = 32, W = 16; neutral at r = 8, 2% slower at r = 4)
-      if (rank > 8) {
-        refresh_mfma(Sku);
-        return;
-      }
+    if constexpr (MMA) {
+      refresh_mfma(Sku);
+      return;
     }
     const bool b3 = (lane >> 3) & 1;
     for (int m0 = 0; m0 < rank; m0 += 8) {
