@@ -692,15 +692,16 @@ def main(argv=None) -> int:
     # ---- attainable HBM rate for the state's read + write: the library's in-place stream
     # probe over a buffer of the state's size, in the update's access order (shape 0) and in
     # flat 128 KB runs per workgroup (shape 1, the fastest plain shape measured) -----------
-    n_tiles = (L.S0_dev.numel() * 4 // 65536) & ~1
-    probe = torch.ones(n_tiles * 16384, device=dev)
+    n_tiles = max(2, (L.S0_dev.numel() * 4 // 65536) & ~1)  # at least two tiles (tiny configs)
+    n_small = max(2, int(round(sk_b / 2 / 65536)) & ~1)
+    probe = torch.ones(max(n_tiles, n_small) * 16384, device=dev)
     probe_gbs = []
     for shape in (0, 1):
-        ms = L.kernel_time(lambda i: ssm.stream_probe(probe, n_tiles, shape, stream=sp), 10)
+        ms = L.kernel_time(lambda i: ssm.stream_probe(probe[:n_tiles * 16384], n_tiles, shape,
+                                                      stream=sp), 10)
         probe_gbs.append(2 * n_tiles * 65536 / (ms * 1e-3) / 1e9)
     # and over a buffer whose read + write equals one sketch read's bytes: the ceiling of a
     # single short streaming launch of that size, launch and ramp included
-    n_small = max(2, int(round(sk_b / 2 / 65536)) & ~1)
     small = probe[:n_small * 16384]
     small_ms = L.kernel_time(lambda i: ssm.stream_probe(small, n_small, 1, stream=sp), 20)
     del probe, small

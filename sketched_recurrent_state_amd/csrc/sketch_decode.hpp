@@ -62,9 +62,19 @@ __device__ __forceinline__ void sketch_read_block(
   extern __shared__ float4 lds4[];
   float* lB = reinterpret_cast<float*>(lds4);  // [rank][DK]
 
-  const int head = blk % heads;
+  // Blocks are dealt to the 8 XCDs in turn. With one rank for all heads, block blk
+  // serves head blk % heads, so each head stays on one XCD (its basis in one L2).
+  // With per-head ranks the heads move different byte counts, and a rank pattern
+  // that repeats with a period dividing 8 would load some XCDs far more than
+  // others (ranks 2, 4, 8, 18 cycled over 32 heads put every rank-18 head on two
+  // XCDs); there consecutive blocks take one head's consecutive row blocks, so
+  // every head is spread over all XCDs.
+  constexpr bool kSpread = std::is_same<RT, RankTable>::value;
+  const int nrb = (batch + UPB - 1) / UPB;    // row blocks per head
+  const int head = kSpread ? blk / nrb : blk % heads;
+  const int rblk = kSpread ? blk % nrb : blk / heads;
   const int rank = rt.rank(head);
-  const int row = (blk / heads) * UPB + threadIdx.x / G;  // batch row
+  const int row = rblk * UPB + threadIdx.x / G;  // batch row
   const int sub = threadIdx.x % G;
   const int tid = threadIdx.x;
   int seq = 0, tau = 0;                       // the row's persistent slot and window position
