@@ -135,10 +135,12 @@ hipError_t launch_decode_step_rule(const ssm_dims& d, int num_slots, const int32
             dim3(read_blocks + update_blocks), dim3(256), lds, stream, a);
         return hipGetLastError();
       };
-      // the refresh on the matrix cores above rank 8 (d_k >= 64, d_v >= 32)
+      // the refresh on the matrix cores from rank 8 (d_k >= 64, d_v >= 32), as in the
+      // variable-length update: a step's update blocks fit in one round of workgroups, so
+      // their arithmetic is not hidden behind other workgroups' streams
       auto go = [&](auto wmax) {
         if constexpr (kDK >= 64 && kDV >= 32) {
-          if (d.rank > 8) return launch(wmax, std::true_type{});
+          if (d.rank >= 8) return launch(wmax, std::true_type{});
         }
         return launch(wmax, std::false_type{});
       };

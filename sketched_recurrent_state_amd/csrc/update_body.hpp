@@ -292,10 +292,11 @@ __device__ __forceinline__ void update_refresh_unit(
     for (int e = tid; e < rank * DV; e += NT) Qu[e] = lQ[e];
   };
 
-  // The refresh on the matrix cores (MMA: chosen for ranks above 8, where the fp32 VALU
-  // refresh, 2 r d_k d_v / NT FMAs per lane, outweighs the token loop: 17% off the GDN
-  // update at r = 32, W = 16; within 1% at r = 8 and 2% slower at r = 4, so not used
-  // there). Eight basis rows at a time, with
+  // The refresh on the matrix cores (MMA, chosen by the host: above rank 8, where the fp32
+  // VALU refresh, 2 r d_k d_v / NT FMAs per lane, outweighs the token loop: 17% off the GDN
+  // update at r = 32, W = 16; and from rank 8 in launches whose update blocks fit in one
+  // round of workgroups, where no other workgroup's stream hides the refresh. Not below
+  // rank 8: at r = 4 it is 2% slower). Eight basis rows at a time, with
   // v_mfma_f32_16x16x32_bf16 (A[i][*] from lane i + 16g, B[*][j] from lane j + 16g,
   // element e of lane group g of A paired with element e of lane group g of B; D[i][j]
   // in lane j + 16 (i / 4), element i % 4) and fp32 accumulation. Each fp32 value is

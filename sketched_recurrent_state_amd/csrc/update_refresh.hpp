@@ -75,10 +75,15 @@ hipError_t launch_update_refresh_rule(const ssm_dims& d, const int32_t* rank_off
                            d.window, rt, rm);
         return hipGetLastError();
       };
-      // the refresh on the matrix cores above rank 8 (d_k >= 64, d_v >= 32)
+      // The refresh on the matrix cores (d_k >= 64, d_v >= 32) where its vector time would
+      // show: above rank 8 in every launch, and from rank 8 in the variable-length update,
+      // whose calls in a serving step update a fraction of the units in one round of
+      // workgroups, so every unit's arithmetic is on the critical path (the single-launch
+      // serving step takes the same choice, so the two give the same bits)
+      const int mma_from = varlen != nullptr ? 8 : 9;
       auto go = [&](auto rt, auto rm) {
         if constexpr (kDK >= 64 && kDV >= 32) {
-          if (sketch != nullptr && max_rank > 8) return launch(rt, rm, std::true_type{});
+          if (sketch != nullptr && max_rank >= mma_from) return launch(rt, rm, std::true_type{});
         }
         return launch(rt, rm, std::false_type{});
       };
