@@ -74,6 +74,20 @@ DV16 = [
 ]
 SMALL += DV16
 
+# Windows of 9 to 16 tokens take the matrix-core form of the window update for Mamba-2
+# and GDN (d_k and d_v multiples of 32, at most 16 basis rows): both rules, both input
+# types, d_k and d_v from 32 to 128 (one to four waves per unit), ranks 1 to 16, a last
+# window cut short.
+CHUNK = [
+    small("gdn", W=16, r=8, N=3, Hh=4, T=35),
+    small("mamba2", d_k=128, d_v=64, W=12, r=5, T=27),
+    small("gdn", "f32", d_k=64, d_v=32, W=9, r=16, T=21),
+    small("gdn", d_k=32, d_v=128, W=11, r=13, T=25),
+    small("mamba2", "f32", d_k=64, d_v=128, W=16, r=1, T=35),
+    small("gdn", d_k=128, d_v=32, W=14, r=3, N=5, Hh=3, T=30),
+]
+SMALL += CHUNK
+
 
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
 def test_small_all_units(cfg):
@@ -182,12 +196,13 @@ def test_two_runs_are_bitwise_equal():
     assert torch.equal(a["final_state"], b["final_state"])
 
 
-@pytest.mark.parametrize("rule", ["mamba2", "gdn", "kda"])
-def test_partial_window_flush(rule):
-    """n < W buffered tokens written early: the state equals the recurrence after n tokens."""
-    W, n = 8, 5
+@pytest.mark.parametrize("rule,W,n", [("mamba2", 8, 5), ("gdn", 8, 5), ("kda", 8, 5),
+                                      ("mamba2", 16, 11), ("gdn", 16, 11)])
+def test_partial_window_flush(rule, W, n):
+    """n < W buffered tokens written early: the state equals the recurrence after n tokens
+    (n = 11 of 16: the matrix-core window with five empty token rows)."""
     cfg = small(rule, W=W, T=n)
-    H.note(f"case partial flush {rule}")
+    H.note(f"case partial flush {rule} W={W} n={n}")
     inp = H.Inputs(cfg, np.arange(cfg.units), n)
     d = H.dims_of(cfg)
     state = inp.S0.clone()
@@ -329,6 +344,14 @@ def _ranked_case(cfg, ranks, steps=None):
     H.note(f"ranked {cfg.name} ranks={sorted(set(ranks))}: max sketch-read err {worst:.2e}")
 
 
+@pytest.mark.parametrize("rule", ["mamba2", "gdn"])
+def test_per_head_ranks_matrix_core_window(rule):
+    """Per-head ranks up to 16 with a 16-token window: the matrix-core window update."""
+    cfg = small(rule, N=3, Hh=5, W=16, T=35)
+    H.note(f"case per-head ranks, 16-token window, {rule}")
+    _ranked_case(cfg, [1, 8, 3, 16, 12])
+
+
 @pytest.mark.parametrize("rule", ["mamba2", "gdn", "kda"])
 def test_per_head_ranks_small(rule):
     cfg = small(rule, N=3, Hh=5, W=4, T=11)
@@ -468,12 +491,14 @@ def test_checkpoint_mid_window_and_resume():
     assert torch.equal(a.state, b.state) and torch.equal(a.sketch, b.sketch)
 
 
-@pytest.mark.parametrize("rule", ["mamba2", "gdn", "kda"])
-def test_extreme_gates(rule):
+@pytest.mark.parametrize("rule,W", [("mamba2", 4), ("gdn", 4), ("kda", 4), ("mamba2", 12),
+                                    ("gdn", 12)])
+def test_extreme_gates(rule, W):
     """Exact zero gates (they clear everything before them), gates of 1, beta of 0 and 1,
-    and a large-magnitude state: the suffix-product update and the walk match the oracle."""
-    cfg = small(rule, N=3, Hh=4, W=4, T=12)
-    H.note(f"case extreme gates {rule}")
+    and a large-magnitude state: the suffix-product update (vector form at W = 4, the
+    matrix-core window at W = 12) and the walk match the oracle."""
+    cfg = small(rule, N=3, Hh=4, W=W, T=3 * W)
+    H.note(f"case extreme gates {rule} W={W}")
     inp = H.Inputs(cfg, np.arange(cfg.units), cfg.steps)
     U = cfg.units
     rng = np.random.default_rng(7)
@@ -508,6 +533,7 @@ BF16_SKETCH = [
     small("gdn", "f32", d_k=64, d_v=32, W=5, r=3), small("kda", d_k=16, d_v=128, W=1, r=16),
     small("gdn", "bf16", d_k=128, d_v=128, W=16, r=32, N=2, Hh=3, T=33),
     small("kda", d_k=64, d_v=16, W=4, r=8),
+    small("gdn", W=16, r=8, N=2, Hh=3, T=33), small("mamba2", d_k=64, d_v=64, W=10, r=12),
 ]
 
 
