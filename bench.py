@@ -308,6 +308,26 @@ class Layer:
         graph_s = self.graph_timed(lambda cs: self.run_sketch(st_p, sk_p, warmup, total, cs))
         return graph_s, eager_s, upd_ms, state, sketch
 
+    def update_steady_ms(self, windows: int = 16) -> dict:
+        """HIP-event times of the update + refresh launches of up to `windows` windows of the
+        sketch path run back to back from S0, with no host synchronisation between them;
+        the mean and median over the second half. A launch that starts after the device has
+        been idle, or fed by host launches slower than it runs, can take up to ~20% longer
+        (kernel trace at W = 16: 950 us against 790 us)."""
+        W = self.W
+        n = min(windows, len(self.ptrs) // W)
+        state = self.S0_dev.clone()
+        sketch = self.new_sketch()
+        st_p, sk_p = state.data_ptr(), sketch.data_ptr()
+        self.update_refresh(st_p, sk_p, self.bp, None, None, None, None, 0, stream=self.sp)
+        ev = []
+        self.run_sketch(st_p, sk_p, 0, n * W, self.sp, ev)
+        self.torch.cuda.synchronize()
+        ms = [s_.elapsed_time(e_) for s_, e_ in ev][n // 2:]
+        del state, sketch
+        return {"mean_ms": float(np.mean(ms)), "median_ms": float(np.median(ms)),
+                "launches": len(ms)}
+
     def full_path(self, warmup, total):
         state_f = self.S0_dev.clone()
         sf_p = state_f.data_ptr()
@@ -403,7 +423,10 @@ def sweep_c5(a, torch, ssm, workloads, dev) -> int:
     update + refresh launches (HIP events), and reports the approximation error over T."""
     base = workloads.c5(8, 8)
     T = base.steps
-    steps, warmup = plan_steps(a.steps, a.warmup, max(workloads.C5_WINDOWS))
+    # at least 8 update launches at every point: one launch's time moves by up to ~10% with
+    # what the caches hold when it starts (kernel trace at W = 16: 788 to 936 us)
+    w_max = max(workloads.C5_WINDOWS)
+    steps, warmup = plan_steps(max(a.steps, 8 * w_max), a.warmup, w_max)
     n_steps = max(T, steps + warmup)
     shared = None
     for W in workloads.C5_WINDOWS:
@@ -423,6 +446,8 @@ def sweep_c5(a, torch, ssm, workloads, dev) -> int:
             U = cfg.units
             upd_avg = float(np.mean(upd_ms))
             upd_gbs = bm["update"] * U / (upd_avg * 1e-3) / 1e9
+            steady = L.update_steady_ms()
+            steady_gbs = bm["update"] * U / (steady["mean_ms"] * 1e-3) / 1e9
             tau_mid = W // 2 + 1
             q0 = L.ptrs[0][0]
             state_probe = L.S0_dev.clone()
@@ -446,6 +471,10 @@ def sweep_c5(a, torch, ssm, workloads, dev) -> int:
                 "full_read_steps_per_s": full["steps_per_s"],
                 "speedup_vs_full_read": value / full["steps_per_s"],
                 "update_refresh_ms": upd_avg, "update_refresh_gbs": upd_gbs,
+                "update_refresh_ms_median": float(np.median(upd_ms)),
+                "update_launches": len(upd_ms),
+                "update_refresh_steady": dict(steady, gbs=steady_gbs,
+                                              frac=steady_gbs / HBM_PEAK_GBS),
                 "update_refresh_frac": upd_gbs / HBM_PEAK_GBS,
                 "update_no_refresh_ms": full["update_no_refresh_ms"],
                 "sketch_decode_ms_tau_mid": sk_ms, "full_read_decode_ms_tau_mid": full_ms,

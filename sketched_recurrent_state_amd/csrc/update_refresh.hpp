@@ -11,7 +11,6 @@
 #include "common.hpp"
 #include "launch.hpp"
 #include "update_body.hpp"
-#include "update_chunk.hpp"
 
 namespace ssm {
 
@@ -36,27 +35,6 @@ update_refresh_kernel(float* __restrict__ state, TSK* __restrict__ sketch,
                                                       dbuf, bbuf, heads, window, rt, b % heads,
                                                       seq, n, CurrentToken<TIN>{});
 }
-
-// The window on the matrix cores (update_chunk.hpp): Mamba-2 and GDN, d_k and d_v
-// multiples of 32, up to 16 tokens and 16 basis rows; same block order.
-template <int RULE, int DK, int DV, typename TIN, typename TSK, typename RT>
-__global__ void __launch_bounds__(2 * DV, 4)
-update_refresh_chunk_kernel(float* __restrict__ state, TSK* __restrict__ sketch,
-                            const float* __restrict__ basis, const TIN* __restrict__ kbuf,
-                            const TIN* __restrict__ vbuf, const float* __restrict__ dbuf,
-                            const float* __restrict__ bbuf, int heads, int window, const RT rt,
-                            int n) {
-  const int G = gridDim.x, xcd = blockIdx.x & 7, q8 = G >> 3, rem = G & 7;
-  const int b = xcd * q8 + min(xcd, rem) + (blockIdx.x >> 3);
-  update_refresh_unit_chunk<RULE, DK, DV, TIN, TSK, RT>(state, sketch, basis, kbuf, vbuf, dbuf,
-                                                        bbuf, heads, window, rt, b % heads,
-                                                        b / heads, n, CurrentToken<TIN>{});
-}
-
-// Windows of at least this many tokens take the matrix-core form (Mamba-2, GDN): below
-// it the vector form is bound by HBM, not by its FMAs, and its waves need no barrier
-// after staging.
-constexpr int kChunkFromTokens = 9;
 
 }  // namespace
 
@@ -109,22 +87,7 @@ hipError_t launch_update_refresh_rule(const ssm_dims& d, const int32_t* rank_off
         }
         return launch(rt, rm, std::false_type{});
       };
-      auto chunk = [&](auto rt) {
-        const size_t chunk_lds = chunk_lds_bytes<kDK, kDV>();
-        hipLaunchKernelGGL((update_refresh_chunk_kernel<kR, kDK, kDV, TIN, TSK, decltype(rt)>),
-                           dim3(units), dim3(2 * kDV), chunk_lds, stream,
-                           state, static_cast<TSK*>(sketch), basis,
-                           static_cast<const TIN*>(k_buf), static_cast<const TIN*>(v_buf),
-                           decay_buf, beta_buf, d.heads, d.window, rt, n);
-        return hipGetLastError();
-      };
       if (varlen != nullptr) return go(UniformRank{d.rank, d.heads}, *varlen);
-      if constexpr (kR != KDA && kDK % 32 == 0 && kDV % 32 == 0) {
-        if (n >= kChunkFromTokens && n <= kChunkTokens && max_rank <= kChunkRank) {
-          if (rank_offsets == nullptr) return chunk(UniformRank{d.rank, d.heads});
-          return chunk(make_rank_table(rank_offsets, d.heads));
-        }
-      }
       if (rank_offsets == nullptr) return go(UniformRank{d.rank, d.heads}, Lockstep{n});
       return go(make_rank_table(rank_offsets, d.heads), Lockstep{n});
     });

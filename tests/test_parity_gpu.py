@@ -74,10 +74,9 @@ DV16 = [
 ]
 SMALL += DV16
 
-# Windows of 9 to 16 tokens take the matrix-core form of the window update for Mamba-2
-# and GDN (d_k and d_v multiples of 32, at most 16 basis rows): both rules, both input
-# types, d_k and d_v from 32 to 128 (one to four waves per unit), ranks 1 to 16, a last
-# window cut short.
+# Windows of 9 to 16 tokens for Mamba-2 and GDN (the windows where the update's FMAs, not
+# HBM, come closest to setting its pace): both rules, both input types, d_k and d_v from
+# 32 to 128 (one to four waves per unit), ranks 1 to 16, a last window cut short.
 CHUNK = [
     small("gdn", W=16, r=8, N=3, Hh=4, T=35),
     small("mamba2", d_k=128, d_v=64, W=12, r=5, T=27),
@@ -199,8 +198,7 @@ def test_two_runs_are_bitwise_equal():
 @pytest.mark.parametrize("rule,W,n", [("mamba2", 8, 5), ("gdn", 8, 5), ("kda", 8, 5),
                                       ("mamba2", 16, 11), ("gdn", 16, 11)])
 def test_partial_window_flush(rule, W, n):
-    """n < W buffered tokens written early: the state equals the recurrence after n tokens
-    (n = 11 of 16: the matrix-core window with five empty token rows)."""
+    """n < W buffered tokens written early: the state equals the recurrence after n tokens."""
     cfg = small(rule, W=W, T=n)
     H.note(f"case partial flush {rule} W={W} n={n}")
     inp = H.Inputs(cfg, np.arange(cfg.units), n)
@@ -345,8 +343,8 @@ def _ranked_case(cfg, ranks, steps=None):
 
 
 @pytest.mark.parametrize("rule", ["mamba2", "gdn"])
-def test_per_head_ranks_matrix_core_window(rule):
-    """Per-head ranks up to 16 with a 16-token window: the matrix-core window update."""
+def test_per_head_ranks_window_16(rule):
+    """Per-head ranks up to 16 with a 16-token window."""
     cfg = small(rule, N=3, Hh=5, W=16, T=35)
     H.note(f"case per-head ranks, 16-token window, {rule}")
     _ranked_case(cfg, [1, 8, 3, 16, 12])
@@ -495,8 +493,8 @@ def test_checkpoint_mid_window_and_resume():
                                     ("gdn", 12)])
 def test_extreme_gates(rule, W):
     """Exact zero gates (they clear everything before them), gates of 1, beta of 0 and 1,
-    and a large-magnitude state: the suffix-product update (vector form at W = 4, the
-    matrix-core window at W = 12) and the walk match the oracle."""
+    and a large-magnitude state: the suffix-product update and the walk match the oracle,
+    at W = 4 and W = 12."""
     cfg = small(rule, N=3, Hh=4, W=W, T=3 * W)
     H.note(f"case extreme gates {rule} W={W}")
     inp = H.Inputs(cfg, np.arange(cfg.units), cfg.steps)
