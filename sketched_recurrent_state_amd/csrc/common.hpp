@@ -377,6 +377,11 @@ constexpr int kMaxRankedHeads = 256;
 struct RankTable {  // per-head ranks: off[h + 1] - off[h], off[0] = 0 (checked on the host)
   int heads;
   int off[kMaxRankedHeads + 1];
+  // The heads by rank, largest first (ties by index): the order in which the sketch read
+  // deals its blocks out, so that each round of resident workgroups holds one rank class
+  // and every compute unit receives a mix of ranks (heads of equal rank on one unit would
+  // make it the slowest).
+  uint8_t order[kMaxRankedHeads];
   __device__ __forceinline__ int rank(int h) const { return off[h + 1] - off[h]; }
   __device__ __forceinline__ int offset(int h) const { return off[h]; }
   __device__ __forceinline__ int total() const { return off[heads]; }

@@ -16,6 +16,16 @@ inline RankTable make_rank_table(const int32_t* rank_offsets, int heads) {
   RankTable t;
   t.heads = heads;
   for (int h = 0; h <= heads; ++h) t.off[h] = rank_offsets[h];
+  // heads by rank, largest first, ties by index (a stable insertion sort; heads <= 256)
+  for (int h = 0; h < heads; ++h) {
+    const int r = t.off[h + 1] - t.off[h];
+    int i = h;
+    while (i > 0 && t.off[t.order[i - 1] + 1] - t.off[t.order[i - 1]] < r) {
+      t.order[i] = t.order[i - 1];
+      --i;
+    }
+    t.order[i] = (uint8_t)h;
+  }
   return t;
 }
 

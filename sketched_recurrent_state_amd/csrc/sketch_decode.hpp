@@ -68,10 +68,15 @@ __device__ __forceinline__ void sketch_read_block(
   // that repeats with a period dividing 8 would load some XCDs far more than
   // others (ranks 2, 4, 8, 18 cycled over 32 heads put every rank-18 head on two
   // XCDs); there consecutive blocks take one head's consecutive row blocks, so
-  // every head is spread over all XCDs.
+  // every head is spread over all XCDs, and the heads come largest rank first
+  // (rt.order): the blocks resident together in one round then share a rank, and
+  // each compute unit takes one block of each round. In head order, ranks 2, 4, 8,
+  // 18 cycled over 32 heads gave every unit four blocks of one rank, and the units
+  // holding rank 18 set the launch's time (14.9 against 13.2 us at N = 256).
   constexpr bool kSpread = std::is_same<RT, RankTable>::value;
   const int nrb = (batch + UPB - 1) / UPB;    // row blocks per head
-  const int head = kSpread ? blk / nrb : blk % heads;
+  int head = blk % heads;
+  if constexpr (kSpread) head = rt.order[blk / nrb];
   const int rblk = kSpread ? blk % nrb : blk / heads;
   const int rank = rt.rank(head);
   const int row = rblk * UPB + threadIdx.x / G;  // batch row
