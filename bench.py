@@ -436,6 +436,14 @@ def sweep_c5(a, torch, ssm, workloads, dev) -> int:
             if shared is None:
                 L = Layer(cfg, n_steps, dev, torch, ssm, workloads)
                 shared = dict(S0=L.S0_dev, steps_host=L.steps_host, inputs=L.inputs)
+                # the per-token decode (every step writes and reads the full state) does not
+                # depend on r or W: timed once, on the same tokens, as the points' comparator
+                state_r = L.S0_dev.clone()
+                sr_p = state_r.data_ptr()
+                L.run_rec(sr_p, 0, warmup, L.sp)
+                per_token_sps = steps / L.graph_timed(lambda cs: L.run_rec(sr_p, warmup,
+                                                                           warmup + steps, cs))
+                del state_r
             else:
                 L = Layer(cfg, n_steps, dev, torch, ssm, workloads, **shared)
             total = warmup + steps
@@ -470,6 +478,8 @@ def sweep_c5(a, torch, ssm, workloads, dev) -> int:
                 "eager_steps_per_s": steps / eager_s,
                 "full_read_steps_per_s": full["steps_per_s"],
                 "speedup_vs_full_read": value / full["steps_per_s"],
+                "per_token_steps_per_s": per_token_sps,
+                "speedup_vs_per_token": value / per_token_sps,
                 "update_refresh_ms": upd_avg, "update_refresh_gbs": upd_gbs,
                 "update_refresh_ms_median": float(np.median(upd_ms)),
                 "update_launches": len(upd_ms),
