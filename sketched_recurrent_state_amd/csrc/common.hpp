@@ -243,6 +243,16 @@ __device__ __forceinline__ double readlane_f64(double x, int k) {
   return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
+// 1 / sqrt(d) for d > 0: the hardware estimate (v_rsq_f64) and two Newton steps
+// y <- y (3 - d y^2) / 2, each of which doubles the correct bits.
+__device__ __forceinline__ double rsqrt_f64(double d) {
+  double y = __builtin_amdgcn_rsq(d);
+  const double h = 0.5 * d;
+  y = y * fma(-h, y * y, 1.5);
+  y = y * fma(-h, y * y, 1.5);
+  return y;
+}
+
 // The value of lane l ^ 4: reversing each 8 lanes (p -> 7 - p) and then each 4
 // (p -> 3 - p) maps position p to p ^ 4.
 __device__ __forceinline__ float xor4(float x) {

@@ -131,13 +131,17 @@ __device__ __forceinline__ void update_refresh_unit(
   // Least-squares refresh, after the rows of Sk are in LDS (lQ). The rows are made
   // orthonormal as Gram-Schmidt would, through the Cholesky factor of their Gram
   // matrix (Sk = L Q with Q orthonormal rows, L lower triangular, G = Sk Sk^T = L L^T):
-  //   a. G in fp64 (products of fp32 values are exact there), four lanes per entry;
-  //   b. wave 0 factors G = L L^T column by column, lane i owning row i; a row whose
-  //      pivot, its squared residual against the rows before it, is below
-  //      kLsRelTol^2 of the largest squared row norm is dropped (zero column of L);
+  //   a. the lower triangle of G in fp64 (products of fp32 values are exact there),
+  //      four lanes per entry, each over d_v / 4 columns in 16-byte reads;
+  //   b. one wave (it rotates with the unit, so no SIMD takes every unit's share)
+  //      factors G = L L^T column by column, lane i owning row i; a row whose pivot,
+  //      its squared residual against the rows before it, is below kLsRelTol^2 of the
+  //      largest squared row norm is dropped (zero column of L). The inverse pivot is
+  //      the reciprocal square root of the pivot (v_rsq_f64 and two Newton steps);
   //   c. step b also forms L^-1 (fp64, in place of L, the inverse pivots on the
   //      diagonal; a dropped row is zero), then Q = L^-1 Sk in place, one column of
-  //      the sketch per thread, each row from the exact fp32 sketch;
+  //      the sketch per thread (the threads rotate with the unit as in b), each row
+  //      from the exact fp32 sketch;
   //   d. every wave forms Y = Q S^T over its 32 columns: per row of S a dot product
   //      of 4 columns, summed over the 8 lanes of the row group (lane bits 0..2) as a
   //      reduce-scatter over four rows of Q at a time;
@@ -145,28 +149,43 @@ __device__ __forceinline__ void update_refresh_unit(
   float* lQ = lB + rank * DK;  // [rank][DV] (LS only)
   float* lP = lQ + rank * DV;  // [DV / 32][rank][DK] per-wave partial Y (LS only)
   double* lG = reinterpret_cast<double*>(lP + (DV / 32) * rank * DK);  // [rank][rank] (LS only)
+  const int ls_turn = (int)(unit % (NT / 64));  // the wave (and threads) of steps b and c
   auto ls_epilogue = [&](float* Qu) {
     __syncthreads();
-    for (int e0 = 0; e0 < rank * rank; e0 += NT / 4) {  // a. Gram matrix, lower triangle
+    // a. Gram matrix, lower triangle: entry (i, j), j <= i, is number i (i + 1) / 2 + j
+    const int ntri = rank * (rank + 1) / 2;
+    for (int e0 = 0; e0 < ntri; e0 += NT / 4) {
       const int e = e0 + tid / 4, part = tid & 3;
-      double g = 0.0;
-      if (e < rank * rank) {
-        const float* ri = lQ + (e / rank) * DV;
-        const float* rj = lQ + (e % rank) * DV;
-        // the rows all start on the same LDS bank: each entry walks the columns from its own
-        // offset, so the lanes of a wave read different banks
-        const int rot = 8 * (e % rank) + 32 * ((e / rank) & 1);
-        for (int c = part; c < DV; c += 4) {
-          const int cc = (c + rot) & (DV - 1);
-          g = fma((double)ri[cc], (double)rj[cc], g);
+      int i = 0, j = 0;
+      double g0 = 0.0, g1 = 0.0;
+      if (e < ntri) {
+        i = (int)((__builtin_sqrtf(8.f * (float)e + 1.f) - 1.f) * 0.5f);
+        if ((i + 1) * (i + 2) / 2 <= e) ++i;  // the float root rounded down past a square
+        if (i * (i + 1) / 2 > e) --i;
+        j = e - i * (i + 1) / 2;
+        const float* ri = lQ + i * DV;
+        const float* rj = lQ + j * DV;
+        // the rows all start on the same LDS bank: the entries of a wave walk the columns
+        // from different offsets, so their lanes read different banks
+        const int rot = 16 * ((tid >> 2) & 7);
+#pragma unroll
+        for (int c = 0; c < DV; c += 16) {
+          const int cc = (c + 4 * part + rot) & (DV - 1);
+          const float4 a = *reinterpret_cast<const float4*>(ri + cc);
+          const float4 b = *reinterpret_cast<const float4*>(rj + cc);
+          g0 = fma((double)a.x, (double)b.x, g0);
+          g1 = fma((double)a.y, (double)b.y, g1);
+          g0 = fma((double)a.z, (double)b.z, g0);
+          g1 = fma((double)a.w, (double)b.w, g1);
         }
       }
+      double g = g0 + g1;
       g += __shfl_xor(g, 1);
       g += __shfl_xor(g, 2);
-      if (e < rank * rank && part == 0 && e % rank <= e / rank) lG[e] = g;
+      if (e < ntri && part == 0) lG[i * rank + j] = g;
     }
     __syncthreads();
-    if (wave == 0) {  // b. Cholesky, left-looking
+    if (wave == ls_turn) {  // b. Cholesky, left-looking
       double maxd = 0.0;
       for (int i = 0; i < rank; ++i) maxd = fmax(maxd, lG[i * rank + i]);
       const double thr = (double)kLsRelTol * (double)kLsRelTol * maxd;
@@ -174,10 +193,11 @@ __device__ __forceinline__ void update_refresh_unit(
       if (rank <= 8) {
         // In registers: lane i holds row i of G, then of L; row k of L comes from lane k
         // by readlane, so the factorisation makes no LDS round trip (entries above the
-        // diagonal are scratch). Only L^-1 goes back to LDS.
+        // diagonal are scratch, zero at the start). Only L^-1 goes back to LDS.
         double g[8];
 #pragma unroll
-        for (int p = 0; p < 8; ++p) g[p] = lG[min(i, rank - 1) * rank + min(p, rank - 1)];
+        for (int p = 0; p < 8; ++p)
+          g[p] = (i < rank && p <= i) ? lG[i * rank + p] : 0.0;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           if (k < rank) {
@@ -185,8 +205,7 @@ __device__ __forceinline__ void update_refresh_unit(
 #pragma unroll
             for (int p = 0; p < k; ++p) d = fma(-g[p], g[p], d);
             d = readlane_f64(d, k);
-            const double lkk = d > thr ? sqrt(d) : 0.0;
-            const double inv = lkk > 0.0 ? 1.0 / lkk : 0.0;
+            const double inv = d > thr ? rsqrt_f64(d) : 0.0;
             double x = g[k];
 #pragma unroll
             for (int p = 0; p < k; ++p) x = fma(-g[p], readlane_f64(g[p], k), x);
@@ -214,15 +233,15 @@ __device__ __forceinline__ void update_refresh_unit(
           // every lane reads row k (and its own row) before lanes i >= k write column k
           double dk = lG[k * rank + k];
           for (int p = 0; p < k; ++p) dk = fma(-lG[k * rank + p], lG[k * rank + p], dk);
-          const double lkk = dk > thr ? sqrt(dk) : 0.0;
+          const double inv = dk > thr ? rsqrt_f64(dk) : 0.0;
           double x = 0.0;
-          if (i > k && i < rank && lkk > 0.0) {
+          if (i > k && i < rank && inv > 0.0) {
             x = lG[i * rank + k];
             for (int p = 0; p < k; ++p) x = fma(-lG[i * rank + p], lG[k * rank + p], x);
-            x /= lkk;
+            x *= inv;
           }
           if (i > k && i < rank) lG[i * rank + k] = x;
-          if (i == k) lG[k * rank + k] = lkk > 0.0 ? 1.0 / lkk : 0.0;  // kept: the inverse pivot
+          if (i == k) lG[k * rank + k] = inv;  // kept: the inverse pivot
         }
         // L^-1 by columns into the upper triangle (L^-1[r][j] at row j, column r), lane j
         // taking column j; L^-1[k][j] for k >= j is then lG[j][k], the diagonal included.
@@ -238,14 +257,31 @@ __device__ __forceinline__ void update_refresh_unit(
       }
     }
     __syncthreads();
-    // c. Q = L^-1 Sk, one column per thread, last row first so that row m still reads the
-    //    sketch rows p <= m it needs (in place); each row is formed in fp64 from the exact
-    //    sketch values, with no rounded row of Q feeding the next
-    for (int c = tid; c < DV; c += NT) {
-      for (int m = rank - 1; m >= 0; --m) {
-        double x = 0.0;
-        for (int p = 0; p <= m; ++p) x = fma(lG[m * rank + p], (double)lQ[p * DV + c], x);
-        lQ[m * DV + c] = (float)x;  // zero for a dropped row
+    // c. Q = L^-1 Sk in place, one column per thread: up to rank 8 the column is read into
+    //    registers first; above, the rows go last first, so that row m still reads the
+    //    sketch rows p <= m it needs. Each row is formed in fp64 from the exact sketch
+    //    values, with no rounded row of Q feeding the next.
+    const int c = (tid + DV * ls_turn) % NT;  // DV divides NT
+    if (c < DV) {
+      if (rank <= 8) {  // the column in registers first, then every row from it
+        double x[8];
+#pragma unroll
+        for (int p = 0; p < 8; ++p) x[p] = p < rank ? (double)lQ[p * DV + c] : 0.0;
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          if (m < rank) {
+            double q = 0.0;
+#pragma unroll
+            for (int p = 0; p <= m; ++p) q = fma(lG[m * rank + p], x[p], q);
+            lQ[m * DV + c] = (float)q;  // zero for a dropped row
+          }
+        }
+      } else {
+        for (int m = rank - 1; m >= 0; --m) {
+          double q = 0.0;
+          for (int p = 0; p <= m; ++p) q = fma(lG[m * rank + p], (double)lQ[p * DV + c], q);
+          lQ[m * DV + c] = (float)q;  // zero for a dropped row
+        }
       }
     }
     __syncthreads();
