@@ -357,6 +357,16 @@ def test_per_head_ranks_small(rule):
     _ranked_case(cfg, [1, 8, 3, 16, 32])
 
 
+@pytest.mark.parametrize("rule", ["mamba2", "gdn", "kda"])
+def test_per_head_ranks_above_eight(rule):
+    """Odd and even ranks above the eight sketch rows fetched with the step's other loads
+    (9, 16, 17, 25: further fetches of one to eight live rows), beside ranks of 8 and below in
+    the same launch, over 5 rows (a ragged workgroup)."""
+    cfg = small(rule, N=5, Hh=6, W=8, T=19)
+    H.note(f"case per-head ranks above 8, {rule}")
+    _ranked_case(cfg, [9, 17, 2, 25, 8, 16])
+
+
 def test_per_head_ranks_d_v_16():
     cfg = small("gdn", d_k=64, d_v=16, N=3, Hh=5, W=4, T=11)
     H.note("case per-head ranks d_v=16")
