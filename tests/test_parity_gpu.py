@@ -50,14 +50,16 @@ SMALL = [
 ]
 
 
-# More Mamba-2 and GDN shapes at the model sizes (d_k, d_v in {64, 128}): odd windows,
-# W = 1 and 16, ranks from 1 to 30, both input types.
+# More shapes at the model sizes (d_k, d_v in {64, 128}): odd windows, W = 1 and 16, ranks
+# from 1 to 30, both input types.
 MODEL_SHAPES = [
     small("gdn", d_k=64, d_v=128, W=6, r=5),
     small("mamba2", d_k=64, d_v=64, W=7, r=12),
     small("gdn", "f32", d_k=128, d_v=64, W=3, r=2),
     small("mamba2", d_k=128, d_v=128, W=16, r=16, T=37),
     small("gdn", d_k=64, d_v=64, W=1, r=1, T=5),
+    # a basis of 1,536 floats: a second 1,024-float LDS chunk, half of it a clamped tail
+    small("kda", d_k=64, d_v=128, W=8, r=24, T=19),
     small("gdn", "f32", d_k=128, d_v=128, W=13, r=30, N=2, Hh=3, T=29),
 ]
 SMALL += MODEL_SHAPES
