@@ -44,6 +44,9 @@ SMALL = [
     small("gdn", "f32", d_k=64, d_v=64, W=4, r=16), small("kda", "f32", d_k=128, d_v=32, W=6, r=8),
     small("mamba2", "f32", d_k=16, d_v=64, W=3, r=16),
     small("gdn", N=7, Hh=9, W=8, r=8),   # 63 units: a ragged last wave of the sketch read
+    # 32 x 32 (one wave per unit): every rule, r = d_k = 32 included (a full basis)
+    small("gdn", d_k=32, d_v=32, W=7, r=5), small("mamba2", d_k=32, d_v=32, W=2, r=1),
+    small("kda", "f32", d_k=32, d_v=32, W=12, r=32, T=27),
     # the largest supported shapes: LDS and registers at their maximum
     small("kda", "f32", d_k=128, d_v=128, W=16, r=32, N=2, Hh=3, T=35),
     small("gdn", "bf16", d_k=128, d_v=128, W=16, r=32, N=2, Hh=3, T=33),
