@@ -296,7 +296,7 @@ def test_recurrent_step_small(cfg):
     H.compare_recurrent(cfg, H.run_gpu_recurrent(cfg, inp), inp)
 
 
-@pytest.mark.parametrize("name", ["c3", "c4"])
+@pytest.mark.parametrize("name", ["c2", "c3", "c4"])
 def test_recurrent_step_workload_sampled(name):
     cfg = workloads.get(name).with_(steps=24)
     H.note(f"case recurrent {name} (sampled units, 24 steps)")
