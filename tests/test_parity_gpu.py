@@ -174,17 +174,18 @@ def test_full_read_fused_append(rule):
     H.assert_mats(a["S"], ref["S_win"][:a["S"].shape[0]], H.S_TOL, "state")
 
 
-def test_full_read_workload_sampled():
-    """The exact full-read path at the GDN workload's size (N=256, H=32, 128x128, W=8), with
-    the fused append, in the launch configuration the bench's comparison leg times; 40
-    sampled units, every step and window."""
-    cfg = workloads.C3
-    H.note("case full read c3 (sampled units)")
+@pytest.mark.parametrize("name", ["c2", "c3", "c4"])
+def test_full_read_workload_sampled(name):
+    """The exact full-read path at a workload's size (C3: the GDN layer, N=256, H=32, 128x128,
+    W=8), with the fused append, in the launch configuration the bench's comparison leg times;
+    40 sampled units, every step and window."""
+    cfg = workloads.get(name)
+    H.note(f"case full read {name} (sampled units)")
     inp = H.Inputs(cfg, workloads.sample_units(cfg, 40), cfg.steps)
     got = H.run_gpu_full(cfg, inp, fused=True)
     ref = H.run_oracle(cfg, inp)
     e = H.rel_rows(got["y"], ref["y_exact"])
-    H.note(f"full read c3: y {e.max():.2e}")
+    H.note(f"full read {name}: y {e.max():.2e}")
     assert e.max() <= H.Y_TOL
     H.assert_mats(got["S"], ref["S_win"], H.S_TOL, "state")
 
