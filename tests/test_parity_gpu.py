@@ -562,11 +562,12 @@ def test_bf16_sketch(cfg):
     assert got["sketch"].dtype == torch.bfloat16
 
 
-def test_bf16_sketch_workload_sampled():
-    """The GDN workload at full size with the bf16 sketch, as bench.py times it; 40 sampled
-    units, every step and window."""
-    cfg = workloads.C3
-    H.note("case bf16 sketch c3 (sampled units)")
+@pytest.mark.parametrize("name", ["c2", "c3", "c4"])
+def test_bf16_sketch_workload_sampled(name):
+    """A workload at full size with the bf16 sketch, as bench.py times it; 40 sampled units,
+    every step and window."""
+    cfg = workloads.get(name)
+    H.note(f"case bf16 sketch {name} (sampled units)")
     inp = H.Inputs(cfg, workloads.sample_units(cfg, 40), cfg.steps)
     got = H.run_gpu(cfg, inp, sketch_dtype="bf16")
     ref = H.run_oracle(cfg, inp, sketch_bf16=True, want_ls=True)  # want_ls: q~ for the slack
@@ -624,11 +625,12 @@ def test_least_squares_coefficients(cfg):
     check_least_squares(cfg, got, ref)
 
 
-def test_least_squares_workload_sampled():
-    """The GDN workload at full size (N=256, H=32, 128x128, W=8, r=8) with least-squares
+@pytest.mark.parametrize("name", ["c2", "c3", "c4"])
+def test_least_squares_workload_sampled(name):
+    """A workload at full size (C3: N=256, H=32, 128x128, W=8, r=8) with least-squares
     coefficients, as bench.py times it; 40 sampled units, every step and window."""
-    cfg = workloads.C3
-    H.note("case least squares c3 (sampled units)")
+    cfg = workloads.get(name)
+    H.note(f"case least squares {name} (sampled units)")
     inp = H.Inputs(cfg, workloads.sample_units(cfg, 40), cfg.steps)
     got = H.run_gpu(cfg, inp, coefficients="least_squares")
     ref = H.run_oracle(cfg, inp, want_ls=True)
