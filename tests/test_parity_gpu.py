@@ -379,10 +379,11 @@ def test_per_head_ranks_d_v_16():
     _ranked_case(cfg, [1, 8, 3, 16, 32])
 
 
-def test_per_head_ranks_average_8_workload():
-    """The GDN workload with a mean-8 rank pattern (2, 4, 8, 18 cycled over heads)."""
-    cfg = workloads.C3.with_(steps=24)
-    H.note("case per-head ranks c3 (sampled units)")
+@pytest.mark.parametrize("name", ["c2", "c3", "c4"])
+def test_per_head_ranks_average_8_workload(name):
+    """A workload at full size with a mean-8 rank pattern (2, 4, 8, 18 cycled over heads)."""
+    cfg = workloads.get(name).with_(steps=24)
+    H.note(f"case per-head ranks {name} (sampled units)")
     _ranked_case(cfg, workloads.average_rank_8(cfg.heads))
 
 
