@@ -774,10 +774,11 @@ def _staggered_run(cfg, T, units, single_launch: bool):
     basis = H._to_dev(B, dev)
     d = H.dims_of(cfg)
     sketch = [torch.empty((N, Hh, cfg.rank, dv), device=dev) for _ in range(2)]
-    kb = torch.zeros((N, Hh, W, dk), device=dev, dtype=torch.bfloat16)
-    vb = torch.zeros((N, Hh, W, dv), device=dev, dtype=torch.bfloat16)
-    db = torch.zeros((N, Hh, W), device=dev)
-    bb = torch.zeros((N, Hh, W), device=dev)
+    tin = torch.bfloat16 if cfg.in_dtype == "bf16" else torch.float32
+    kb = torch.zeros((N, Hh, W, dk), device=dev, dtype=tin)
+    vb = torch.zeros((N, Hh, W, dv), device=dev, dtype=tin)
+    db = torch.zeros(workloads.decay_shape(cfg, (N, Hh, W)), device=dev)
+    bb = torch.zeros((N, Hh, W), device=dev) if cfg.has_beta else None
     ssm.window_update_refresh(d, state, sketch[0], basis, None, None, None, None, 0)
     idx = torch.as_tensor(units, device=dev)
     sentinel = 777.0
@@ -787,7 +788,9 @@ def _staggered_run(cfg, T, units, single_launch: bool):
 
     def mix(field, t):
         """Global step t's input: row n from sequence n's local step t - join[n] (zeros
-        before it joins)."""
+        before it joins); None for a field the rule does not have."""
+        if getattr(local[0], field) is None:
+            return None
         out = np.zeros_like(getattr(local[0], field))
         for s in range(W):
             live = (join == s) & (t >= s)
@@ -799,7 +802,8 @@ def _staggered_run(cfg, T, units, single_launch: bool):
         tau = np.where(t >= join, (t - join) % W + 1, 0).astype(np.int32)
         parity = np.where(t >= join, ((t - join) // W) % 2, 0).astype(np.int32)
         y.fill_(sentinel)
-        td = lambda f: H._to_dev(np.ascontiguousarray(mix(f, t)), dev)
+        td = lambda f: None if mix(f, t) is None else H._to_dev(np.ascontiguousarray(mix(f, t)),
+                                                               dev)
         ups = rows[tau == W].astype(np.int32)
         if single_launch:
             ssm.decode_step_varlen(d, N, None, H._to_dev(tau, dev), H._to_dev(parity, dev),
@@ -848,8 +852,8 @@ def _staggered_check(cfg, T, units, got, S_end, K_end, S0, B, local, join):
         ref = oracle.run(cfg.rule, S0.reshape(N * Hh, dk, dv)[us].astype(np.float64),
                          B[us % Hh].astype(np.float64), workloads.widen(pick("q", dk)),
                          workloads.widen(pick("k", dk)), workloads.widen(pick("v", dv)),
-                         pick("decay", 0).astype(np.float64), pick("beta", 0).astype(np.float64),
-                         W)
+                         pick("decay", dk if cfg.per_channel_decay else 0).astype(np.float64),
+                         pick("beta", 0).astype(np.float64) if cfg.has_beta else None, W)
         g = np.stack([np.stack(got[int(u)]) for u in us], axis=1)    # [Tn][U][dv]
         e = H.rel_rows(g, ref["y_sketch"])
         worst = max(worst, float(e.max()))
@@ -860,31 +864,33 @@ def _staggered_check(cfg, T, units, got, S_end, K_end, S0, B, local, join):
     return worst
 
 
-def test_staggered_windows_workload_sampled():
-    """The GDN workload at full size (N=256, H=32, 128x128, W=8, r=8) on the staggered schedule
+@pytest.mark.parametrize("name", ["c2", "c3", "c4"])
+def test_staggered_windows_workload_sampled(name):
+    """A workload at full size (C3: N=256, H=32, 128x128, W=8, r=8) on the staggered schedule
     bench.py times: sequence n joins at step n mod W, so from step W - 1 on every step reads
     all rows at their own window positions (one varlen read, identity slots) and updates the
     N/W rows whose window just filled (one varlen update). Rows that have not joined are
     padding (tau = 0) and keep their output. 40 sampled units are checked against the oracle
     over their local steps: every output, and the final state and sketch."""
-    cfg = workloads.C3
+    cfg = workloads.get(name)
     T = 64 + cfg.window - 1                      # the last joiner still runs 64 local steps
-    H.note("case staggered windows c3 (sampled units)")
+    H.note(f"case staggered windows {name} (sampled units)")
     units = workloads.sample_units(cfg, 40)
     res = _staggered_run(cfg, T, units, single_launch=False)
     worst = _staggered_check(cfg, T, units, *res)
-    H.note(f"staggered c3: worst sketch-read error {worst:.2e}")
+    H.note(f"staggered {name}: worst sketch-read error {worst:.2e}")
 
 
-def test_single_launch_step_staggered_workload_sampled():
+@pytest.mark.parametrize("name", ["c2", "c3", "c4"])
+def test_single_launch_step_staggered_workload_sampled(name):
     """The same staggered schedule through ssm_decode_step_varlen, one launch per step (the
     read of every row, the update of the rows whose window fills, a double-buffered sketch
     chosen per row by parity), as bench.py times it: against the oracle, and bit for bit
     equal to the two-launch schedule (same arithmetic; the update takes the window's newest
     token from the step's inputs instead of the buffer, the same bits)."""
-    cfg = workloads.C3
+    cfg = workloads.get(name)
     T = 64 + cfg.window - 1
-    H.note("case single-launch staggered step c3 (sampled units)")
+    H.note(f"case single-launch staggered step {name} (sampled units)")
     units = workloads.sample_units(cfg, 40)
     one = _staggered_run(cfg, T, units, single_launch=True)
     worst = _staggered_check(cfg, T, units, *one)
@@ -892,7 +898,7 @@ def test_single_launch_step_staggered_workload_sampled():
     for u in units:
         assert np.array_equal(np.stack(one[0][int(u)]), np.stack(two[0][int(u)])), f"unit {u}"
     assert np.array_equal(one[1], two[1]) and np.array_equal(one[2], two[2])
-    H.note(f"single-launch staggered c3: worst sketch-read error {worst:.2e}")
+    H.note(f"single-launch staggered {name}: worst sketch-read error {worst:.2e}")
 
 
 @pytest.mark.parametrize("rule,sketch_dtype,d_v", [
