@@ -10,9 +10,10 @@ refresh writes the state once and stores the new sketch. The timed steps are
 whole windows, so every window's state write is inside the timed region:
 --steps and --warmup are rounded up to multiples of W, and the JSON line
 reports both the requested and the timed (effective) counts. The timed steps
-are captured once into a HIP graph and the headline times one replay of it;
-the same steps launched one by one are timed too (eager), with HIP events
-around every update + refresh launch for the roofline.
+are captured once into a HIP graph and the headline times one replay of it,
+bracketed by device synchronisations; the same steps launched one by one are
+timed too (eager: enqueued right behind the warmup steps, with HIP events
+around every update + refresh launch for the roofline).
 
 Prints one JSON line. Extra fields: per-kernel times, two comparison paths on
 the same tokens (the exact buffered full read, and the per-token recurrent
@@ -260,6 +261,21 @@ class Layer:
         wall = time.perf_counter() - w0
         return max(e0.elapsed_time(e1) / 1e3, wall)
 
+    def eager_timed(self, warm, run):
+        """The eager legs: warm() enqueued, then run() right behind it with no host
+        synchronisation between them, so that the device does not idle (and slow its first
+        timed launches) between the warmup and the timed steps. Returns the HIP-event time
+        of run() on the bench stream."""
+        torch = self.torch
+        torch.cuda.synchronize()
+        warm()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        run()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3
+
     def graph_timed(self, enqueue):
         """Capture the timed steps into one HIP graph, replay once untimed, then time a replay."""
         torch = self.torch
@@ -298,10 +314,10 @@ class Layer:
         sketch = self.new_sketch()
         st_p, sk_p = state.data_ptr(), sketch.data_ptr()
         self.update_refresh(st_p, sk_p, self.bp, None, None, None, None, 0, stream=self.sp)
-        self.run_sketch(st_p, sk_p, 0, warmup, self.sp, only=only)
         upd_ev = []
-        eager_s = self.timed(lambda: self.run_sketch(st_p, sk_p, warmup, total, self.sp, upd_ev,
-                                                     only=only))
+        eager_s = self.eager_timed(
+            lambda: self.run_sketch(st_p, sk_p, 0, warmup, self.sp, only=only),
+            lambda: self.run_sketch(st_p, sk_p, warmup, total, self.sp, upd_ev, only=only))
         upd_ms = [s_.elapsed_time(e_) for s_, e_ in upd_ev]
         if only is not None:
             return None, eager_s, upd_ms, state, sketch
@@ -331,9 +347,9 @@ class Layer:
     def full_path(self, warmup, total):
         state_f = self.S0_dev.clone()
         sf_p = state_f.data_ptr()
-        self.run_full(sf_p, 0, warmup, self.sp)
         upd_f = []
-        eager_f = self.timed(lambda: self.run_full(sf_p, warmup, total, self.sp, upd_f))
+        eager_f = self.eager_timed(lambda: self.run_full(sf_p, 0, warmup, self.sp),
+                                   lambda: self.run_full(sf_p, warmup, total, self.sp, upd_f))
         graph_f = self.graph_timed(lambda cs: self.run_full(sf_p, warmup, total, cs))
         steps = total - warmup
         return {"steps_per_s": steps / graph_f, "ms_per_step": graph_f * 1e3 / steps,
@@ -425,8 +441,10 @@ def sweep_c5(a, torch, ssm, workloads, dev) -> int:
     T = base.steps
     # at least 8 update launches at every point: one launch's time moves by up to ~10% with
     # what the caches hold when it starts (kernel trace at W = 16: 788 to 936 us)
+    # and at least 4 windows of warmup: after the device has been idle, memory-bound launches
+    # run slow for a few milliseconds (the first W = 16 updates up to ~20%)
     w_max = max(workloads.C5_WINDOWS)
-    steps, warmup = plan_steps(max(a.steps, 8 * w_max), a.warmup, w_max)
+    steps, warmup = plan_steps(max(a.steps, 8 * w_max), max(a.warmup, 4 * w_max), w_max)
     n_steps = max(T, steps + warmup)
     shared = None
     for W in workloads.C5_WINDOWS:
@@ -661,15 +679,15 @@ def main(argv=None) -> int:
                     if upd_events is not None:
                         upd_events[-1][1].record(L.stream)
 
-        run_single(0, warmup, sp)
-        eager_1 = L.timed(lambda: run_single(warmup, total, sp))
+        eager_1 = L.eager_timed(lambda: run_single(0, warmup, sp),
+                                lambda: run_single(warmup, total, sp))
         graph_1 = L.graph_timed(lambda cs: run_single(warmup, total, cs))
         step_ms = L.kernel_time(lambda i: ssm.decode_step_varlen(
             d, N, None, tp[W - 1], pp[W - 1], d_ups[W - 1].batch, up[W - 1], st_p, sk_p, ska_p,
             bp, *L.ptrs[0][:5], kb, vb, db, bb, yp, stream=sp), 16)
-        run_two(0, warmup, sp)
         stg_ev = []
-        eager_2 = L.timed(lambda: run_two(warmup, total, sp, stg_ev))
+        eager_2 = L.eager_timed(lambda: run_two(0, warmup, sp),
+                                lambda: run_two(warmup, total, sp, stg_ev))
         graph_2 = L.graph_timed(lambda cs: run_two(warmup, total, cs))
         staggered = {"steps_per_s": steps / graph_1, "ms_per_step": graph_1 * 1e3 / steps,
                      "eager_steps_per_s": steps / eager_1, "launch_ms": step_ms,
@@ -704,8 +722,8 @@ def main(argv=None) -> int:
     if not a.no_compare:
         state_r = L.S0_dev.clone()
         sr_p = P(state_r)
-        L.run_rec(sr_p, 0, warmup, sp)
-        eager_r = L.timed(lambda: L.run_rec(sr_p, warmup, total, sp))
+        eager_r = L.eager_timed(lambda: L.run_rec(sr_p, 0, warmup, sp),
+                                lambda: L.run_rec(sr_p, warmup, total, sp))
         graph_r = L.graph_timed(lambda cs: L.run_rec(sr_p, warmup, total, cs))
         q0_, k0_, v0_, d0_, b0_ = L.ptrs[0]
         rec_ms = L.kernel_time(lambda i: ssm.recurrent_decode_step(L.d, sr_p, q0_, k0_, v0_, d0_,
