@@ -373,6 +373,51 @@ def test_per_head_ranks_above_eight(rule):
     _ranked_case(cfg, [9, 17, 2, 25, 8, 16])
 
 
+@pytest.mark.parametrize("rule", ["mamba2", "gdn", "kda"])
+def test_per_head_ranks_bf16_sketch(rule):
+    """Per-head ranks with the sketch stored in bf16: for every rank group, both reads, the
+    state and the stored sketch against the oracle's bf16 mode, with the oracle-only rounding
+    windows of the uniform-rank bf16 tests."""
+    import oracle
+    cfg = small(rule, N=3, Hh=5, W=4, T=11)
+    ranks = [1, 8, 3, 16, 12]
+    H.note(f"case per-head ranks, bf16 sketch, {rule}")
+    inp = H.Inputs(cfg, np.arange(cfg.units), cfg.steps)
+    B = workloads.basis_ranked(cfg, ranks)
+    off = np.concatenate([[0], np.cumsum(ranks)])
+    d = H.dims_of(cfg.with_(rank=max(ranks)), "bf16")
+    U, W, R = cfg.units, cfg.window, int(off[-1])
+    state = inp.S0.clone()
+    dec = WindowedDecoder(d, state, torch.from_numpy(B).cuda(), read="both", ranks=ranks)
+    dec.refresh()
+    ys, yf = [], []
+    S_snap = [state.view(U, cfg.d_k, cfg.d_v).cpu().double().numpy()]
+    Sk_snap = [dec.sketch.view(cfg.batch, R, cfg.d_v).float().cpu().double().numpy()]
+    for t in range(cfg.steps):
+        y, y2 = dec.step(inp.q[t], inp.k[t], inp.v[t], inp.decay[t], inp.beta[t])
+        ys.append(y.view(U, -1).cpu().double().numpy())
+        yf.append(y2.view(U, -1).cpu().double().numpy())
+        if (t + 1) % W == 0:
+            S_snap.append(state.view(U, cfg.d_k, cfg.d_v).cpu().double().numpy())
+            Sk_snap.append(dec.sketch.view(cfg.batch, R, cfg.d_v).float().cpu().double().numpy())
+    torch.cuda.synchronize()
+    ys, yf, S_snap = np.stack(ys), np.stack(yf), np.stack(S_snap)
+    heads = np.arange(U) % cfg.heads
+    h = inp.host
+    for r in sorted(set(ranks)):
+        sel = np.nonzero(np.array([ranks[x] == r for x in heads]))[0]
+        Bu = np.stack([B[off[heads[i]]:off[heads[i]] + r] for i in sel]).astype(np.float64)
+        args = (cfg.rule, inp.host_S0[sel], Bu, h["q"][:, sel], h["k"][:, sel], h["v"][:, sel],
+                h["decay"][:, sel], None if h["beta"] is None else h["beta"][:, sel], W)
+        ref = oracle.run(*args, sketch_bf16=True, want_ls=True)
+        ref_exact = oracle.run(*args)
+        sk = np.stack([np.stack([Sk_snap[w][i // cfg.heads, off[heads[i]]:off[heads[i]] + r]
+                                 for i in sel]) for w in range(len(Sk_snap))])
+        got = dict(y_sketch=ys[:, sel], y_full=yf[:, sel], S=S_snap[:, sel], Sk=sk)
+        H.compare(cfg.with_(rank=r), got, ref, sketch_bf16=True, host_basis=Bu,
+                  ref_exact=ref_exact)
+
+
 def test_per_head_ranks_d_v_16():
     cfg = small("gdn", d_k=64, d_v=16, N=3, Hh=5, W=4, T=11)
     H.note("case per-head ranks d_v=16")
