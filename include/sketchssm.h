@@ -51,8 +51,7 @@
  * exception crosses this interface. The detail of the last failure on the
  * calling thread is in ssm_last_error().
  *
- * Supported shapes: d_k in {16, 32, 64, 128}; d_v in {16, 32, 64, 128}
- * (the least-squares entry points need d_v >= 32); 1 <= W <= 16;
+ * Supported shapes: d_k in {16, 32, 64, 128}; d_v in {16, 32, 64, 128}; 1 <= W <= 16;
  * 1 <= r <= min(d_k, 32); N >= 0 (N = 0 is a no-op); H >= 1; N*H < 2^24, which
  * keeps every grid (one workgroup of up to 256 threads per unit) below 2^32
  * threads. Every pointer must be 16-byte aligned. Outputs must not overlap any

@@ -264,9 +264,6 @@ static ssm_status update_refresh_impl(const char* fn, const ssm_dims* d, const i
   if (ls) {
     if (d->sketch_dtype != SSM_SKETCH_F32)
       return fail(SSM_E_RANGE, "%s: least-squares coefficients need an fp32 sketch", fn);
-    if (d->d_v < 32)
-      return fail(SSM_E_SHAPE, "%s: least-squares coefficients need d_v >= 32 (got %d)", fn,
-                  d->d_v);
     if (sketch == nullptr) return fail(SSM_E_NULL, "%s: sketch_q is NULL", fn);
     if (read_map == nullptr) return fail(SSM_E_NULL, "%s: read_map is NULL", fn);
   }
@@ -310,9 +307,6 @@ static ssm_status sketch_decode_impl(const char* fn, const ssm_dims* d, const in
   if (d->batch == 0) return ok();
   if (ls && d->sketch_dtype != SSM_SKETCH_F32)
     return fail(SSM_E_RANGE, "%s: least-squares coefficients need an fp32 sketch", fn);
-  if (ls && d->d_v < 32)
-    return fail(SSM_E_SHAPE, "%s: least-squares coefficients need d_v >= 32 (got %d)", fn,
-                d->d_v);
   if (sketch == nullptr) return fail(SSM_E_NULL, "%s: %s is NULL", fn, ls ? "sketch_q" : "sketch");
   if (basis == nullptr) return fail(SSM_E_NULL, "%s: %s is NULL", fn, ls ? "read_map" : "basis");
   if (q == nullptr) return fail(SSM_E_NULL, "%s: q is NULL", fn);

@@ -265,8 +265,7 @@ hipError_t launch_sketch_decode_rule(const ssm_dims& d, const int32_t* rank_offs
     constexpr unsigned UPB = 256u / sketch_group<kDK, kDV>();
     const unsigned blocks = (unsigned)d.heads * (((unsigned)d.batch + UPB - 1) / UPB);
     const size_t lds = (size_t)max_rank * kDK * sizeof(float);
-    if (per_unit_map) {  // least squares: fp32 sketch, uniform rank, lockstep, d_v >= 32
-      if constexpr (kDV < 32) return hipErrorInvalidValue;  // rejected by the entry point
+    if (per_unit_map) {  // least squares: fp32 sketch, uniform rank, lockstep
       auto go_map = [&](auto wmax) {
         constexpr int kW = decltype(wmax)::value;
         hipLaunchKernelGGL(

@@ -58,7 +58,6 @@ __device__ __forceinline__ void update_refresh_unit(
   constexpr int RPL = TL::RPL;             // rows of S per lane
   constexpr int NT = TL::NT;               // threads per unit: one wave per 4 CG columns
   constexpr int DSTR = (RULE == KDA) ? DK : 1;
-  static_assert(!LS || CG == 8, "the least-squares refresh needs d_v >= 32");
   static_assert(!MMA || (!LS && CG == 8), "the matrix-core refresh: d_v >= 32, no least squares");
 
   extern __shared__ float4 lds4[];
@@ -146,9 +145,10 @@ __device__ __forceinline__ void update_refresh_unit(
   //      of 4 columns, summed over the 8 lanes of the row group (lane bits 0..2) as a
   //      reduce-scatter over four rows of Q at a time;
   //   e. the waves' partial Y are added in a fixed order and stored with Q.
+  constexpr int NW = TL::WAVES;  // waves of the unit: column blocks of 4 CG columns
   float* lQ = lB + rank * DK;  // [rank][DV] (LS only)
-  float* lP = lQ + rank * DV;  // [DV / 32][rank][DK] per-wave partial Y (LS only)
-  double* lG = reinterpret_cast<double*>(lP + (DV / 32) * rank * DK);  // [rank][rank] (LS only)
+  float* lP = lQ + rank * DV;  // [NW][rank][DK] per-wave partial Y (LS only)
+  double* lG = reinterpret_cast<double*>(lP + NW * rank * DK);  // [rank][rank] (LS only)
   const int ls_turn = (int)(unit % (NT / 64));  // the wave (and threads) of steps b and c
   auto ls_epilogue = [&](float* Qu) {
     __syncthreads();
@@ -285,36 +285,65 @@ __device__ __forceinline__ void update_refresh_unit(
       }
     }
     __syncthreads();
-    // Four rows of Q at a time, summed over the 8 lanes of the row group as a
-    // reduce-scatter: slot sl of lane cg holds Q row m0 + (sl ^ f) with f = lane bits 2, 1
-    // of cg, so the lane that row_half_mirror pairs it with (cg ^ 7) holds the same row in
-    // slot sl ^ 3, and quad_perm 2301's partner (cg ^ 2) in slot sl ^ 1. Four adds leave
-    // row m0 + f summed over all 8 lanes (twelve as four separate all-reduces).
-    const int f = ((cg >> 1) & 1) | ((cg >> 2) << 1);
-    for (int m0 = 0; m0 < rank; m0 += 4) {
-      float4 qv[4];
-#pragma unroll
-      for (int sl = 0; sl < 4; ++sl) {
-        const int m = m0 + (sl ^ f);
-        const float4 x = *reinterpret_cast<const float4*>(lQ + min(m, rank - 1) * DV + col);
-        qv[sl] = m < rank ? x : f4(0.f);
-      }
-#pragma unroll
-      for (int mm = 0; mm < RPL; ++mm) {
-        float a[4];
+    if constexpr (CG == 8) {
+      // Four rows of Q at a time, summed over the 8 lanes of the row group as a
+      // reduce-scatter: slot sl of lane cg holds Q row m0 + (sl ^ f) with f = lane bits 2, 1
+      // of cg, so the lane that row_half_mirror pairs it with (cg ^ 7) holds the same row in
+      // slot sl ^ 3, and quad_perm 2301's partner (cg ^ 2) in slot sl ^ 1. Four adds leave
+      // row m0 + f summed over all 8 lanes (twelve as four separate all-reduces).
+      const int f = ((cg >> 1) & 1) | ((cg >> 2) << 1);
+      for (int m0 = 0; m0 < rank; m0 += 4) {
+        float4 qv[4];
 #pragma unroll
         for (int sl = 0; sl < 4; ++sl) {
-          a[sl] = qv[sl].x * s[mm].x;
-          a[sl] = fmaf(qv[sl].y, s[mm].y, a[sl]);
-          a[sl] = fmaf(qv[sl].z, s[mm].z, a[sl]);
-          a[sl] = fmaf(qv[sl].w, s[mm].w, a[sl]);
+          const int m = m0 + (sl ^ f);
+          const float4 x = *reinterpret_cast<const float4*>(lQ + min(m, rank - 1) * DV + col);
+          qv[sl] = m < rank ? x : f4(0.f);
         }
-        a[0] += dpp<DPP_HALF_MIRROR>(a[3]);  // lanes cg, cg ^ 7
-        a[1] += dpp<DPP_HALF_MIRROR>(a[2]);
-        a[0] += dpp<DPP_QUAD_2301>(a[1]);    // and cg ^ 2, cg ^ 5
-        a[0] += dpp<DPP_QUAD_1032>(a[0]);    // and the other four (cg ^ 1 shares f)
-        // row m0 + f of Q against row mm * 8 + rg of S, over this wave's 32 columns
-        if (!(cg & 1) && m0 + f < rank) lP[(wave * rank + m0 + f) * DK + mm * 8 + rg] = a[0];
+#pragma unroll
+        for (int mm = 0; mm < RPL; ++mm) {
+          float a[4];
+#pragma unroll
+          for (int sl = 0; sl < 4; ++sl) {
+            a[sl] = qv[sl].x * s[mm].x;
+            a[sl] = fmaf(qv[sl].y, s[mm].y, a[sl]);
+            a[sl] = fmaf(qv[sl].z, s[mm].z, a[sl]);
+            a[sl] = fmaf(qv[sl].w, s[mm].w, a[sl]);
+          }
+          a[0] += dpp<DPP_HALF_MIRROR>(a[3]);  // lanes cg, cg ^ 7
+          a[1] += dpp<DPP_HALF_MIRROR>(a[2]);
+          a[0] += dpp<DPP_QUAD_2301>(a[1]);    // and cg ^ 2, cg ^ 5
+          a[0] += dpp<DPP_QUAD_1032>(a[0]);    // and the other four (cg ^ 1 shares f)
+          // row m0 + f of Q against row mm * 8 + rg of S, over this wave's 32 columns
+          if (!(cg & 1) && m0 + f < rank) lP[(wave * rank + m0 + f) * DK + mm * 8 + rg] = a[0];
+        }
+      }
+    } else {
+      // d_v = 16 (4 lanes per row group): four rows of Q at a time, each summed over the row
+      // group's lanes (lane bits 0, 1) by two quad permutations; lane cg keeps row m0 + cg
+      for (int m0 = 0; m0 < rank; m0 += 4) {
+        float4 qv[4];
+#pragma unroll
+        for (int sl = 0; sl < 4; ++sl) {
+          const int m = m0 + sl;
+          const float4 x = *reinterpret_cast<const float4*>(lQ + min(m, rank - 1) * DV + col);
+          qv[sl] = m < rank ? x : f4(0.f);
+        }
+#pragma unroll
+        for (int mm = 0; mm < RPL; ++mm) {
+          float a[4];
+#pragma unroll
+          for (int sl = 0; sl < 4; ++sl) {
+            a[sl] = qv[sl].x * s[mm].x;
+            a[sl] = fmaf(qv[sl].y, s[mm].y, a[sl]);
+            a[sl] = fmaf(qv[sl].z, s[mm].z, a[sl]);
+            a[sl] = fmaf(qv[sl].w, s[mm].w, a[sl]);
+            a[sl] += dpp<DPP_QUAD_1032>(a[sl]);
+            a[sl] += dpp<DPP_QUAD_2301>(a[sl]);
+          }
+          const float mine = cg == 0 ? a[0] : cg == 1 ? a[1] : cg == 2 ? a[2] : a[3];
+          if (m0 + cg < rank) lP[(wave * rank + m0 + cg) * DK + mm * RG + rg] = mine;
+        }
       }
     }
     __syncthreads();
@@ -322,7 +351,7 @@ __device__ __forceinline__ void update_refresh_unit(
     for (int e = tid; e < rank * DK; e += NT) {
       float y = 0.f;
 #pragma unroll
-      for (int w = 0; w < DV / 32; ++w) y += lP[w * rank * DK + e];
+      for (int w = 0; w < NW; ++w) y += lP[w * rank * DK + e];
       Yu[e] = y;
     }
     for (int e = tid; e < rank * DV; e += NT) Qu[e] = lQ[e];

@@ -19,9 +19,11 @@ size_t update_refresh_lds_bytes(const ssm_dims& d, int n, int max_rank, bool ls)
                                        decltype(DV)::value>(n);
     return hipSuccess;
   });
-  // least squares: the sketch rows [r][d_v], the waves' partial read maps [d_v/32][r][d_k]
-  // and the Gram matrix / Cholesky factor [r][r] in fp64
-  const size_t ls_floats = ls ? (size_t)max_rank * d.d_v + (size_t)(d.d_v / 32) * max_rank * d.d_k +
+  // least squares: the sketch rows [r][d_v], the waves' partial read maps [waves][r][d_k]
+  // (one wave per 32 columns, one at d_v = 16) and the Gram matrix / Cholesky factor [r][r]
+  // in fp64
+  const size_t waves = d.d_v >= 32 ? (size_t)(d.d_v / 32) : 1;
+  const size_t ls_floats = ls ? (size_t)max_rank * d.d_v + waves * max_rank * d.d_k +
                                     2 * (size_t)max_rank * max_rank
                               : 0;
   return (floats + (size_t)max_rank * d.d_k + ls_floats) * sizeof(float);

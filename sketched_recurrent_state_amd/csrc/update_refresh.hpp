@@ -53,16 +53,13 @@ hipError_t launch_update_refresh_rule(const ssm_dims& d, const int32_t* rank_off
     using TIN = typename decltype(T)::type;
     constexpr int kR = RULE, kDK = decltype(DK)::value, kDV = decltype(DV)::value;
     constexpr unsigned NT = TileLayout<kDK, kDV>::NT;
-    if (read_map != nullptr) {  // least squares: fp32 sketch, uniform rank, lockstep, d_v >= 32
-      if constexpr (kDV >= 32) {
-        hipLaunchKernelGGL(
-            (update_refresh_kernel<kR, kDK, kDV, TIN, float, true, UniformRank, Lockstep, false>),
-            dim3(units), dim3(NT), lds, stream, state, static_cast<float*>(sketch), read_map,
-            basis, static_cast<const TIN*>(k_buf), static_cast<const TIN*>(v_buf), decay_buf,
-            beta_buf, d.heads, d.window, UniformRank{d.rank, d.heads}, Lockstep{n});
-        return hipGetLastError();
-      }
-      return hipErrorInvalidValue;  // rejected by the entry point's checks
+    if (read_map != nullptr) {  // least squares: fp32 sketch, uniform rank, lockstep
+      hipLaunchKernelGGL(
+          (update_refresh_kernel<kR, kDK, kDV, TIN, float, true, UniformRank, Lockstep, false>),
+          dim3(units), dim3(NT), lds, stream, state, static_cast<float*>(sketch), read_map,
+          basis, static_cast<const TIN*>(k_buf), static_cast<const TIN*>(v_buf), decay_buf,
+          beta_buf, d.heads, d.window, UniformRank{d.rank, d.heads}, Lockstep{n});
+      return hipGetLastError();
     }
     return with_sketch_type(d, [&](auto SK) {
       using TSK = typename decltype(SK)::type;

@@ -382,15 +382,14 @@ def test_decode_step_varlen_validation():
     assert status_of(ssm.decode_step_varlen, d0, P, *([None] * 3), 0, *([None] * 16))[0] == 0
 
 
-def test_least_squares_needs_d_v_32():
-    """d_v = 16 is a supported shape, but not for the least-squares refresh (its read map is
-    summed over the 8 column groups of a 32-column wave)."""
+def test_least_squares_takes_d_v_16():
+    """d_v = 16 is a supported shape for every entry point, the least-squares ones included:
+    calls that are valid but for one NULL pointer stop at that pointer, not at the shape."""
     p = addrs(10)
     d = dims(d_v=16)
-    st, msg = status_of(ssm.window_update_refresh_ls, d, *p[:8], 1)
-    assert st == 2 and "d_v >= 32" in msg
-    st, msg = status_of(ssm.sketch_decode_step_ls, d, *p[:7], 1, p[7])
-    assert st == 2 and "d_v >= 32" in msg
-    # the other entry points take d_v = 16: a valid call stops at its NULL state
+    st, msg = status_of(ssm.window_update_refresh_ls, d, None, *p[1:8], 1)
+    assert st == 1 and "state" in msg
+    st, msg = status_of(ssm.sketch_decode_step_ls, d, None, *p[1:7], 1, p[7])
+    assert st == 1 and "sketch_q" in msg
     st, msg = status_of(ssm.window_update_refresh, d, None, *p[1:7], 1)
     assert st == 1 and "state" in msg

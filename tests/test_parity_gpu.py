@@ -628,6 +628,11 @@ LS_CASES = [
     small("gdn"), small("mamba2", d_k=128, d_v=64), small("kda", W=4, r=8),
     small("gdn", "f32", d_k=64, d_v=32, W=5, r=3),
     small("kda", d_k=16, d_v=128, W=1, r=16),   # r = d_k: the read is exact
+    # d_v = 16: 4 lanes per row group; factorisation in registers (r = 8) and in LDS (r = 12),
+    # and r = 24 > d_v, where the rows past the 16th are dependent and dropped (the read is
+    # then the exact window-start read)
+    small("gdn", d_k=128, d_v=16, W=8, r=8), small("kda", d_k=64, d_v=16, W=5, r=12),
+    small("mamba2", "f32", d_k=32, d_v=16, W=3, r=24),
     small("gdn", "bf16", d_k=128, d_v=128, W=16, r=32, N=2, Hh=3, T=33),
 ]
 
