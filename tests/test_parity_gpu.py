@@ -418,6 +418,15 @@ def test_per_head_ranks_bf16_sketch(rule):
                   ref_exact=ref_exact)
 
 
+@pytest.mark.parametrize("rule", ["mamba2", "gdn", "kda"])
+def test_per_head_ranks_f32_inputs(rule):
+    """Per-head ranks with fp32 q, k, v: ranks on both sides of the eight fetched ahead, an
+    odd window."""
+    cfg = small(rule, "f32", d_k=64, d_v=64, N=3, Hh=5, W=6, T=13)
+    H.note(f"case per-head ranks, fp32 inputs, {rule}")
+    _ranked_case(cfg, [4, 9, 2, 17, 8])
+
+
 def test_per_head_ranks_d_v_16():
     cfg = small("gdn", d_k=64, d_v=16, N=3, Hh=5, W=4, T=11)
     H.note("case per-head ranks d_v=16")
