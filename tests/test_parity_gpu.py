@@ -960,11 +960,12 @@ def test_single_launch_step_staggered_workload_sampled(name):
     H.note(f"single-launch staggered {name}: worst sketch-read error {worst:.2e}")
 
 
-@pytest.mark.parametrize("rule,sketch_dtype,d_v", [
-    ("mamba2", "f32", 64), ("gdn", "f32", 64), ("kda", "f32", 64),
-    ("mamba2", "bf16", 64), ("gdn", "bf16", 64), ("kda", "bf16", 64),
-    ("gdn", "f32", 16), ("kda", "bf16", 16)])
-def test_single_launch_step_continuous_batching(rule, sketch_dtype, d_v):
+@pytest.mark.parametrize("rule,sketch_dtype,d_v,in_dtype", [
+    ("mamba2", "f32", 64, "bf16"), ("gdn", "f32", 64, "bf16"), ("kda", "f32", 64, "bf16"),
+    ("mamba2", "bf16", 64, "bf16"), ("gdn", "bf16", 64, "bf16"), ("kda", "bf16", 64, "bf16"),
+    ("gdn", "f32", 16, "bf16"), ("kda", "bf16", 16, "bf16"),
+    ("mamba2", "f32", 16, "f32"), ("gdn", "bf16", 64, "f32"), ("kda", "f32", 64, "f32")])
+def test_single_launch_step_continuous_batching(rule, sketch_dtype, d_v, in_dtype):
     """ssm_decode_step_varlen with sequences joining at different steps into permuted pool
     slots, reversed row order and a padding row (tau = 0, its output left untouched): every
     sequence against its own oracle run (outputs every step, state and current sketch at the
@@ -976,15 +977,16 @@ def test_single_launch_step_continuous_batching(rule, sketch_dtype, d_v):
     joins = [0, 1, 2, 3, 5, 6]
     slots = [5, 0, 7, 2, 3, 6]
     P = 8                                      # pool size
-    cfg = small(rule, d_k=64, d_v=d_v, W=W, r=8, N=len(joins), Hh=3, T=T)
-    H.note(f"case single-launch step, continuous batching {rule} {sketch_dtype} d_v={d_v}")
+    cfg = small(rule, in_dtype, d_k=64, d_v=d_v, W=W, r=8, N=len(joins), Hh=3, T=T)
+    H.note(f"case single-launch step, continuous batching {rule} {sketch_dtype} d_v={d_v} "
+           f"{in_dtype} inputs")
     Hh, dk, dv = cfg.heads, cfg.d_k, cfg.d_v
     S0 = np.concatenate([workloads.initial_state(cfg, [n]) for n in range(len(joins))])
     B = workloads.basis(cfg)
     steps = [workloads.step_inputs(cfg, j) for j in range(T)]   # local step j, row n = sequence n
     d_pool = H.dims_of(cfg.with_(batch=P), sketch_dtype)
     dev = "cuda"
-    tin = torch.bfloat16
+    tin = torch.bfloat16 if in_dtype == "bf16" else torch.float32
     skt = torch.bfloat16 if sketch_dtype == "bf16" else torch.float32
 
     def td(x):
